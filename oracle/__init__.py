@@ -1,0 +1,197 @@
+"""CPU oracle for MoE dispatch/combine -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may import
+this package.  The product path (``combine_moe_route_top_amd``) never imports it.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64); this module only builds it with gcc and
+marshals numpy arrays through ctypes.  Each wrapper allocates its outputs and returns them.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_HDR = os.path.join(_HERE, "oracle.h")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+# -ffp-contract=off: every fp32 operation in oracle.c is one IEEE operation (no implicit FMA).
+CFLAGS = ["-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c into liboracle.so with gcc (always when ``force``)."""
+    stale = (not os.path.exists(_LIB)) or any(
+        os.path.getmtime(p) > os.path.getmtime(_LIB) for p in (_SRC, _HDR))
+    if force or stale:
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    """Load liboracle.so (building it if stale).  MOE_ORACLE_LIB names another build of
+    oracle.c to load instead; the mutation tests use it to run the pins on planted mistakes."""
+    global _lib
+    if _lib is None:
+        path = os.environ.get("MOE_ORACLE_LIB")
+        if not path:
+            path = build()
+        _lib = ctypes.CDLL(path)
+        _lib.oracle_bf16_from_double.restype = ctypes.c_uint16
+        _lib.oracle_bf16_from_double.argtypes = [ctypes.c_double]
+        _lib.oracle_bf16_to_double.restype = ctypes.c_double
+        _lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+        _lib.oracle_e4m3_to_double.restype = ctypes.c_double
+        _lib.oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
+        _lib.oracle_row_bytes.restype = ctypes.c_long
+    return _lib
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int),
+                ("E", ctypes.c_int), ("R", ctypes.c_int), ("fp8", ctypes.c_int),
+                ("B", ctypes.c_long)]
+
+
+def _p(a):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def shape(N, T, H, E, R, fp8=False, B=None) -> Shape:
+    if B is None:
+        B = N * T * max(R, E // N)
+    return Shape(N, T, H, E, R, int(bool(fp8)), B)
+
+
+def row_bytes(sh: Shape) -> int:
+    return int(lib().oracle_row_bytes(ctypes.byref(sh)))
+
+
+def bf16_from_double(x: float) -> int:
+    return int(lib().oracle_bf16_from_double(float(x)))
+
+
+def bf16_to_double(b: int) -> float:
+    return float(lib().oracle_bf16_to_double(int(b)))
+
+
+def e4m3_to_double(b: int) -> float:
+    return float(lib().oracle_e4m3_to_double(int(b)))
+
+
+def route(logits: np.ndarray, bias, R: int):
+    """logits f32[n][E], bias f32[E] or None -> (idx i32[n][R], w f32[n][R])."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    n, E = logits.shape
+    idx = np.empty((n, R), np.int32)
+    w = np.empty((n, R), np.float32)
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    lib().oracle_route(ctypes.c_int(n), ctypes.c_int(E), ctypes.c_int(R), _p(logits), _p(b),
+                       _p(idx), _p(w))
+    return idx, w
+
+
+def dispatch_send(sh: Shape, x: np.ndarray, x_scale, topk_idx: np.ndarray):
+    """x: uint16[N][T][H] (bf16 bits) or uint8[N][T][H] (e4m3 codes); x_scale f32[N][T][H/128]."""
+    N, T, E, R = sh.N, sh.T, sh.E, sh.R
+    P = row_bytes(sh)
+    x = np.ascontiguousarray(x)
+    xs = None if not sh.fp8 else np.ascontiguousarray(x_scale, dtype=np.float32)
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    counts = np.empty((N, E), np.int32)
+    send_off = np.empty((N, N + 1), np.int32)
+    send_pos = np.empty((N, T * R), np.int32)
+    send_buf = np.zeros((N, T * R, P), np.uint8)
+    send_meta = np.zeros((N, T * R, 2), np.int32)
+    lib().oracle_dispatch_send(ctypes.byref(sh), _p(x), _p(xs), _p(idx), _p(counts), _p(send_off),
+                               _p(send_pos), _p(send_buf), _p(send_meta))
+    return dict(counts=counts, send_off=send_off, send_pos=send_pos, send_buf=send_buf,
+                send_meta=send_meta)
+
+
+def net_dispatch(sh: Shape, send_off, send_buf, send_meta):
+    N, B = sh.N, sh.B
+    P = row_bytes(sh)
+    recv_buf = np.zeros((N, B, P), np.uint8)
+    recv_meta = np.zeros((N, B, 2), np.int32)
+    recv_off = np.empty((N, N + 1), np.int32)
+    lib().oracle_net_dispatch(ctypes.byref(sh), _p(send_off), _p(send_buf), _p(send_meta),
+                              _p(recv_buf), _p(recv_meta), _p(recv_off))
+    return dict(recv_buf=recv_buf, recv_meta=recv_meta, recv_off=recv_off)
+
+
+def dispatch_recv(sh: Shape, counts, recv_off, recv_buf, recv_meta):
+    N, B, H = sh.N, sh.B, sh.H
+    L = sh.E // N
+    if sh.fp8:
+        expert_x = np.zeros((N, B, H), np.uint8)
+        expert_scale = np.zeros((N, B, H // 128), np.float32)
+    else:
+        expert_x = np.zeros((N, B, H), np.uint16)
+        expert_scale = None
+    expert_cnt = np.empty((N, L), np.int32)
+    expert_off = np.empty((N, L + 1), np.int32)
+    expert_src = np.full((N, B), -1, np.int32)
+    expert_rpos = np.full((N, B), -1, np.int32)
+    lib().oracle_dispatch_recv(ctypes.byref(sh), _p(counts), _p(recv_off), _p(recv_buf),
+                               _p(recv_meta), _p(expert_x), _p(expert_scale), _p(expert_cnt),
+                               _p(expert_off), _p(expert_src), _p(expert_rpos))
+    return dict(expert_x=expert_x, expert_scale=expert_scale, expert_cnt=expert_cnt,
+                expert_off=expert_off, expert_src=expert_src, expert_rpos=expert_rpos)
+
+
+def expert(sh: Shape, mode: int, expert_x, expert_scale, expert_off):
+    N, B, H = sh.N, sh.B, sh.H
+    y = np.zeros((N, B, H), np.uint16)
+    lib().oracle_expert(ctypes.byref(sh), ctypes.c_int(mode), _p(np.ascontiguousarray(expert_x)),
+                        _p(expert_scale), _p(expert_off), _p(y))
+    return y
+
+
+def combine(sh: Shape, mode: int, expert_y, expert_rpos, recv_off, send_off, send_pos, topk_w):
+    N, B, H, T, R = sh.N, sh.B, sh.H, sh.T, sh.R
+    cs = np.zeros((N, B, H), np.uint16)
+    cr = np.zeros((N, T * R, H), np.uint16)
+    out = np.empty((N, T, H), np.uint16)
+    w = np.ascontiguousarray(topk_w, dtype=np.float32)
+    lib().oracle_combine(ctypes.byref(sh), ctypes.c_int(mode), _p(expert_y), _p(expert_rpos),
+                         _p(recv_off), _p(send_off), _p(send_pos), _p(w), _p(cs), _p(cr),
+                         _p(out))
+    return dict(cs_buf=cs, cr_buf=cr, out=out)
+
+
+def run_all(sh: Shape, inp: dict, expert_mode: int = 0, combine_mode: int = 0,
+            tight: bool = False) -> dict:
+    """The whole path on one input set (see moe_synth.make_inputs).
+
+    With ``tight`` the receive-side arrays get exactly max_d(rows received by d) rows per rank
+    instead of ``sh.B`` (keeps host memory small for the large workloads); ``res["shape"]``
+    is the shape actually used."""
+    res = {}
+    idx, w = route(inp["logits"], inp["bias"], sh.R)
+    res["topk_idx"], res["topk_w"] = idx, w
+    res.update(dispatch_send(sh, inp["x"], inp.get("x_scale"), idx.reshape(sh.N, sh.T * sh.R)))
+    if tight:
+        n = np.diff(res["send_off"], axis=1)          # n[s][d]
+        sh = Shape(sh.N, sh.T, sh.H, sh.E, sh.R, sh.fp8, max(1, int(n.sum(axis=0).max())))
+    res["shape"] = sh
+    res.update(net_dispatch(sh, res["send_off"], res["send_buf"], res["send_meta"]))
+    res.update(dispatch_recv(sh, res["counts"], res["recv_off"], res["recv_buf"],
+                             res["recv_meta"]))
+    res["expert_y"] = expert(sh, expert_mode, res["expert_x"], res["expert_scale"],
+                             res["expert_off"])
+    res.update(combine(sh, combine_mode, res["expert_y"], res["expert_rpos"], res["recv_off"],
+                       res["send_off"], res["send_pos"], w))
+    return res

@@ -1,0 +1,350 @@
+/*
+ * oracle.c -- plain, slow CPU oracle for MoE expert-parallel dispatch and combine.
+ *
+ * TEST INFRASTRUCTURE ONLY: loaded by tests/, the smoke check and the benchmark's CPU-baseline
+ * leg, never by the product.  Plain loops in the order the pages describe the method; no
+ * blocking, fusion or reordering.  Floating point the method computes is done in fp64 and
+ * rounded once.  Build with -ffp-contract=off and without fast-math so that every fp32
+ * operation written here is exactly one IEEE operation.
+ *
+ * Pages cited: [EFA] "Enabling trillion-parameter models on AWS EFA";
+ * [PORT] "Efficient and portable mixture-of-experts communication";
+ * [DSK] "Lower latency and higher throughput with multi-node DeepSeek deployment".
+ *
+ * Readings of the pages taken here (the pages leave these steps open):
+ *  - expert e lives on rank e / L, L = E / N (contiguous blocks; [DSK] Expert Parallelism only
+ *    says each GPU holds E / EP experts);
+ *  - one row per (token, slot), i.e. one copy per routed expert ([PORT] Dispatch: the same
+ *    buffer is sent once to each expert);
+ *  - slot order is descending (logit + bias), ties to the lower expert id; the weights are the
+ *    softmax of the selected R values; combine does not renormalise;
+ *  - inside a send segment rows keep the (token, slot) order; the receive buffer therefore
+ *    holds rows in (source, token, slot) order and the expert-major tensor in
+ *    (local expert, source, token, slot) order.
+ */
+#include "oracle.h"
+
+#include <assert.h>
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+long oracle_row_bytes(const oracle_shape* sh) {
+    if (!sh->fp8) return 2L * sh->H;
+    return (long)sh->H + 4L * (sh->H / 128);
+}
+
+/* ---------------------------------------------------------------- scalar formats */
+
+/* bf16 = the upper half of an IEEE binary32: 1 sign, 8 exponent, 7 fraction bits.  Round a
+ * double to the nearest bf16 value, ties to even, by scaling it so that one bf16 ulp becomes
+ * 1.0 (an exact power-of-two scaling), rounding to an integer with nearbyint (the default
+ * rounding mode is to-nearest-even) and scaling back. */
+uint16_t oracle_bf16_from_double(double x) {
+    if (isnan(x)) return 0x7FC0;
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (a == 0.0) return sign;
+    if (isinf(a)) return sign | 0x7F80;
+    int ex;
+    frexp(a, &ex);                     /* a = m * 2^ex, 0.5 <= m < 1 */
+    int ulp_exp = ex - 8;              /* 8 significant bits */
+    if (ulp_exp < -133) ulp_exp = -133; /* subnormal spacing 2^-126 * 2^-7 */
+    double q = nearbyint(ldexp(a, -ulp_exp));
+    double r = ldexp(q, ulp_exp);
+    const double bf16_max = ldexp(255.0, 120); /* (2 - 2^-7) * 2^127 */
+    if (r > bf16_max) return sign | 0x7F80;
+    float f = (float)r;                /* exact: r has at most 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return sign | (uint16_t)(u >> 16);
+}
+
+double oracle_bf16_to_double(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* OCP 8-bit E4M3: 1 sign, 4 exponent (bias 7), 3 mantissa bits; no infinities; S.1111.111 is
+ * NaN; exponent field 0 holds subnormals m/8 * 2^-6. */
+double oracle_e4m3_to_double(uint8_t b) {
+    int s = b >> 7, e = (b >> 3) & 15, m = b & 7;
+    if (e == 15 && m == 7) return NAN;
+    double v = (e == 0) ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+    return s ? -v : v;
+}
+
+/* ---------------------------------------------------------------- routing */
+
+/* [DSK] Expert Parallelism: each token goes to 8 of the 256 routed experts and the expert
+ * results are summed with weights.  [DSK] MoE Router: the router sorts the scores while
+ * tracking the indices of the sorted elements.  [PORT] introduction: weights come from the
+ * router's probability distribution and the output is a weighted average.
+ * Selection: R passes, each taking the best unselected expert under (v desc, e asc). */
+void oracle_route(int n_tokens, int E, int R, const float* logits, const float* bias,
+                  int32_t* topk_idx, float* topk_w) {
+    assert(E >= 1 && R >= 1 && R <= E);
+    float* v = (float*)malloc(sizeof(float) * E);
+    char* taken = (char*)malloc(E);
+    double* z = (double*)malloc(sizeof(double) * R);
+    for (int n = 0; n < n_tokens; ++n) {
+        for (int e = 0; e < E; ++e) {
+            float l = logits[(long)n * E + e];
+            assert(isfinite(l));
+            v[e] = bias ? l + bias[e] : l; /* one fp32 addition */
+            taken[e] = 0;
+        }
+        for (int k = 0; k < R; ++k) {
+            int best = -1;
+            for (int e = 0; e < E; ++e) {
+                if (taken[e]) continue;
+                if (best < 0 || v[e] > v[best]) best = e; /* strict '>' keeps the lower id on ties */
+            }
+            taken[best] = 1;
+            topk_idx[(long)n * R + k] = best;
+        }
+        /* softmax over the selected values, in fp64, shifted by the largest (slot 0) */
+        double v0 = (double)v[topk_idx[(long)n * R]];
+        double sum = 0.0;
+        for (int k = 0; k < R; ++k) {
+            z[k] = exp((double)v[topk_idx[(long)n * R + k]] - v0);
+            sum += z[k];
+        }
+        for (int k = 0; k < R; ++k) topk_w[(long)n * R + k] = (float)(z[k] / sum);
+    }
+    free(v);
+    free(taken);
+    free(z);
+}
+
+/* ---------------------------------------------------------------- dispatch */
+
+/* [EFA] dispatch timing paragraph: the send kernel counts tokens per expert, takes a cumulative
+ * sum of the counts to find the offsets that pack tokens into send buffers contiguous per peer,
+ * and packs them.  [EFA] send-buffer paragraph: senders must lay out their writes contiguously.
+ * [PORT] Dispatch: activations, block scales and the token's index travel together.
+ * Row metadata: meta[0] = e*T*R + t*R + k (expert and source slot), meta[1] = how many earlier
+ * slots of the same source chose the same expert. */
+void oracle_dispatch_send(const oracle_shape* sh, const uint8_t* x, const float* x_scale,
+                          const int32_t* topk_idx, int32_t* counts, int32_t* send_off,
+                          int32_t* send_pos, uint8_t* send_buf, int32_t* send_meta) {
+    const int N = sh->N, T = sh->T, H = sh->H, E = sh->E, R = sh->R;
+    assert(N >= 1 && E % N == 0);
+    const int L = E / N;
+    const long P = oracle_row_bytes(sh);
+    const long TR = (long)T * R;
+    const long xrow = sh->fp8 ? H : 2L * H; /* payload bytes of one token */
+    const int nsc = H / 128;               /* fp8 block scales per token */
+    int32_t* fill = (int32_t*)malloc(sizeof(int32_t) * N);
+    int32_t* seen = (int32_t*)malloc(sizeof(int32_t) * E);
+    for (int s = 0; s < N; ++s) {
+        const int32_t* idx = topk_idx + s * TR;
+        int32_t* cnt = counts + (long)s * E;
+        int32_t* off = send_off + (long)s * (N + 1);
+        /* per-expert token counts */
+        for (int e = 0; e < E; ++e) cnt[e] = 0;
+        for (long i = 0; i < TR; ++i) {
+            int e = idx[i];
+            assert(e >= 0 && e < E);
+            cnt[e] += 1;
+        }
+        /* per-destination sizes, exclusive scan */
+        off[0] = 0;
+        for (int d = 0; d < N; ++d) {
+            int n = 0;
+            for (int e = d * L; e < (d + 1) * L; ++e) n += cnt[e];
+            off[d + 1] = off[d] + n;
+        }
+        /* pack in (token, slot) order */
+        for (int d = 0; d < N; ++d) fill[d] = 0;
+        for (int e = 0; e < E; ++e) seen[e] = 0;
+        for (int t = 0; t < T; ++t) {
+            for (int k = 0; k < R; ++k) {
+                long i = (long)t * R + k;
+                int e = idx[i];
+                for (int kk = 0; kk < k; ++kk) assert(idx[(long)t * R + kk] != e); /* distinct */
+                int d = e / L;
+                long pos = off[d] + fill[d];
+                fill[d] += 1;
+                send_pos[s * TR + i] = (int32_t)pos;
+                uint8_t* row = send_buf + ((long)s * TR + pos) * P;
+                memcpy(row, x + ((long)s * T + t) * xrow, xrow);
+                if (sh->fp8)
+                    memcpy(row + xrow, x_scale + ((long)s * T + t) * nsc, 4L * nsc);
+                int32_t* meta = send_meta + 2 * ((long)s * TR + pos);
+                meta[0] = (int32_t)((long)e * TR + i);
+                meta[1] = seen[e];
+                seen[e] += 1;
+            }
+        }
+    }
+    free(fill);
+    free(seen);
+}
+
+/* [EFA] send-buffer paragraph: once the per-expert counts are exchanged every rank knows where
+ * its writes land and at which offset each source's tokens arrive; the bulk then moves as one
+ * write per peer.  recv_off[d][s] = sum over s' < s of what s' sends to d. */
+void oracle_net_dispatch(const oracle_shape* sh, const int32_t* send_off, const uint8_t* send_buf,
+                         const int32_t* send_meta, uint8_t* recv_buf, int32_t* recv_meta,
+                         int32_t* recv_off) {
+    const int N = sh->N;
+    const long P = oracle_row_bytes(sh);
+    const long TR = (long)sh->T * sh->R;
+    for (int d = 0; d < N; ++d) {
+        int32_t* roff = recv_off + (long)d * (N + 1);
+        roff[0] = 0;
+        for (int s = 0; s < N; ++s) {
+            const int32_t* soff = send_off + (long)s * (N + 1);
+            roff[s + 1] = roff[s] + (soff[d + 1] - soff[d]);
+        }
+        assert(roff[N] <= sh->B);
+    }
+    for (int s = 0; s < N; ++s) {
+        const int32_t* soff = send_off + (long)s * (N + 1);
+        for (int d = 0; d < N; ++d) {
+            long n = soff[d + 1] - soff[d];
+            long src = (long)s * TR + soff[d];
+            long dst = (long)d * sh->B + recv_off[(long)d * (N + 1) + s];
+            memcpy(recv_buf + dst * P, send_buf + src * P, n * P);
+            memcpy(recv_meta + 2 * dst, send_meta + 2 * src, 8 * n);
+        }
+    }
+}
+
+/* [PORT] Dispatch: the receiver copies tokens into contiguous buffers that feed the grouped
+ * GEMM, grouping tokens of one expert together, and stores source rank, expert index and token
+ * index for combine.  Expert-major order: walking the receive rows in order and appending each
+ * to its local expert's group keeps (source, token, slot) order inside the group. */
+void oracle_dispatch_recv(const oracle_shape* sh, const int32_t* counts, const int32_t* recv_off,
+                          const uint8_t* recv_buf, const int32_t* recv_meta, uint8_t* expert_x,
+                          float* expert_scale, int32_t* expert_cnt, int32_t* expert_off,
+                          int32_t* expert_src, int32_t* expert_rpos) {
+    const int N = sh->N, H = sh->H, E = sh->E;
+    const int L = E / N;
+    const long P = oracle_row_bytes(sh);
+    const long TR = (long)sh->T * sh->R;
+    const long xrow = sh->fp8 ? H : 2L * H;
+    const int nsc = H / 128;
+    int32_t* fill = (int32_t*)malloc(sizeof(int32_t) * L);
+    for (int d = 0; d < N; ++d) {
+        int32_t* ecnt = expert_cnt + (long)d * L;
+        int32_t* eoff = expert_off + (long)d * (L + 1);
+        const int32_t* roff = recv_off + (long)d * (N + 1);
+        eoff[0] = 0;
+        for (int j = 0; j < L; ++j) {
+            int c = 0;
+            for (int s = 0; s < N; ++s) c += counts[(long)s * E + d * L + j];
+            ecnt[j] = c;
+            eoff[j + 1] = eoff[j] + c;
+        }
+        assert(eoff[L] == roff[N]);
+        for (int j = 0; j < L; ++j) fill[j] = 0;
+        int s = 0;
+        for (long r = 0; r < roff[N]; ++r) {
+            while (r >= roff[s + 1]) ++s; /* source rank of receive row r */
+            const int32_t* meta = recv_meta + 2 * ((long)d * sh->B + r);
+            int e = (int)(meta[0] / TR);
+            long i = meta[0] % TR;
+            assert(e / L == d);
+            int j = e - d * L;
+            long q = eoff[j] + fill[j];
+            fill[j] += 1;
+            const uint8_t* row = recv_buf + ((long)d * sh->B + r) * P;
+            memcpy(expert_x + ((long)d * sh->B + q) * xrow, row, xrow);
+            if (sh->fp8)
+                memcpy(expert_scale + ((long)d * sh->B + q) * nsc, row + xrow, 4L * nsc);
+            expert_src[(long)d * sh->B + q] = (int32_t)((long)s * TR + i);
+            expert_rpos[(long)d * sh->B + q] = (int32_t)r;
+        }
+    }
+    free(fill);
+}
+
+/* Stand-in for the grouped GEMM ([EFA] dispatch/combine overview: the grouped GEMM multiplies
+ * tokens by expert weights between dispatch and combine).  Identity: y = the dispatched value
+ * (bf16 as is; fp8 decoded and multiplied by its block scale, rounded once to bf16).  Tagged:
+ * y = bf16(identity * (64 + e % 64) / 64), which makes every expert's output distinct. */
+void oracle_expert(const oracle_shape* sh, int mode, const uint8_t* expert_x,
+                   const float* expert_scale, const int32_t* expert_off, uint16_t* expert_y) {
+    const int N = sh->N, H = sh->H, L = sh->E / sh->N;
+    const int nsc = H / 128;
+    for (int d = 0; d < N; ++d) {
+        const int32_t* eoff = expert_off + (long)d * (L + 1);
+        for (int j = 0; j < L; ++j) {
+            int e = d * L + j;
+            double tag = (mode == 1) ? (double)(64 + e % 64) / 64.0 : 1.0;
+            for (long q = eoff[j]; q < eoff[j + 1]; ++q) {
+                long row = (long)d * sh->B + q;
+                for (int h = 0; h < H; ++h) {
+                    double v;
+                    if (sh->fp8) {
+                        v = oracle_e4m3_to_double(expert_x[row * H + h]) *
+                            (double)expert_scale[row * nsc + h / 128];
+                    } else {
+                        uint16_t b;
+                        memcpy(&b, expert_x + (row * H + h) * 2, 2);
+                        v = oracle_bf16_to_double(b);
+                    }
+                    expert_y[row * H + h] = oracle_bf16_from_double(v * tag);
+                }
+            }
+        }
+    }
+}
+
+/* ---------------------------------------------------------------- combine */
+
+/* [EFA] combine paragraphs: the routing metadata is already known from dispatch, so combine
+ * shuffles the expert outputs, copies them back with one write per peer, and the receiver then
+ * reads its receive buffer and accumulates the weighted average into the output tensor.
+ * [PORT] Combine: senders copy unquantized 16-bit activations; the receiver computes the
+ * weighted average of all expert contributions locally.
+ * cs[d] is rank d's combine send buffer in its receive order; cr[s] is rank s's combine receive
+ * buffer laid out like its dispatch send buffer. */
+void oracle_combine(const oracle_shape* sh, int mode, const uint16_t* expert_y,
+                    const int32_t* expert_rpos, const int32_t* recv_off, const int32_t* send_off,
+                    const int32_t* send_pos, const float* topk_w, uint16_t* cs_buf, uint16_t* cr_buf,
+                    uint16_t* out) {
+    const int N = sh->N, T = sh->T, H = sh->H, R = sh->R;
+    const long TR = (long)T * R;
+    /* shuffle: expert-major row q goes back to receive position rpos[q] */
+    for (int d = 0; d < N; ++d) {
+        long total = recv_off[(long)d * (N + 1) + N];
+        for (long q = 0; q < total; ++q) {
+            long r = expert_rpos[(long)d * sh->B + q];
+            memcpy(cs_buf + ((long)d * sh->B + r) * H, expert_y + ((long)d * sh->B + q) * H, 2L * H);
+        }
+    }
+    /* network back: segment (d -> s) lands where s's dispatch segment for d sat */
+    for (int s = 0; s < N; ++s) {
+        const int32_t* soff = send_off + (long)s * (N + 1);
+        for (int d = 0; d < N; ++d) {
+            long n = soff[d + 1] - soff[d];
+            long src = (long)d * sh->B + recv_off[(long)d * (N + 1) + s];
+            long dst = (long)s * TR + soff[d];
+            memcpy(cr_buf + dst * H, cs_buf + src * H, 2L * n * H);
+        }
+    }
+    /* weighted sum over the token's R slots */
+    for (int s = 0; s < N; ++s) {
+        for (int t = 0; t < T; ++t) {
+            const long base = (long)s * TR + (long)t * R;
+            for (int h = 0; h < H; ++h) {
+                double acc = 0.0;
+                float accf = 0.0f;
+                for (int k = 0; k < R; ++k) {
+                    long row = (long)s * TR + send_pos[base + k];
+                    uint16_t yb = cr_buf[row * H + h];
+                    double y = oracle_bf16_to_double(yb);
+                    if (mode == 0) acc += (double)topk_w[base + k] * y;
+                    else accf = fmaf(topk_w[base + k], (float)y, accf);
+                }
+                out[((long)s * T + t) * H + h] =
+                    oracle_bf16_from_double(mode == 0 ? acc : (double)accf);
+            }
+        }
+    }
+}

@@ -1,0 +1,73 @@
+/*
+ * oracle.h -- plain, slow CPU oracle for MoE expert-parallel dispatch and combine.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only tests/, the smoke check and the CPU-baseline leg of the
+ * benchmark may load this library.  The product (the HIP library and its Python binding)
+ * never calls it and shares no code, header or constant with it.
+ *
+ * Pages cited (by title; sections named in each function's comment):
+ *   [EFA]  "Enabling trillion-parameter models on AWS EFA"
+ *   [PORT] "Efficient and portable mixture-of-experts communication"
+ *   [DSK]  "Lower latency and higher throughput with multi-node DeepSeek deployment"
+ *
+ * Problem statement ([EFA], send-buffer design paragraph): N ranks, each dispatching T tokens,
+ * every token routed to R of E experts; expert e lives on rank e / L with L = E / N.
+ *
+ * All arrays are dense, row-major and rank-major ([N][...]).  Every function asserts its
+ * contract (valid indices, capacity) and aborts on violation: the oracle defines results
+ * for valid inputs only.
+ *
+ * Parity pins: every function here is pinned by CPU tests against brute force, closed forms
+ * and invariants (tests/test_oracle_pins.py).  Nothing here is "parity unpinned".
+ */
+#ifndef MOE_ORACLE_H
+#define MOE_ORACLE_H
+#include <stdint.h>
+
+typedef struct {
+    int N, T, H, E, R;
+    int fp8;   /* 0: bf16 payload (2H bytes per row); 1: e4m3 payload + fp32 scale per 128 */
+    long B;    /* receive-side rows per rank (row stride of every [N][B][...] array) */
+} oracle_shape;
+
+/* Bytes of one dispatched row: the payload, then (fp8 only) its block scales. */
+long oracle_row_bytes(const oracle_shape* sh);
+
+/* Scalar conversions, written from the IEEE-754 binary16-brain-float and OCP E4M3 definitions. */
+uint16_t oracle_bf16_from_double(double x);  /* round to nearest, ties to even */
+double oracle_bf16_to_double(uint16_t b);
+double oracle_e4m3_to_double(uint8_t b);
+
+/* Router: top-R experts of fp32 (logits + bias) and softmax weights over the selected R. */
+void oracle_route(int n_tokens, int E, int R, const float* logits, const float* bias,
+                  int32_t* topk_idx, float* topk_w);
+
+/* Dispatch send: counts, exclusive-scan offsets, positions, packed send rows and metadata. */
+void oracle_dispatch_send(const oracle_shape* sh, const uint8_t* x, const float* x_scale,
+                          const int32_t* topk_idx, int32_t* counts, int32_t* send_off,
+                          int32_t* send_pos, uint8_t* send_buf, int32_t* send_meta);
+
+/* The network: one contiguous copy per (source, destination) segment. */
+void oracle_net_dispatch(const oracle_shape* sh, const int32_t* send_off, const uint8_t* send_buf,
+                         const int32_t* send_meta, uint8_t* recv_buf, int32_t* recv_meta,
+                         int32_t* recv_off);
+
+/* Dispatch receive: shuffle received rows into expert-major order for the grouped GEMM. */
+void oracle_dispatch_recv(const oracle_shape* sh, const int32_t* counts, const int32_t* recv_off,
+                          const uint8_t* recv_buf, const int32_t* recv_meta, uint8_t* expert_x,
+                          float* expert_scale, int32_t* expert_cnt, int32_t* expert_off,
+                          int32_t* expert_src, int32_t* expert_rpos);
+
+/* Stand-in expert (not part of the method): mode 0 identity, mode 1 tagged (y * (64 + e%64)/64). */
+void oracle_expert(const oracle_shape* sh, int mode, const uint8_t* expert_x,
+                   const float* expert_scale, const int32_t* expert_off, uint16_t* expert_y);
+
+/* Combine: rows back to their source slots, then the router-weighted sum.
+ * mode 0: the sum in fp64, rounded once to bf16.
+ * mode 1: an fp32 fused-multiply-add chain in slot order 0..R-1, then rounded to bf16. */
+void oracle_combine(const oracle_shape* sh, int mode, const uint16_t* expert_y,
+                    const int32_t* expert_rpos, const int32_t* recv_off, const int32_t* send_off,
+                    const int32_t* send_pos, const float* topk_w, uint16_t* cs_buf, uint16_t* cr_buf,
+                    uint16_t* out);
+
+#endif

@@ -1,0 +1,66 @@
+"""Plant plausible mistakes in copies of the oracle and check that the pins catch each one.
+
+Each mutant is oracle.c with one textual change (a dropped term, a wrong sign or index, a
+transposed operand, a wrong tie-break or rounding).  It is compiled to a private library and the
+pin suite (tests/test_oracle_pins.py) runs against it in a subprocess; the suite must fail.
+CPU only; nothing here touches the product path.
+"""
+import os
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+MUTANTS = {
+    "route_tie_to_higher_id": ("v[e] > v[best]) best = e;", "v[e] >= v[best]) best = e;"),
+    "route_softmax_drops_last_term": ("        sum += z[k];", "        if (k + 1 < R) sum += z[k];"),
+    "route_bias_sign": ("l + bias[e]", "l - bias[e]"),
+    "send_scan_not_cumulative": ("off[d + 1] = off[d] + n;", "off[d + 1] = n;"),
+    "send_owner_modulo": ("int d = e / L;\n                long pos", "int d = e % N;\n                long pos"),
+    "send_meta_drops_slot": ("meta[0] = (int32_t)((long)e * TR + i);", "meta[0] = (int32_t)((long)e * TR + t * R);"),
+    "send_meta_rank_off_by_one": ("meta[1] = seen[e];", "meta[1] = seen[e] + 1;"),
+    "net_offsets_transposed": ("roff[s + 1] = roff[s] + (soff[d + 1] - soff[d]);",
+                               "roff[s + 1] = roff[s] + (soff[s + 1] - soff[s]);"),
+    "recv_src_uses_dest_rank": ("expert_src[(long)d * sh->B + q] = (int32_t)((long)s * TR + i);",
+                                "expert_src[(long)d * sh->B + q] = (int32_t)((long)d * TR + i);"),
+    "recv_expert_off_not_scanned": ("eoff[j + 1] = eoff[j] + c;", "eoff[j + 1] = c;"),
+    "expert_tag_local_id": ("(double)(64 + e % 64) / 64.0", "(double)(64 + j % 64) / 64.0"),
+    "combine_shuffle_inverted": (
+        "memcpy(cs_buf + ((long)d * sh->B + r) * H, expert_y + ((long)d * sh->B + q) * H, 2L * H);",
+        "memcpy(cs_buf + ((long)d * sh->B + q) * H, expert_y + ((long)d * sh->B + r) * H, 2L * H);"),
+    "combine_net_offsets_transposed": ("long src = (long)d * sh->B + recv_off[(long)d * (N + 1) + s];",
+                                       "long src = (long)d * sh->B + recv_off[(long)s * (N + 1) + d];"),
+    "combine_weight_of_slot0": ("acc += (double)topk_w[base + k] * y;", "acc += (double)topk_w[base] * y;"),
+    "combine_drops_last_slot": ("for (int k = 0; k < R; ++k) {\n                    long row",
+                                "for (int k = 0; k < R - 1; ++k) {\n                    long row"),
+    "bf16_truncates": ("double q = nearbyint(ldexp(a, -ulp_exp));", "double q = floor(ldexp(a, -ulp_exp));"),
+    "bf16_one_bit_short": ("int ulp_exp = ex - 8;", "int ulp_exp = ex - 7;"),
+    "e4m3_wrong_bias": ("ldexp((double)(8 + m), e - 10)", "ldexp((double)(8 + m), e - 9)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name):
+    before, after = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(before) == 1, f"mutation site for {name} not unique"
+    with tempfile.TemporaryDirectory() as tmp:
+        c = os.path.join(tmp, "oracle.c")
+        with open(c, "w") as f:
+            f.write(src.replace(before, after))
+        with open(os.path.join(tmp, "oracle.h"), "w") as f:
+            f.write(open(os.path.join(ROOT, "oracle", "oracle.h")).read())
+        so = os.path.join(tmp, "liboracle.so")
+        subprocess.check_call(["gcc", *oracle.CFLAGS, c, "-o", so, "-lm"])
+        env = dict(os.environ, MOE_ORACLE_LIB=so)
+        p = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                            "-k", "not groupgemm and not qwen_prefill and not receive_bound",
+                            os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                           cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+        assert p.returncode != 0, f"mutant {name} survived the pins:\n{p.stdout[-2000:]}"
