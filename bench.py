@@ -1,0 +1,266 @@
+"""Benchmark: MoE dispatch + combine on one MI355X (all N logical ranks in one GPU's HBM).
+
+One step = one pass of the whole path over one batch: route -> dispatch send -> network ->
+dispatch receive -> combine (shuffle, network back, weighted sum).  The stand-in expert between
+dispatch and combine is not part of the metric: for bf16 identity experts it is no work at all
+(combine reads the dispatched tensor), for fp8 it runs between the timed phases.
+
+Prints ONE JSON line.  value = effective HBM GB/s of dispatch + combine = algorithmic bytes /
+(dispatch + combine time), both phases timed with HIP events on the stream the kernels run on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "dispatch+combine µs/layer and effective HBM GB/s (fraction of MI355X peak)"
+PEAK_HBM_GBS = 8000.0
+HEADLINE = "deepseek_v3_decode"
+EXTRA = ["deepseek_v3_decode_fp8", "kimi_k2_worst"]
+
+
+def alg_bytes(c) -> dict:
+    """Compulsory bytes each ABI call reads and writes (every routed row is valid)."""
+    N, T, H, E, R, L = c.N, c.T, c.H, c.E, c.R, c.L
+    NT, M = N * T, N * T * R
+    xrow = (H + 4 * (H // 128)) if c.fp8 else 2 * H   # a token's payload (+ scales)
+    P = xrow                                          # one dispatched row
+    Pc = 2 * H                                        # one combine row (bf16)
+    bias = E * 4 if c.bias != "none" else 0
+    b = {}
+    b["route"] = NT * E * 4 + bias + M * 8
+    b["dispatch_send"] = (M * 4 + NT * xrow) + (N * E * 4 + N * (N + 1) * 4 + M * 4 + M * 8 + M * P)
+    b["net_dispatch"] = (M * (P + 8) + N * (N + 1) * 4) + (M * (P + 8) + N * (N + 1) * 4)
+    b["dispatch_recv"] = (M * (P + 8) + N * E * 4 + N * (N + 1) * 4) + (M * P + M * 8 + N * (2 * L + 1) * 4)
+    b["combine_pack"] = (M * Pc + M * 4 + N * (N + 1) * 4) + M * Pc
+    b["combine_net"] = (M * Pc + 2 * N * (N + 1) * 4) + M * Pc
+    b["combine_wsum"] = (M * Pc + M * 8) + NT * Pc
+    b["combine"] = b["combine_pack"] + b["combine_net"] + b["combine_wsum"]
+    b["dispatch"] = b["route"] + b["dispatch_send"] + b["net_dispatch"] + b["dispatch_recv"]
+    b["total"] = b["dispatch"] + b["combine"]
+    return b
+
+
+def run_workload(name, steps, warmup, check=True):
+    import numpy as np
+    import torch
+
+    import combine_moe_route_top_amd as moe
+    import moe_synth as ms
+
+    c = ms.CONFIGS[name]
+    inp = ms.config_inputs(c)
+    b = moe.alloc_buffers(c.N, c.T, c.H, c.E, c.R, c.fp8)
+    b.logits.copy_(torch.from_numpy(inp["logits"]))
+    use_bias = inp["bias"] is not None
+    if use_bias:
+        b.bias.copy_(torch.from_numpy(inp["bias"]))
+    x = inp["x"]
+    b.x.copy_(torch.from_numpy(x.view(np.int16) if x.dtype == np.uint16 else x))
+    if c.fp8:
+        b.x_scale.copy_(torch.from_numpy(inp["x_scale"]))
+    stream = torch.cuda.current_stream()
+    sh = b.shape
+    y = b.expert_y if c.fp8 else b.expert_x   # identity expert: bf16 combine reads expert_x
+
+    names = ["route", "dispatch_send", "net_dispatch", "dispatch_recv", "stub", "combine"]
+
+    def step(ev=None):
+        def rec(i):
+            if ev is not None:
+                ev[i].record(stream)
+        rec(0)
+        moe.moe_route(sh, b.logits, b.bias if use_bias else None, b.topk_idx, b.topk_w, stream)
+        rec(1)
+        moe.moe_dispatch_send(sh, b.x, b.x_scale, b.topk_idx, b.counts, b.send_off, b.send_pos,
+                              b.send_buf, b.send_meta, b.workspace, stream)
+        rec(2)
+        moe.moe_net_dispatch(sh, b.send_off, b.send_buf, b.send_meta, b.recv_buf, b.recv_meta,
+                             b.recv_off, stream)
+        rec(3)
+        moe.moe_dispatch_recv(sh, b.counts, b.recv_off, b.recv_buf, b.recv_meta, b.expert_x,
+                              b.expert_scale, b.expert_cnt, b.expert_off, b.expert_src,
+                              b.expert_rpos, b.workspace, stream)
+        rec(4)
+        if c.fp8:
+            moe.moe_expert_stub(sh, 0, b.expert_x, b.expert_scale, b.expert_off, b.expert_y, stream)
+        rec(5)
+        moe.moe_combine(sh, y, b.expert_rpos, b.recv_off, b.send_off, b.send_pos, b.topk_w,
+                        b.cs_buf, b.cr_buf, b.out, stream)
+        rec(6)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {n: 0.0 for n in names}
+    for k in range(steps):
+        for i, n in enumerate(names):
+            per[n] += evs[k][i].elapsed_time(evs[k][i + 1]) * 1e3 / steps   # us
+    dispatch_us = per["route"] + per["dispatch_send"] + per["net_dispatch"] + per["dispatch_recv"]
+    combine_us = per["combine"]
+    layer_us = dispatch_us + combine_us
+    ab = alg_bytes(c)
+    res = dict(workload=name, desc=c.desc, dtype=c.dtype, N=c.N, T=c.T, H=c.H, E=c.E, R=c.R,
+               layer_us=layer_us, dispatch_us=dispatch_us, combine_us=combine_us,
+               wall_ms_per_step=wall * 1e3 / steps,
+               per_call_us={n: round(v, 2) for n, v in per.items()},
+               alg_bytes=ab, gbs=ab["total"] / (layer_us * 1e-6) / 1e9)
+    res["per_call_gbs"] = {n: round(ab[n] / (per[n] * 1e-6) / 1e9, 1)
+                           for n in ["route", "dispatch_send", "net_dispatch", "dispatch_recv", "combine"]}
+    if check:
+        res["check"] = closed_form_check(b, c)
+    status = int(b.status.item())
+    if status != 0:
+        raise RuntimeError(f"device status word {status} ({moe.moe_strerror(status)})")
+    del b
+    torch.cuda.empty_cache()
+    return res
+
+
+def closed_form_check(b, c) -> str:
+    """Identity experts: out == bf16(y * sum_k w_k) up to 1 bf16 ulp for every token (y the
+    dispatched value), and each rank's counts sum to T*R.  A property check at full size; the
+    element-wise oracle comparison lives in the GPU parity tests."""
+    import torch
+    sw = b.topk_w.double().sum(1).view(c.N, c.T, 1)
+    if c.fp8:
+        xv = b.x.view(torch.float8_e4m3fn).double() * b.x_scale.double().repeat_interleave(128, dim=2)
+    else:
+        xv = b.x.view(torch.bfloat16).double()
+    want = (xv * sw).to(torch.float32).to(torch.bfloat16) if not c.fp8 else \
+        (xv.to(torch.bfloat16).double() * sw).to(torch.float32).to(torch.bfloat16)
+    got = b.out.view(torch.bfloat16)
+    a = want.view(torch.int16).int()
+    g = got.view(torch.int16).int()
+    key = lambda u: torch.where(u < 0, -(u & 0x7FFF), u & 0x7FFF)  # noqa: E731
+    ulp = (key(a) - key(g)).abs().max().item()
+    counts_ok = bool((b.counts.sum(1) == c.T * c.R).all().item())
+    if ulp > 2 or not counts_ok:  # the torch reference itself rounds twice (fp64->fp32->bf16)
+        raise RuntimeError(f"closed-form check failed: max {ulp} bf16 ulp, counts ok {counts_ok}")
+    return f"ok (max {ulp} bf16 ulp vs identity closed form; counts sum to T*R)"
+
+
+def dominant_kernel(res) -> dict:
+    """Roofline of the dominant single-kernel call: the network stand-in (k_net_dispatch plus
+    the tiny recv_off scan k_net_prep, both inside moe_net_dispatch)."""
+    ab = res["alg_bytes"]
+    us = res["per_call_us"]["net_dispatch"]
+    achieved = ab["net_dispatch"] / (us * 1e-6) / 1e9
+    return {"kernel": "k_net_dispatch (+k_net_prep) via moe_net_dispatch", "bound": "hbm",
+            "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+            "bytes_per_launch": ab["net_dispatch"], "us_per_launch": round(us, 2)}
+
+
+def cpu_baseline(name, budget_s=25.0) -> dict:
+    """The oracle, as it stands, on one full layer of the workload on the host cores."""
+    import numpy as np
+
+    import moe_synth as ms
+    import oracle
+    c = ms.CONFIGS[name]
+    inp = ms.config_inputs(c)
+    ab = alg_bytes(c)
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        sh = oracle.shape(c.N, c.T, c.H, c.E, c.R, c.fp8)
+        idx, w = oracle.route(inp["logits"], inp["bias"], c.R)
+        r = oracle.dispatch_send(sh, inp["x"], inp["x_scale"], idx.reshape(c.N, -1))
+        sh = oracle.packed_shape(c.N, c.T, c.H, c.E, c.R, c.fp8,
+                                 np.diff(r["send_off"], axis=1).sum(axis=0))
+        r.update(oracle.net_dispatch(sh, r["send_off"], r["send_buf"], r["send_meta"]))
+        r.update(oracle.dispatch_recv(sh, r["counts"], r["recv_off"], r["recv_buf"], r["recv_meta"]))
+        t1 = time.perf_counter()
+        y = oracle.expert(sh, 0, r["expert_x"], r["expert_scale"], r["expert_off"])
+        t2 = time.perf_counter()
+        oracle.combine(sh, 0, y, r["expert_rpos"], r["recv_off"], r["send_off"], r["send_pos"], w)
+        t3 = time.perf_counter()
+        times.append((t1 - t0) + (t3 - t2))
+        if time.perf_counter() - t_start > budget_s * 0.5 or len(times) >= 3:
+            break
+    t = float(np.median(times))
+    return {"value": round(ab["total"] / t / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "us_per_layer": round(t * 1e6, 1),
+            "sample": f"one full {name} layer (all {c.N} ranks) through the single-threaded C oracle "
+                      f"(route, dispatch, network, unpack, combine; stand-in expert excluded), "
+                      f"median of {len(times)}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--extra", default=",".join(EXTRA),
+                    help="comma-separated workloads reported beside the headline ('' for none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-check", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the N expert-parallel ranks are simulated inside one "
+              "GPU's HBM (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+
+    head = run_workload(args.workload, args.steps, args.warmup, check=not args.no_check)
+    extras = {}
+    for name in [e for e in args.extra.split(",") if e and e != args.workload]:
+        r = run_workload(name, args.steps, args.warmup, check=not args.no_check)
+        extras[name] = {k: (round(v, 2) if isinstance(v, float) else v) for k, v in r.items()
+                        if k in ("layer_us", "dispatch_us", "combine_us", "gbs", "per_call_us",
+                                 "per_call_gbs", "check", "dtype")}
+        extras[name]["frac_of_peak"] = round(r["gbs"] / PEAK_HBM_GBS, 4)
+    line = {
+        "metric": METRIC,
+        "value": round(head["gbs"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["wall_ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if head["dtype"] == "bf16" else "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "N": head["N"], "T": head["T"], "H": head["H"],
+                   "E": head["E"], "R": head["R"], "payload": head["dtype"],
+                   "ranks_simulated_on_one_gpu": head["N"]},
+        "us_per_layer": round(head["layer_us"], 2),
+        "dispatch_us": round(head["dispatch_us"], 2),
+        "combine_us": round(head["combine_us"], 2),
+        "frac_of_peak": round(head["gbs"] / PEAK_HBM_GBS, 4),
+        "alg_bytes_per_layer": head["alg_bytes"]["total"],
+        "per_call_us": head["per_call_us"],
+        "per_call_gbs": head["per_call_gbs"],
+        "check": head.get("check"),
+        "roofline": dominant_kernel(head),
+        "other_workloads": extras,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.workload)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,217 @@
+// api.hip -- the extern "C" entry points of libmoe (declared in include/moe.h): host-side
+// validation, buffer sizes, and the kernel launches of each step.  No allocation, no
+// synchronisation: every call enqueues on the caller's stream and returns.
+#include <limits.h>
+#include <stdint.h>
+
+#include "common.cuh"
+
+namespace moe {
+hipError_t launch_route(const Dims&, const float*, const float*, int32_t*, float*, hipStream_t);
+size_t send_workspace_bytes(const Dims&);
+size_t recv_workspace_bytes(const Dims&);
+hipError_t launch_dispatch_send(const Dims&, const void*, const float*, const int32_t*, int32_t*,
+                                int32_t*, int32_t*, void*, int32_t*, void*, hipStream_t);
+hipError_t launch_net_dispatch(const Dims&, const int32_t*, const void*, const int32_t*, void*,
+                               int32_t*, int32_t*, hipStream_t);
+hipError_t launch_dispatch_recv(const Dims&, const int32_t*, const int32_t*, const void*,
+                                const int32_t*, void*, float*, int32_t*, int32_t*, int32_t*,
+                                int32_t*, void*, hipStream_t);
+hipError_t launch_expert_stub(const Dims&, int, const void*, const float*, const int32_t*,
+                              uint16_t*, hipStream_t);
+hipError_t launch_combine(const Dims&, const uint16_t*, const int32_t*, const int32_t*,
+                          const int32_t*, const int32_t*, const float*, uint16_t*, uint16_t*,
+                          uint16_t*, hipStream_t);
+}  // namespace moe
+
+using moe::Dims;
+
+namespace {
+
+constexpr int kMaxN = 1024;
+constexpr int kMaxE = 1024;
+constexpr int kMaxR = 64;
+
+// Validate a shape and derive the kernels' view of it.  Returns MOE_OK or an error code.
+int make_dims(const moe_shape* sh, Dims* D) {
+    if (!sh) return MOE_EINVAL;
+    const long long N = sh->N, T = sh->T, H = sh->H, E = sh->E, R = sh->R;
+    if (N < 1 || T < 1 || H < 1 || E < 1 || R < 1) return MOE_EINVAL;
+    if (E % N != 0 || R > E) return MOE_EINVAL;
+    if (sh->dtype != MOE_BF16 && sh->dtype != MOE_FP8_E4M3) return MOE_EINVAL;
+    if (N > kMaxN || E > kMaxE || R > kMaxR) return MOE_EUNSUPPORTED;
+    const bool fp8 = sh->dtype == MOE_FP8_E4M3;
+    if (!fp8 && H % 8 != 0) return MOE_EUNSUPPORTED;   // 16-byte rows
+    if (fp8 && H % 512 != 0) return MOE_EUNSUPPORTED;  // 16-byte rows of codes and of scales
+    const long long L = E / N;
+    const long long TR = T * R;
+    if (N * TR > INT_MAX || E * TR > INT_MAX) return MOE_EUNSUPPORTED;  // int32 indices, meta
+    const long long tight = N * T * (R < L ? R : L);
+    const long long bound = N * T * (R > L ? R : L);
+    const long long B = sh->capacity == 0 ? bound : sh->capacity;
+    if (B < tight) return MOE_EINVAL;
+    if (B > INT_MAX) return MOE_EUNSUPPORTED;
+    if (H > (1 << 20)) return MOE_EUNSUPPORTED;
+    D->N = (int)N;
+    D->T = (int)T;
+    D->H = (int)H;
+    D->E = (int)E;
+    D->R = (int)R;
+    D->L = (int)L;
+    D->fp8 = fp8;
+    D->TR = (int)TR;
+    D->B = B;
+    D->P = fp8 ? (int)(H + H / 32) : (int)(2 * H);
+    D->P16 = D->P / 16;
+    D->X16 = fp8 ? (int)(H / 16) : (int)(2 * H / 16);
+    D->nsc = (int)(H / 128);
+    D->Y16 = (int)(2 * H / 16);
+    D->status = sh->status;
+    return MOE_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return p && (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_strerror(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_EINVAL: return "invalid argument (shape, null or misaligned pointer, inconsistent tables)";
+        case MOE_EUNSUPPORTED: return "unsupported shape for these kernels";
+        case MOE_EHIP: return "HIP launch error";
+        case MOE_EBADIDX: return "expert id out of range or repeated within a token";
+        default: return "unknown status";
+    }
+}
+
+int moe_sizes(const moe_shape* shape, moe_sizes_t* out) {
+    Dims D;
+    int rc = make_dims(shape, &D);
+    if (rc) return rc;
+    if (!out) return MOE_EINVAL;
+    const int64_t N = D.N, T = D.T, H = D.H, E = D.E, R = D.R, L = D.L, B = D.B, P = D.P;
+    const int64_t NT = N * T, M = N * T * R;
+    const int64_t xb = D.fp8 ? 1 : 2;
+    out->capacity = B;
+    out->row_bytes = P;
+    out->logits = NT * E * 4;
+    out->bias = E * 4;
+    out->topk_idx = M * 4;
+    out->topk_w = M * 4;
+    out->x = NT * H * xb;
+    out->x_scale = D.fp8 ? NT * (H / 128) * 4 : 0;
+    out->counts = N * E * 4;
+    out->send_off = N * (N + 1) * 4;
+    out->send_pos = M * 4;
+    out->send_buf = M * P;
+    out->send_meta = M * 8;
+    out->recv_buf = N * B * P;
+    out->recv_meta = N * B * 8;
+    out->recv_off = N * (N + 1) * 4;
+    out->expert_x = N * B * H * xb;
+    out->expert_scale = D.fp8 ? N * B * (H / 128) * 4 : 0;
+    out->expert_cnt = N * L * 4;
+    out->expert_off = N * (L + 1) * 4;
+    out->expert_src = N * B * 4;
+    out->expert_rpos = N * B * 4;
+    out->expert_y = N * B * H * 2;
+    out->cs_buf = N * B * H * 2;
+    out->cr_buf = M * H * 2;
+    out->out = NT * H * 2;
+    size_t ws = moe::send_workspace_bytes(D);
+    size_t wr = moe::recv_workspace_bytes(D);
+    out->workspace = (int64_t)(ws > wr ? ws : wr);
+    return MOE_OK;
+}
+
+int moe_route(const moe_shape* shape, const float* logits, const float* bias, int32_t* topk_idx,
+              float* topk_w, void* stream) {
+    Dims D;
+    int rc = make_dims(shape, &D);
+    if (rc) return rc;
+    if (!aligned(logits, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4)) return MOE_EINVAL;
+    if (bias && !aligned(bias, 4)) return MOE_EINVAL;
+    return hip_status(moe::launch_route(D, logits, bias, topk_idx, topk_w, (hipStream_t)stream));
+}
+
+int moe_dispatch_send(const moe_shape* shape, const void* x, const float* x_scale,
+                      const int32_t* topk_idx, int32_t* counts, int32_t* send_off, int32_t* send_pos,
+                      void* send_buf, int32_t* send_meta, void* workspace, void* stream) {
+    Dims D;
+    int rc = make_dims(shape, &D);
+    if (rc) return rc;
+    if (!aligned(x, 16) || !aligned(send_buf, 16) || !aligned(send_meta, 8)) return MOE_EINVAL;
+    if (D.fp8 && !aligned(x_scale, 16)) return MOE_EINVAL;
+    if (!aligned(topk_idx, 4) || !aligned(counts, 4) || !aligned(send_off, 4) || !aligned(send_pos, 4))
+        return MOE_EINVAL;
+    if (moe::send_workspace_bytes(D) > 0 && !aligned(workspace, 4)) return MOE_EINVAL;
+    return hip_status(moe::launch_dispatch_send(D, x, x_scale, topk_idx, counts, send_off, send_pos,
+                                                send_buf, send_meta, workspace, (hipStream_t)stream));
+}
+
+int moe_net_dispatch(const moe_shape* shape, const int32_t* send_off, const void* send_buf,
+                     const int32_t* send_meta, void* recv_buf, int32_t* recv_meta, int32_t* recv_off,
+                     void* stream) {
+    Dims D;
+    int rc = make_dims(shape, &D);
+    if (rc) return rc;
+    if (!aligned(send_off, 4) || !aligned(send_buf, 16) || !aligned(send_meta, 8) ||
+        !aligned(recv_buf, 16) || !aligned(recv_meta, 8) || !aligned(recv_off, 4))
+        return MOE_EINVAL;
+    return hip_status(moe::launch_net_dispatch(D, send_off, send_buf, send_meta, recv_buf, recv_meta,
+                                               recv_off, (hipStream_t)stream));
+}
+
+int moe_dispatch_recv(const moe_shape* shape, const int32_t* counts, const int32_t* recv_off,
+                      const void* recv_buf, const int32_t* recv_meta, void* expert_x,
+                      float* expert_scale, int32_t* expert_cnt, int32_t* expert_off,
+                      int32_t* expert_src, int32_t* expert_rpos, void* workspace, void* stream) {
+    Dims D;
+    int rc = make_dims(shape, &D);
+    if (rc) return rc;
+    if (!aligned(counts, 4) || !aligned(recv_off, 4) || !aligned(recv_buf, 16) ||
+        !aligned(recv_meta, 8) || !aligned(expert_x, 16) || !aligned(expert_cnt, 4) ||
+        !aligned(expert_off, 4) || !aligned(expert_src, 4) || !aligned(expert_rpos, 4) ||
+        !aligned(workspace, 4))
+        return MOE_EINVAL;
+    if (D.fp8 && !aligned(expert_scale, 16)) return MOE_EINVAL;
+    return hip_status(moe::launch_dispatch_recv(D, counts, recv_off, recv_buf, recv_meta, expert_x,
+                                                expert_scale, expert_cnt, expert_off, expert_src,
+                                                expert_rpos, workspace, (hipStream_t)stream));
+}
+
+int moe_combine(const moe_shape* shape, const uint16_t* expert_y, const int32_t* expert_rpos,
+                const int32_t* recv_off, const int32_t* send_off, const int32_t* send_pos,
+                const float* topk_w, uint16_t* cs_buf, uint16_t* cr_buf, uint16_t* out, void* stream) {
+    Dims D;
+    int rc = make_dims(shape, &D);
+    if (rc) return rc;
+    if (!aligned(expert_y, 16) || !aligned(expert_rpos, 4) || !aligned(recv_off, 4) ||
+        !aligned(send_off, 4) || !aligned(send_pos, 4) || !aligned(topk_w, 4) ||
+        !aligned(cs_buf, 16) || !aligned(cr_buf, 16) || !aligned(out, 16))
+        return MOE_EINVAL;
+    return hip_status(moe::launch_combine(D, expert_y, expert_rpos, recv_off, send_off, send_pos,
+                                          topk_w, cs_buf, cr_buf, out, (hipStream_t)stream));
+}
+
+int moe_expert_stub(const moe_shape* shape, int32_t mode, const void* expert_x,
+                    const float* expert_scale, const int32_t* expert_off, uint16_t* expert_y,
+                    void* stream) {
+    Dims D;
+    int rc = make_dims(shape, &D);
+    if (rc) return rc;
+    if (mode != 0 && mode != 1) return MOE_EINVAL;
+    if (!aligned(expert_x, 16) || !aligned(expert_off, 4) || !aligned(expert_y, 16)) return MOE_EINVAL;
+    if (D.fp8 && !aligned(expert_scale, 4)) return MOE_EINVAL;
+    return hip_status(moe::launch_expert_stub(D, mode, expert_x, expert_scale, expert_off, expert_y,
+                                              (hipStream_t)stream));
+}
+
+}  // extern "C"

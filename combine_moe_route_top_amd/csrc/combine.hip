@@ -1,0 +1,226 @@
+// combine.hip -- MoE combine: shuffle the expert outputs back into receive order, move them
+// back with one contiguous write per (rank, peer) segment, and take the router-weighted sum.
+// Also the stand-in expert between dispatch and combine.
+//
+// Pages: [EFA] = "Enabling trillion-parameter models on AWS EFA" (combine paragraphs: the
+// metadata is known from dispatch, tokens are shuffled, sent back with one write per peer and
+// accumulated from the receive buffer into the output); [PORT] = "Efficient and portable
+// mixture-of-experts communication" (section Combine: 16-bit activations, the receiver forms
+// the weighted average of all expert contributions into an externally allocated tensor).
+#include "common.cuh"
+
+namespace moe {
+
+__device__ __forceinline__ void rank_bases_c(const int32_t* table, int stride, int col, int N, int* gb) {
+    if (wave_id() != 0) return;
+    int carry = 0;
+    for (int b = 0; b < N; b += kWave) {
+        const int dd = b + lane_id();
+        const int v = dd < N ? table[(long)dd * stride + col] : 0;
+        const int inc = wave_incl_scan(v);
+        if (dd < N) gb[dd] = carry + inc - v;
+        carry += readlane(inc, kWave - 1);
+    }
+    if (lane_id() == 0) gb[N] = carry;
+}
+
+// ------------------------------------------------------------------ stand-in expert
+
+// e4m3 (OCP: bias 7, 3 mantissa bits, S.1111.111 = NaN) to double, exactly.
+__device__ __forceinline__ double e4m3_to_f64(uint32_t b) {
+    const int e = (b >> 3) & 15, m = b & 7;
+    double v;
+    if (e == 15 && m == 7) v = __longlong_as_double(0x7FF8000000000000ll);
+    else if (e == 0) v = ldexp((double)m, -9);
+    else v = ldexp((double)(8 + m), e - 10);
+    return (b & 0x80) ? -v : v;
+}
+
+// Round a double to bf16 (nearest even) without double rounding: first to fp32 rounding to odd
+// (sticky low bit), which keeps enough bits for the second, nearest-even, rounding to be exact.
+__device__ __forceinline__ uint32_t f64_to_bf16(double x) {
+    float f = (float)x;
+    if ((double)f != x && !isnan(x) && !isinf(f)) {
+        uint32_t u = __float_as_uint(f);
+        if (fabs((double)f) > fabs(x)) u -= 1;  // step back toward zero: the truncated value
+        u |= 1;
+        f = __uint_as_float(u);
+    }
+    return f32_to_bf16(f);
+}
+
+// One wave per expert-major row (flattened over ranks).  mode 0: identity; mode 1: times
+// (64 + e % 64) / 64.  The product is formed exactly in fp64 and rounded once to bf16.
+__global__ __launch_bounds__(kBlock) void k_expert_stub(Dims D, int mode, const uint8_t* __restrict__ expert_x,
+                                                        const float* __restrict__ expert_scale,
+                                                        const int32_t* __restrict__ expert_off,
+                                                        uint16_t* __restrict__ expert_y) {
+    extern __shared__ int gb[];
+    const int N = D.N, L = D.L;
+    rank_bases_c(expert_off, L + 1, L, N, gb);
+    __syncthreads();
+    const long G = (long)blockIdx.x * kWavesPerBlock + wave_id();
+    if (G >= gb[N]) return;
+    const int d = wave_count_le(gb + 1, N, G);
+    const long q = G - gb[d];
+    const int j = wave_count_le(expert_off + (long)d * (L + 1) + 1, L, q);
+    const int e = d * L + j;
+    const double tag = mode == 1 ? (double)(64 + e % 64) / 64.0 : 1.0;
+    const size_t row = (size_t)d * D.B + q;
+    const int H = D.H;
+    uint16_t* y = expert_y + row * H;
+    // 8 outputs per lane per step: one 16-byte store
+    for (int h0 = lane_id() * 8; h0 < H; h0 += kWave * 8) {
+        uint32_t o[8];
+        if (D.fp8) {
+            const uint8_t* xq = expert_x + row * H;
+            const float sc = expert_scale[row * D.nsc + h0 / 128];
+            const uint2 codes = *reinterpret_cast<const uint2*>(xq + h0);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const uint32_t b = ((u < 4 ? codes.x : codes.y) >> (8 * (u & 3))) & 0xFF;
+                o[u] = f64_to_bf16(e4m3_to_f64(b) * (double)sc * tag);
+            }
+        } else {
+            const uint16_t* xb = reinterpret_cast<const uint16_t*>(expert_x) + row * H;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(xb + h0);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const uint32_t b = (v[u >> 1] >> (16 * (u & 1))) & 0xFFFF;
+                o[u] = f64_to_bf16((double)bf16_to_f32(b) * tag);
+            }
+        }
+        u32x4 w;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) w[u] = o[2 * u] | (o[2 * u + 1] << 16);
+        *reinterpret_cast<u32x4*>(y + h0) = w;
+    }
+}
+
+// ------------------------------------------------------------------ combine
+
+// Shuffle: cs[d][expert_rpos[q]] = y[d][q].  One wave per expert-major row, flattened.
+template <int U>
+__global__ __launch_bounds__(kBlock) void k_combine_pack(Dims D, const uint16_t* __restrict__ expert_y,
+                                                         const int32_t* __restrict__ expert_rpos,
+                                                         const int32_t* __restrict__ recv_off,
+                                                         uint16_t* __restrict__ cs_buf) {
+    extern __shared__ int gb[];
+    const int N = D.N;
+    rank_bases_c(recv_off, N + 1, N, N, gb);
+    __syncthreads();
+    const long G = (long)blockIdx.x * kWavesPerBlock + wave_id();
+    if (G >= gb[N]) return;
+    const int d = wave_count_le(gb + 1, N, G);
+    const long q = G - gb[d];
+    const long r = expert_rpos[(size_t)d * D.B + q];
+    if (r < 0 || r >= D.B) {
+        set_status(D.status, MOE_EINVAL);
+        return;
+    }
+    wave_copy_row<U>(reinterpret_cast<const u32x4*>(expert_y + ((size_t)d * D.B + q) * D.H),
+                     reinterpret_cast<u32x4*>(cs_buf + ((size_t)d * D.B + r) * D.H), D.Y16);
+}
+
+// Network back: row i of rank s's combine receive buffer comes from segment (d -> s) of rank
+// d's combine send buffer.  One wave per row of cr.
+template <int U>
+__global__ __launch_bounds__(kBlock) void k_combine_net(Dims D, const uint16_t* __restrict__ cs_buf,
+                                                        const int32_t* __restrict__ recv_off,
+                                                        const int32_t* __restrict__ send_off,
+                                                        uint16_t* __restrict__ cr_buf) {
+    const long g = (long)blockIdx.x * kWavesPerBlock + wave_id();
+    const int N = D.N;
+    if (g >= (long)N * D.TR) return;
+    const long s = g / D.TR;
+    const int i = (int)(g - s * D.TR);
+    const int32_t* so = send_off + s * (N + 1);
+    if (i >= so[N]) return;
+    const int d = wave_count_le(so, N, i) - 1;
+    const long r = recv_off[(long)d * (N + 1) + s] + (i - so[d]);
+    if (d < 0 || r < 0 || r >= D.B) {
+        set_status(D.status, MOE_EINVAL);
+        return;
+    }
+    wave_copy_row<U>(reinterpret_cast<const u32x4*>(cs_buf + ((size_t)d * D.B + r) * D.H),
+                     reinterpret_cast<u32x4*>(cr_buf + ((size_t)s * D.TR + i) * D.H), D.Y16);
+}
+
+// Weighted sum: out[s][t] = bf16(sum_k w[k] * cr[s][send_pos[k]]), fp32 fused multiply-adds in
+// slot order k = 0..R-1; dropped slots (send_pos < 0) add nothing.  One wave per token; each
+// lane owns 8 hidden values (one 16-byte chunk) per step, loads up to 8 slots ahead.
+__global__ __launch_bounds__(kBlock) void k_wsum(Dims D, const uint16_t* __restrict__ cr_buf,
+                                                 const int32_t* __restrict__ send_pos,
+                                                 const float* __restrict__ topk_w,
+                                                 uint16_t* __restrict__ out) {
+    const long tok = (long)blockIdx.x * kWavesPerBlock + wave_id();
+    if (tok >= (long)D.N * D.T) return;
+    const int lane = lane_id();
+    const int R = D.R;
+    const long s = tok / D.T;
+    const int my_pos = lane < R ? send_pos[tok * R + lane] : -1;
+    const float my_w = lane < R ? topk_w[tok * R + lane] : 0.0f;
+    const u32x4* rank_rows = reinterpret_cast<const u32x4*>(cr_buf + (size_t)s * D.TR * D.H);
+    u32x4* orow = reinterpret_cast<u32x4*>(out + (size_t)tok * D.H);
+    const int n16 = D.Y16;
+    for (int c = lane; c < n16; c += kWave) {
+        float acc[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc[u] = 0.0f;
+        for (int k0 = 0; k0 < R; k0 += 8) {
+            u32x4 v[8];
+            float wk[8];
+            bool ok[8];
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                const int k = k0 + kk;
+                const int pos = k < R ? readlane(my_pos, k) : -1;
+                ok[kk] = pos >= 0 && pos < D.TR;
+                wk[kk] = k < R ? readlane_f(my_w, k) : 0.0f;
+                if (ok[kk]) v[kk] = rank_rows[(size_t)pos * n16 + c];
+            }
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                if (!ok[kk]) continue;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const float y = bf16_to_f32((v[kk][u >> 1] >> (16 * (u & 1))) & 0xFFFF);
+                    acc[u] = __builtin_fmaf(wk[kk], y, acc[u]);
+                }
+            }
+        }
+        u32x4 o;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) o[u] = f32_to_bf16(acc[2 * u]) | (f32_to_bf16(acc[2 * u + 1]) << 16);
+        orow[c] = o;
+    }
+}
+
+// ------------------------------------------------------------------ launchers
+
+hipError_t launch_expert_stub(const Dims& D, int mode, const void* expert_x, const float* expert_scale,
+                              const int32_t* expert_off, uint16_t* expert_y, hipStream_t st) {
+    const long rows = (long)D.N * D.TR;
+    hipLaunchKernelGGL(k_expert_stub, dim3((rows + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock),
+                       (D.N + 1) * 4, st, D, mode, (const uint8_t*)expert_x, expert_scale, expert_off,
+                       expert_y);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(const Dims& D, const uint16_t* expert_y, const int32_t* expert_rpos,
+                          const int32_t* recv_off, const int32_t* send_off, const int32_t* send_pos,
+                          const float* topk_w, uint16_t* cs_buf, uint16_t* cr_buf, uint16_t* out,
+                          hipStream_t st) {
+    const long rows = (long)D.N * D.TR;
+    const dim3 grid_rows((rows + kWavesPerBlock - 1) / kWavesPerBlock);
+    hipLaunchKernelGGL(k_combine_pack<8>, grid_rows, dim3(kBlock), (D.N + 1) * 4, st, D, expert_y,
+                       expert_rpos, recv_off, cs_buf);
+    hipLaunchKernelGGL(k_combine_net<8>, grid_rows, dim3(kBlock), 0, st, D, (const uint16_t*)cs_buf,
+                       recv_off, send_off, cr_buf);
+    const long ntok = (long)D.N * D.T;
+    hipLaunchKernelGGL(k_wsum, dim3((ntok + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock), 0, st, D,
+                       (const uint16_t*)cr_buf, send_pos, topk_w, out);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,180 @@
+/*
+ * moe.h -- C ABI of libmoe: MoE expert-parallel token dispatch and combine on one MI355X.
+ *
+ * Pages cited by title:
+ *   [EFA]  "Enabling trillion-parameter models on AWS EFA"
+ *   [PORT] "Efficient and portable mixture-of-experts communication"
+ *   [DSK]  "Lower latency and higher throughput with multi-node DeepSeek deployment"
+ *
+ * The problem ([EFA], send-buffer design paragraph): N ranks each dispatch T tokens of hidden
+ * size H; every token goes to R of E experts; expert e lives on rank e / L, L = E / N.  Here all
+ * N ranks live in one GPU's memory: every array below is rank-major ([N][...]) and a device copy
+ * kernel stands in for the network between the send and receive halves.
+ *
+ * Conventions for every call:
+ *  - Every pointer is a device pointer owned by the caller.  The library never allocates, frees
+ *    or synchronises; each call only enqueues kernels on `stream` (a hipStream_t; NULL is the
+ *    legacy default stream) and returns.  Outputs are valid once the stream reaches that point.
+ *  - Return value: MOE_OK, or a negative moe_status after host-side validation (nothing is
+ *    enqueued then), or MOE_EHIP if a launch failed.
+ *  - Payload buffers (x, x_scale, send_buf, recv_buf, expert_x, expert_scale, expert_y,
+ *    cs_buf, cr_buf, out) must be 16-byte aligned; metadata 8-byte; everything else 4-byte.
+ *  - Index types are int32.  Rows are addressed as [rank][row] with the row strides given by
+ *    moe_sizes().
+ *  - Device-detected errors (an expert id outside [0, E), or the same expert twice in one
+ *    token's R slots) set *shape->status to MOE_EBADIDX if it is still 0 (sticky) and drop the
+ *    offending slot: it is not counted, not sent, gets send_pos = -1 and adds nothing to the
+ *    combine.  The caller reads the status word after its own synchronisation.
+ *  - Calls are reentrant; the library keeps no state.  Two calls that overlap in time must not
+ *    share output buffers or a workspace.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_EINVAL = -1,        /* bad shape, null or misaligned pointer */
+    MOE_EUNSUPPORTED = -2,  /* valid but outside what these kernels implement */
+    MOE_EHIP = -3,          /* a HIP launch failed */
+    MOE_EBADIDX = -5        /* (device status word) bad expert id in topk_idx */
+} moe_status;
+
+typedef enum {
+    MOE_BF16 = 0,       /* dispatch payload: H bf16 values per row */
+    MOE_FP8_E4M3 = 1    /* OCP e4m3 codes, H per row, plus one fp32 scale per 128 of them */
+} moe_dtype;
+
+typedef struct {
+    int32_t N;          /* ranks (expert-parallel size), 1..1024 */
+    int32_t T;          /* tokens dispatched per rank */
+    int32_t H;          /* hidden size; multiple of 8 (bf16) or 512 (fp8) */
+    int32_t E;          /* experts, multiple of N, at most 1024 */
+    int32_t R;          /* experts per token, 1..min(E, 64) */
+    int32_t dtype;      /* moe_dtype of the dispatch payload; combine is always bf16 */
+    int64_t capacity;   /* receive-side rows per rank; 0 = N*T*max(R, E/N), the [EFA] bound.
+                           Must be at least N*T*min(R, E/N), the most any rank can receive. */
+    int32_t* status;    /* device int32 sticky error word, or NULL */
+} moe_shape;
+
+/* Byte sizes of every buffer for a shape.  rows: capacity = B (receive-side rows per rank),
+ * row_bytes = P (one dispatched row: the payload, then for fp8 its H/128 fp32 scales). */
+typedef struct {
+    int64_t capacity, row_bytes;
+    int64_t logits, bias, topk_idx, topk_w;
+    int64_t x, x_scale;
+    int64_t counts, send_off, send_pos, send_buf, send_meta;
+    int64_t recv_buf, recv_meta, recv_off;
+    int64_t expert_x, expert_scale, expert_cnt, expert_off, expert_src, expert_rpos;
+    int64_t expert_y, cs_buf, cr_buf, out;
+    int64_t workspace;
+} moe_sizes_t;
+
+/* Host only; no GPU needed.  Fills *out for a valid shape, else returns MOE_EINVAL or
+ * MOE_EUNSUPPORTED. */
+int moe_sizes(const moe_shape* shape, moe_sizes_t* out);
+
+/* Router.  [DSK] Expert Parallelism and MoE Router: each token takes R experts from a sort of
+ * the router scores that tracks indices, and the expert outputs are summed with weights;
+ * [PORT] introduction: the weights come from the router's probability distribution.
+ *   logits   f32[N*T][E]        router scores
+ *   bias     f32[E] or NULL     added to every token's scores before selection (one fp32 add)
+ *   topk_idx i32[N*T][R] (out)  experts by descending (score + bias), ties to the lower id
+ *   topk_w   f32[N*T][R] (out)  softmax over the R selected values, computed in fp64 and
+ *                                rounded to fp32 */
+int moe_route(const moe_shape* shape, const float* logits, const float* bias,
+              int32_t* topk_idx, float* topk_w, void* stream);
+
+/* Dispatch, send half.  [EFA] dispatch timing paragraph: count tokens per expert, take the
+ * cumulative sum of the counts as offsets into a send buffer contiguous per destination rank,
+ * pack the tokens; [PORT] Dispatch: activations, block scales and index travel together.
+ *   x         bf16[N][T][H] or e4m3 u8[N][T][H]   tokens
+ *   x_scale   f32[N][T][H/128] (fp8) or NULL       block scales
+ *   topk_idx  i32[N][T*R]                          experts per (token, slot)
+ *   counts    i32[N][E] (out)       counts[s][e] = slots of rank s that chose expert e
+ *   send_off  i32[N][N+1] (out)     exclusive scan over destinations of rows s sends to d
+ *   send_pos  i32[N][T*R] (out)     row of slot (t, k) in s's send buffer, -1 if dropped
+ *   send_buf  u8[N][T*R][P] (out)   rows grouped by destination rank, (token, slot) order
+ *                                    inside each group; row = payload bytes, then scales
+ *   send_meta i32[N][T*R][2] (out)  per send row: {e*T*R + t*R + k, number of earlier slots of
+ *                                    rank s that chose the same expert e}
+ *   workspace device scratch of moe_sizes().workspace bytes (may be NULL if that is 0) */
+int moe_dispatch_send(const moe_shape* shape, const void* x, const float* x_scale,
+                      const int32_t* topk_idx, int32_t* counts, int32_t* send_off,
+                      int32_t* send_pos, void* send_buf, int32_t* send_meta, void* workspace,
+                      void* stream);
+
+/* The network stand-in.  [EFA] send-buffer paragraph: after the per-expert counts are
+ * exchanged every rank knows where its writes go and where each source's tokens land, and the
+ * bulk moves with one write per peer.
+ *   send_off  i32[N][N+1]          from moe_dispatch_send (every source's: the exchanged table)
+ *   send_buf, send_meta            from moe_dispatch_send
+ *   recv_buf  u8[N][B][P] (out)    rank d receives segment (s -> d) at row recv_off[d][s]
+ *   recv_meta i32[N][B][2] (out)   the rows' metadata, moved with them
+ *   recv_off  i32[N][N+1] (out)    exclusive scan over sources of rows d receives; the total
+ *                                   recv_off[d][N] <= N*T*min(R, E/N) <= B */
+int moe_net_dispatch(const moe_shape* shape, const int32_t* send_off, const void* send_buf,
+                     const int32_t* send_meta, void* recv_buf, int32_t* recv_meta,
+                     int32_t* recv_off, void* stream);
+
+/* Dispatch, receive half.  [PORT] Dispatch: the receiver copies tokens into contiguous buffers
+ * that feed the grouped GEMM, tokens of one expert together, and keeps source rank, expert and
+ * token index for combine; [DSK] Cuda Graph: tokens per expert stay on the device.
+ *   counts, recv_off, recv_buf, recv_meta   from the calls above
+ *   expert_x     bf16[N][B][H] or u8[N][B][H] (out)  rows in (local expert, source, token,
+ *                                                     slot) order
+ *   expert_scale f32[N][B][H/128] (out, fp8) or NULL
+ *   expert_cnt   i32[N][L] (out)    rows per local expert
+ *   expert_off   i32[N][L+1] (out)  exclusive scan of expert_cnt
+ *   expert_src   i32[N][B] (out)    s*T*R + t*R + k of each expert-major row
+ *   expert_rpos  i32[N][B] (out)    the row's index in recv_buf (its receive position)
+ *   workspace    as for moe_dispatch_send */
+int moe_dispatch_recv(const moe_shape* shape, const int32_t* counts, const int32_t* recv_off,
+                      const void* recv_buf, const int32_t* recv_meta, void* expert_x,
+                      float* expert_scale, int32_t* expert_cnt, int32_t* expert_off,
+                      int32_t* expert_src, int32_t* expert_rpos, void* workspace, void* stream);
+
+/* Combine.  [EFA] combine paragraphs: with the metadata known from dispatch, shuffle the expert
+ * outputs, copy them back with one write per peer, and accumulate the weighted average from the
+ * receive buffer into the output; [PORT] Combine: 16-bit activations, the weighted average is
+ * computed by the receiver into an externally allocated tensor.
+ *   expert_y   bf16[N][B][H]        expert outputs in expert-major order
+ *   expert_rpos, recv_off           from dispatch (receive side)
+ *   send_off, send_pos, topk_w      from dispatch (send side) and the router
+ *   cs_buf     bf16[N][B][H] (out)  combine send buffer: cs[d][expert_rpos[q]] = y[d][q]
+ *   cr_buf     bf16[N][T*R][H] (out) combine receive buffer, laid out like send_buf
+ *   out        bf16[N][T][H] (out)  bf16(sum over k = 0..R-1 of w[t][k] * cr[send_pos[t][k]]),
+ *                                    accumulated in fp32 with fused multiply-adds in slot order */
+int moe_combine(const moe_shape* shape, const uint16_t* expert_y, const int32_t* expert_rpos,
+                const int32_t* recv_off, const int32_t* send_off, const int32_t* send_pos,
+                const float* topk_w, uint16_t* cs_buf, uint16_t* cr_buf, uint16_t* out,
+                void* stream);
+
+/* Stand-in for the grouped GEMM between dispatch and combine (not part of dispatch/combine;
+ * [EFA] overview: the grouped GEMM multiplies tokens by expert weights in between).
+ *   mode 0 (identity): y = the dispatched value (bf16 as is; e4m3 decoded times its block
+ *          scale, rounded once to bf16)
+ *   mode 1 (tagged):   y = bf16(that value * (64 + e % 64) / 64) for the row's expert e
+ *   expert_x, expert_scale, expert_off  from moe_dispatch_recv;  expert_y bf16[N][B][H] (out) */
+int moe_expert_stub(const moe_shape* shape, int32_t mode, const void* expert_x,
+                    const float* expert_scale, const int32_t* expert_off, uint16_t* expert_y,
+                    void* stream);
+
+/* Static string for a status code. */
+const char* moe_strerror(int status);
+
+/* MOE_ABI_VERSION of the loaded library. */
+int moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -59,7 +59,34 @@ def lib():
 class Shape(ctypes.Structure):
     _fields_ = [("N", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int),
                 ("E", ctypes.c_int), ("R", ctypes.c_int), ("fp8", ctypes.c_int),
-                ("B", ctypes.c_long)]
+                ("B", ctypes.c_long), ("rbase", ctypes.c_void_p)]
+
+    # With rbase set (an int64 array of N+1 row bases kept alive here), receive-side arrays are
+    # packed: rank d owns rows rbase[d] .. rbase[d+1]-1 of one [rows][...] array.
+    _rbase_arr = None
+
+    def rows(self) -> int:
+        return int(self._rbase_arr[-1]) if self._rbase_arr is not None else self.N * self.B
+
+    def lead(self):
+        """Leading dimensions of a receive-side array."""
+        return (self.rows(),) if self._rbase_arr is not None else (self.N, self.B)
+
+    def rank_rows(self, arr, d, n=None):
+        """The first n receive-side rows of rank d (all of its rows if n is None)."""
+        if self._rbase_arr is None:
+            return arr[d] if n is None else arr[d, :n]
+        b0, b1 = int(self._rbase_arr[d]), int(self._rbase_arr[d + 1])
+        return arr[b0:b1] if n is None else arr[b0:b0 + n]
+
+
+def packed_shape(N, T, H, E, R, fp8, rows_per_rank) -> Shape:
+    """A shape whose receive-side arrays hold exactly rows_per_rank[d] rows for rank d."""
+    rb = np.zeros(N + 1, np.int64)
+    rb[1:] = np.cumsum(np.asarray(rows_per_rank, np.int64))
+    sh = Shape(N, T, H, E, R, int(bool(fp8)), int(max(1, np.max(rows_per_rank))), rb.ctypes.data)
+    sh._rbase_arr = rb
+    return sh
 
 
 def _p(a):
@@ -72,7 +99,7 @@ def _p(a):
 def shape(N, T, H, E, R, fp8=False, B=None) -> Shape:
     if B is None:
         B = N * T * max(R, E // N)
-    return Shape(N, T, H, E, R, int(bool(fp8)), B)
+    return Shape(N, T, H, E, R, int(bool(fp8)), B, None)
 
 
 def row_bytes(sh: Shape) -> int:
@@ -122,10 +149,10 @@ def dispatch_send(sh: Shape, x: np.ndarray, x_scale, topk_idx: np.ndarray):
 
 
 def net_dispatch(sh: Shape, send_off, send_buf, send_meta):
-    N, B = sh.N, sh.B
+    N = sh.N
     P = row_bytes(sh)
-    recv_buf = np.zeros((N, B, P), np.uint8)
-    recv_meta = np.zeros((N, B, 2), np.int32)
+    recv_buf = np.zeros(sh.lead() + (P,), np.uint8)
+    recv_meta = np.zeros(sh.lead() + (2,), np.int32)
     recv_off = np.empty((N, N + 1), np.int32)
     lib().oracle_net_dispatch(ctypes.byref(sh), _p(send_off), _p(send_buf), _p(send_meta),
                               _p(recv_buf), _p(recv_meta), _p(recv_off))
@@ -133,18 +160,19 @@ def net_dispatch(sh: Shape, send_off, send_buf, send_meta):
 
 
 def dispatch_recv(sh: Shape, counts, recv_off, recv_buf, recv_meta):
-    N, B, H = sh.N, sh.B, sh.H
+    N, H = sh.N, sh.H
     L = sh.E // N
+    lead = sh.lead()
     if sh.fp8:
-        expert_x = np.zeros((N, B, H), np.uint8)
-        expert_scale = np.zeros((N, B, H // 128), np.float32)
+        expert_x = np.zeros(lead + (H,), np.uint8)
+        expert_scale = np.zeros(lead + (H // 128,), np.float32)
     else:
-        expert_x = np.zeros((N, B, H), np.uint16)
+        expert_x = np.zeros(lead + (H,), np.uint16)
         expert_scale = None
     expert_cnt = np.empty((N, L), np.int32)
     expert_off = np.empty((N, L + 1), np.int32)
-    expert_src = np.full((N, B), -1, np.int32)
-    expert_rpos = np.full((N, B), -1, np.int32)
+    expert_src = np.full(lead, -1, np.int32)
+    expert_rpos = np.full(lead, -1, np.int32)
     lib().oracle_dispatch_recv(ctypes.byref(sh), _p(counts), _p(recv_off), _p(recv_buf),
                                _p(recv_meta), _p(expert_x), _p(expert_scale), _p(expert_cnt),
                                _p(expert_off), _p(expert_src), _p(expert_rpos))
@@ -153,16 +181,15 @@ def dispatch_recv(sh: Shape, counts, recv_off, recv_buf, recv_meta):
 
 
 def expert(sh: Shape, mode: int, expert_x, expert_scale, expert_off):
-    N, B, H = sh.N, sh.B, sh.H
-    y = np.zeros((N, B, H), np.uint16)
+    y = np.zeros(sh.lead() + (sh.H,), np.uint16)
     lib().oracle_expert(ctypes.byref(sh), ctypes.c_int(mode), _p(np.ascontiguousarray(expert_x)),
                         _p(expert_scale), _p(expert_off), _p(y))
     return y
 
 
 def combine(sh: Shape, mode: int, expert_y, expert_rpos, recv_off, send_off, send_pos, topk_w):
-    N, B, H, T, R = sh.N, sh.B, sh.H, sh.T, sh.R
-    cs = np.zeros((N, B, H), np.uint16)
+    N, H, T, R = sh.N, sh.H, sh.T, sh.R
+    cs = np.zeros(sh.lead() + (H,), np.uint16)
     cr = np.zeros((N, T * R, H), np.uint16)
     out = np.empty((N, T, H), np.uint16)
     w = np.ascontiguousarray(topk_w, dtype=np.float32)
@@ -176,16 +203,16 @@ def run_all(sh: Shape, inp: dict, expert_mode: int = 0, combine_mode: int = 0,
             tight: bool = False) -> dict:
     """The whole path on one input set (see moe_synth.make_inputs).
 
-    With ``tight`` the receive-side arrays get exactly max_d(rows received by d) rows per rank
-    instead of ``sh.B`` (keeps host memory small for the large workloads); ``res["shape"]``
-    is the shape actually used."""
+    With ``tight`` the receive-side arrays are packed: rank d gets exactly the rows it receives
+    (keeps host memory small for the large, skewed workloads); ``res["shape"]`` is the shape
+    actually used (see Shape.rank_rows)."""
     res = {}
     idx, w = route(inp["logits"], inp["bias"], sh.R)
     res["topk_idx"], res["topk_w"] = idx, w
     res.update(dispatch_send(sh, inp["x"], inp.get("x_scale"), idx.reshape(sh.N, sh.T * sh.R)))
     if tight:
         n = np.diff(res["send_off"], axis=1)          # n[s][d]
-        sh = Shape(sh.N, sh.T, sh.H, sh.E, sh.R, sh.fp8, max(1, int(n.sum(axis=0).max())))
+        sh = packed_shape(sh.N, sh.T, sh.H, sh.E, sh.R, sh.fp8, n.sum(axis=0))
     res["shape"] = sh
     res.update(net_dispatch(sh, res["send_off"], res["send_buf"], res["send_meta"]))
     res.update(dispatch_recv(sh, res["counts"], res["recv_off"], res["recv_buf"],

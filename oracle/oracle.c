@@ -29,6 +29,12 @@
 #include <stdlib.h>
 #include <string.h>
 
+/* First receive-side row of rank d, and how many rows rank d has room for. */
+static long rrow0(const oracle_shape* sh, int d) { return sh->rbase ? sh->rbase[d] : (long)d * sh->B; }
+static long rcap(const oracle_shape* sh, int d) {
+    return sh->rbase ? sh->rbase[d + 1] - sh->rbase[d] : sh->B;
+}
+
 long oracle_row_bytes(const oracle_shape* sh) {
     if (!sh->fp8) return 2L * sh->H;
     return (long)sh->H + 4L * (sh->H / 128);
@@ -200,14 +206,14 @@ void oracle_net_dispatch(const oracle_shape* sh, const int32_t* send_off, const 
             const int32_t* soff = send_off + (long)s * (N + 1);
             roff[s + 1] = roff[s] + (soff[d + 1] - soff[d]);
         }
-        assert(roff[N] <= sh->B);
+        assert(roff[N] <= rcap(sh, d));
     }
     for (int s = 0; s < N; ++s) {
         const int32_t* soff = send_off + (long)s * (N + 1);
         for (int d = 0; d < N; ++d) {
             long n = soff[d + 1] - soff[d];
             long src = (long)s * TR + soff[d];
-            long dst = (long)d * sh->B + recv_off[(long)d * (N + 1) + s];
+            long dst = rrow0(sh, d) + recv_off[(long)d * (N + 1) + s];
             memcpy(recv_buf + dst * P, send_buf + src * P, n * P);
             memcpy(recv_meta + 2 * dst, send_meta + 2 * src, 8 * n);
         }
@@ -245,19 +251,19 @@ void oracle_dispatch_recv(const oracle_shape* sh, const int32_t* counts, const i
         int s = 0;
         for (long r = 0; r < roff[N]; ++r) {
             while (r >= roff[s + 1]) ++s; /* source rank of receive row r */
-            const int32_t* meta = recv_meta + 2 * ((long)d * sh->B + r);
+            const int32_t* meta = recv_meta + 2 * (rrow0(sh, d) + r);
             int e = (int)(meta[0] / TR);
             long i = meta[0] % TR;
             assert(e / L == d);
             int j = e - d * L;
             long q = eoff[j] + fill[j];
             fill[j] += 1;
-            const uint8_t* row = recv_buf + ((long)d * sh->B + r) * P;
-            memcpy(expert_x + ((long)d * sh->B + q) * xrow, row, xrow);
+            const uint8_t* row = recv_buf + (rrow0(sh, d) + r) * P;
+            memcpy(expert_x + (rrow0(sh, d) + q) * xrow, row, xrow);
             if (sh->fp8)
-                memcpy(expert_scale + ((long)d * sh->B + q) * nsc, row + xrow, 4L * nsc);
-            expert_src[(long)d * sh->B + q] = (int32_t)((long)s * TR + i);
-            expert_rpos[(long)d * sh->B + q] = (int32_t)r;
+                memcpy(expert_scale + (rrow0(sh, d) + q) * nsc, row + xrow, 4L * nsc);
+            expert_src[rrow0(sh, d) + q] = (int32_t)((long)s * TR + i);
+            expert_rpos[rrow0(sh, d) + q] = (int32_t)r;
         }
     }
     free(fill);
@@ -277,7 +283,7 @@ void oracle_expert(const oracle_shape* sh, int mode, const uint8_t* expert_x,
             int e = d * L + j;
             double tag = (mode == 1) ? (double)(64 + e % 64) / 64.0 : 1.0;
             for (long q = eoff[j]; q < eoff[j + 1]; ++q) {
-                long row = (long)d * sh->B + q;
+                long row = rrow0(sh, d) + q;
                 for (int h = 0; h < H; ++h) {
                     double v;
                     if (sh->fp8) {
@@ -314,8 +320,8 @@ void oracle_combine(const oracle_shape* sh, int mode, const uint16_t* expert_y,
     for (int d = 0; d < N; ++d) {
         long total = recv_off[(long)d * (N + 1) + N];
         for (long q = 0; q < total; ++q) {
-            long r = expert_rpos[(long)d * sh->B + q];
-            memcpy(cs_buf + ((long)d * sh->B + r) * H, expert_y + ((long)d * sh->B + q) * H, 2L * H);
+            long r = expert_rpos[rrow0(sh, d) + q];
+            memcpy(cs_buf + (rrow0(sh, d) + r) * H, expert_y + (rrow0(sh, d) + q) * H, 2L * H);
         }
     }
     /* network back: segment (d -> s) lands where s's dispatch segment for d sat */
@@ -323,7 +329,7 @@ void oracle_combine(const oracle_shape* sh, int mode, const uint16_t* expert_y,
         const int32_t* soff = send_off + (long)s * (N + 1);
         for (int d = 0; d < N; ++d) {
             long n = soff[d + 1] - soff[d];
-            long src = (long)d * sh->B + recv_off[(long)d * (N + 1) + s];
+            long src = rrow0(sh, d) + recv_off[(long)d * (N + 1) + s];
             long dst = (long)s * TR + soff[d];
             memcpy(cr_buf + dst * H, cs_buf + src * H, 2L * n * H);
         }

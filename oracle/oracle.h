@@ -28,6 +28,8 @@ typedef struct {
     int N, T, H, E, R;
     int fp8;   /* 0: bf16 payload (2H bytes per row); 1: e4m3 payload + fp32 scale per 128 */
     long B;    /* receive-side rows per rank (row stride of every [N][B][...] array) */
+    const long* rbase; /* optional: rank d's receive-side rows start at row rbase[d] and it has
+                          rbase[d+1] - rbase[d] of them (N+1 entries); NULL means d * B and B */
 } oracle_shape;
 
 /* Bytes of one dispatched row: the payload, then (fp8 only) its block scales. */

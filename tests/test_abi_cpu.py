@@ -1,0 +1,123 @@
+"""The C ABI without a GPU: the library loads, exports every function include/moe.h declares,
+sizes buffers, and rejects invalid calls during host validation (before any launch)."""
+import ctypes
+import os
+import subprocess
+import sys
+
+import pytest
+
+import combine_moe_route_top_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_exports_every_declared_symbol():
+    names = moe.header_functions()
+    assert {"moe_route", "moe_dispatch_send", "moe_net_dispatch", "moe_dispatch_recv",
+            "moe_combine", "moe_sizes", "moe_strerror"} <= set(names)
+    for n in names:
+        assert hasattr(moe._lib, n), n
+    # and they are exported C symbols of libmoe.so (nm -D), not C++-mangled
+    out = subprocess.run(["nm", "-D", "--defined-only", moe.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for n in names:
+        assert n in syms, n
+
+
+def test_abi_version_and_strerror():
+    assert moe.moe_abi_version() == 1
+    for code in (0, -1, -2, -3, -5, 42):
+        assert isinstance(moe.moe_strerror(code), str)
+
+
+def test_sizes_of_the_workloads():
+    sz = moe.moe_sizes(moe.make_shape(32, 128, 7168, 256, 8))
+    assert sz["capacity"] == 32 * 128 * 8 and sz["row_bytes"] == 2 * 7168
+    assert sz["send_buf"] == 32 * 128 * 8 * 14336
+    assert sz["recv_buf"] == 32 * sz["capacity"] * 14336
+    sz = moe.moe_sizes(moe.make_shape(64, 128, 7168, 384, 8, fp8=True))
+    assert sz["row_bytes"] == 7168 + 4 * 56 == 7392
+    assert sz["capacity"] == 64 * 128 * 8
+    assert sz["x_scale"] == 64 * 128 * 56 * 4
+    sz = moe.moe_sizes(moe.make_shape(4, 4096, 4096, 128, 8))
+    assert sz["capacity"] == 4 * 4096 * 32          # N*T*max(R, E/N) with E/N = 32 > R
+    assert sz["workspace"] >= 4 * 32 * 128 * 4       # 32 count chunks of 1024 slots per rank
+    sz = moe.moe_sizes(moe.make_shape(8, 128, 4096, 8, 2, capacity=8 * 128 * 1))
+    assert sz["capacity"] == 1024                    # the tight bound N*T*min(R, E/N)
+
+
+@pytest.mark.parametrize("args,code", [
+    ((3, 16, 256, 8, 2), moe.MOE_EINVAL),            # E not a multiple of N
+    ((2, 16, 256, 8, 9), moe.MOE_EINVAL),            # R > E
+    ((2, 16, 256, 8, 0), moe.MOE_EINVAL),            # R < 1
+    ((0, 16, 256, 8, 2), moe.MOE_EINVAL),            # N < 1
+    ((2, 0, 256, 8, 2), moe.MOE_EINVAL),             # T < 1
+    ((2, 16, 250, 8, 2), moe.MOE_EUNSUPPORTED),      # bf16 rows must be 16-byte multiples
+    ((2, 16, 2048, 2048, 2), moe.MOE_EUNSUPPORTED),  # E > 1024
+    ((2, 16, 256, 128, 65), moe.MOE_EUNSUPPORTED),   # R > 64
+])
+def test_bad_shapes(args, code):
+    with pytest.raises(moe.MoeError) as ex:
+        moe.moe_sizes(moe.make_shape(*args))
+    assert ex.value.code == code
+
+
+def test_bad_fp8_hidden_and_capacity():
+    with pytest.raises(moe.MoeError) as ex:
+        moe.moe_sizes(moe.make_shape(2, 16, 256, 8, 2, fp8=True))   # fp8 needs H % 512 == 0
+    assert ex.value.code == moe.MOE_EUNSUPPORTED
+    with pytest.raises(moe.MoeError) as ex:                          # below the tight bound
+        moe.moe_sizes(moe.make_shape(2, 16, 256, 8, 2, capacity=2 * 16 * 2 - 1))
+    assert ex.value.code == moe.MOE_EINVAL
+
+
+def test_null_and_misaligned_pointers_rejected_before_launch():
+    sh = moe.make_shape(2, 16, 256, 8, 2)
+    good = 1 << 20  # a 16-byte aligned non-null address; never dereferenced on this path
+    bad = good + 4
+    cases = [
+        lambda: moe.moe_route(sh, None, None, good, good, stream=0),
+        lambda: moe.moe_dispatch_send(sh, bad, None, good, good, good, good, good, good, good, stream=0),
+        lambda: moe.moe_dispatch_send(sh, good, None, good, good, good, good, good, good + 4, good, stream=0),
+        lambda: moe.moe_net_dispatch(sh, good, good, good, bad, good, good, stream=0),
+        lambda: moe.moe_dispatch_recv(sh, good, good, good, good, bad, None, good, good, good, good,
+                                      good, stream=0),
+        lambda: moe.moe_dispatch_recv(sh, good, good, good, good, good, None, good, good, good, good,
+                                      None, stream=0),
+        lambda: moe.moe_combine(sh, good, good, good, good, good, good, good, good, bad, stream=0),
+        lambda: moe.moe_expert_stub(sh, 2, good, None, good, good, stream=0),
+    ]
+    for fn in cases:
+        with pytest.raises(moe.MoeError) as ex:
+            fn()
+        assert ex.value.code == moe.MOE_EINVAL
+    fsh = moe.make_shape(2, 16, 512, 8, 2, fp8=True)
+    with pytest.raises(moe.MoeError) as ex:   # fp8 needs the scale pointer
+        moe.moe_dispatch_send(fsh, good, None, good, good, good, good, good, good, good, stream=0)
+    assert ex.value.code == moe.MOE_EINVAL
+    with pytest.raises(moe.MoeError) as ex:
+        moe.moe_route(None if False else moe.make_shape(3, 1, 8, 8, 1), good, None, good, good, stream=0)
+    assert ex.value.code == moe.MOE_EINVAL
+
+
+def test_null_shape_rejected():
+    rc = moe._lib.moe_route(None, None, None, None, None, None)
+    assert rc == moe.MOE_EINVAL
+    out = moe.moe_sizes_t()
+    assert moe._lib.moe_sizes(None, ctypes.byref(out)) == moe.MOE_EINVAL
+
+
+def test_product_does_not_import_oracle():
+    # the product package never imports the oracle; importing it must not load liboracle
+    code = ("import sys, combine_moe_route_top_amd\n"
+            "assert 'oracle' not in sys.modules\n"
+            "maps = open('/proc/self/maps').read()\n"
+            "assert 'liboracle' not in maps\n")
+    subprocess.run([sys.executable, "-c", code], cwd=ROOT, check=True)
+    for dirpath, _, files in os.walk(os.path.join(ROOT, "combine_moe_route_top_amd")):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cuh", ".h", ".cpp")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in src.replace("oracle/", ""), f

@@ -27,15 +27,15 @@ MUTANTS = {
     "send_meta_rank_off_by_one": ("meta[1] = seen[e];", "meta[1] = seen[e] + 1;"),
     "net_offsets_transposed": ("roff[s + 1] = roff[s] + (soff[d + 1] - soff[d]);",
                                "roff[s + 1] = roff[s] + (soff[s + 1] - soff[s]);"),
-    "recv_src_uses_dest_rank": ("expert_src[(long)d * sh->B + q] = (int32_t)((long)s * TR + i);",
-                                "expert_src[(long)d * sh->B + q] = (int32_t)((long)d * TR + i);"),
+    "recv_src_uses_dest_rank": ("expert_src[rrow0(sh, d) + q] = (int32_t)((long)s * TR + i);",
+                                "expert_src[rrow0(sh, d) + q] = (int32_t)((long)d * TR + i);"),
     "recv_expert_off_not_scanned": ("eoff[j + 1] = eoff[j] + c;", "eoff[j + 1] = c;"),
     "expert_tag_local_id": ("(double)(64 + e % 64) / 64.0", "(double)(64 + j % 64) / 64.0"),
     "combine_shuffle_inverted": (
-        "memcpy(cs_buf + ((long)d * sh->B + r) * H, expert_y + ((long)d * sh->B + q) * H, 2L * H);",
-        "memcpy(cs_buf + ((long)d * sh->B + q) * H, expert_y + ((long)d * sh->B + r) * H, 2L * H);"),
-    "combine_net_offsets_transposed": ("long src = (long)d * sh->B + recv_off[(long)d * (N + 1) + s];",
-                                       "long src = (long)d * sh->B + recv_off[(long)s * (N + 1) + d];"),
+        "memcpy(cs_buf + (rrow0(sh, d) + r) * H, expert_y + (rrow0(sh, d) + q) * H, 2L * H);",
+        "memcpy(cs_buf + (rrow0(sh, d) + q) * H, expert_y + (rrow0(sh, d) + r) * H, 2L * H);"),
+    "combine_net_offsets_transposed": ("long src = rrow0(sh, d) + recv_off[(long)d * (N + 1) + s];",
+                                       "long src = rrow0(sh, d) + recv_off[(long)s * (N + 1) + d];"),
     "combine_weight_of_slot0": ("acc += (double)topk_w[base + k] * y;", "acc += (double)topk_w[base] * y;"),
     "combine_drops_last_slot": ("for (int k = 0; k < R; ++k) {\n                    long row",
                                 "for (int k = 0; k < R - 1; ++k) {\n                    long row"),
