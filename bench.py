@@ -153,6 +153,27 @@ def closed_form_check(b, c) -> str:
     return f"ok (max {ulp} bf16 ulp vs identity closed form; counts sum to T*R)"
 
 
+def traffic_record(kernel, workload):
+    """Scaled FETCH_SIZE + WRITE_SIZE bytes per launch from the committed counter summary, or
+    None if there is none or the kernel's source changed since the counters were taken."""
+    import glob
+    import hashlib
+    import re
+    for path in glob.glob(os.path.join(ROOT, "profiles", "counters_*.md")):
+        for line in open(path):
+            m = re.match(r"traffic-record: kernel=(\S+) workload=(\S+) bytes_per_launch=(\d+) "
+                         r"source=(\S+) sha256=([0-9a-f]+)", line.strip())
+            if not m or m.group(1) != kernel or m.group(2) != workload:
+                continue
+            src = os.path.join(ROOT, m.group(4))
+            if not os.path.exists(src):
+                return None
+            if hashlib.sha256(open(src, "rb").read()).hexdigest() != m.group(5):
+                return None
+            return int(m.group(3))
+    return None
+
+
 def dominant_kernel(res) -> dict:
     """Roofline of the dominant single-kernel call: the network stand-in (k_net_dispatch plus
     the tiny recv_off scan k_net_prep, both inside moe_net_dispatch)."""
@@ -161,7 +182,8 @@ def dominant_kernel(res) -> dict:
     achieved = ab["net_dispatch"] / (us * 1e-6) / 1e9
     return {"kernel": "k_net_dispatch (+k_net_prep) via moe_net_dispatch", "bound": "hbm",
             "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": traffic_record("k_net_dispatch", res["workload"]),
             "bytes_per_launch": ab["net_dispatch"], "us_per_launch": round(us, 2)}
 
 
@@ -201,6 +223,28 @@ def cpu_baseline(name, budget_s=25.0) -> dict:
                       f"median of {len(times)}"}
 
 
+def copy_calibration(nbytes=1 << 30, reps=10) -> dict:
+    """A plain device-to-device copy of known size (torch copy_), timed with HIP events: the
+    practical ceiling of a read+write stream on this GPU, and the reference kernel for scaling
+    the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bytes_read": nbytes, "bytes_written": nbytes, "us": round(us, 2),
+            "gbs": round(2 * nbytes / (us * 1e-6) / 1e9, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -211,6 +255,7 @@ def main():
                     help="comma-separated workloads reported beside the headline ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--no-copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the N expert-parallel ranks are simulated inside one "
@@ -222,6 +267,7 @@ def main():
         sys.exit(2)
     torch.cuda.set_device(0)
 
+    calib = None if args.no_copy_calibration else copy_calibration()
     head = run_workload(args.workload, args.steps, args.warmup, check=not args.no_check)
     extras = {}
     for name in [e for e in args.extra.split(",") if e and e != args.workload]:
@@ -257,6 +303,9 @@ def main():
         "roofline": dominant_kernel(head),
         "other_workloads": extras,
     }
+    if calib is not None:
+        line["plain_copy"] = calib
+        line["frac_of_plain_copy"] = round(head["gbs"] / calib["gbs"], 4)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.workload)
     print(json.dumps(line), flush=True)
