@@ -11,19 +11,6 @@
 
 namespace moe {
 
-__device__ __forceinline__ void rank_bases_c(const int32_t* table, int stride, int col, int N, int* gb) {
-    if (wave_id() != 0) return;
-    int carry = 0;
-    for (int b = 0; b < N; b += kWave) {
-        const int dd = b + lane_id();
-        const int v = dd < N ? table[(long)dd * stride + col] : 0;
-        const int inc = wave_incl_scan(v);
-        if (dd < N) gb[dd] = carry + inc - v;
-        carry += readlane(inc, kWave - 1);
-    }
-    if (lane_id() == 0) gb[N] = carry;
-}
-
 // ------------------------------------------------------------------ stand-in expert
 
 // e4m3 (OCP: bias 7, 3 mantissa bits, S.1111.111 = NaN) to double, exactly.
@@ -57,7 +44,7 @@ __global__ __launch_bounds__(kBlock) void k_expert_stub(Dims D, int mode, const 
                                                         uint16_t* __restrict__ expert_y) {
     extern __shared__ int gb[];
     const int N = D.N, L = D.L;
-    rank_bases_c(expert_off, L + 1, L, N, gb);
+    rank_bases(expert_off, L + 1, L, N, gb);
     __syncthreads();
     const long G = (long)blockIdx.x * kWavesPerBlock + wave_id();
     if (G >= gb[N]) return;
@@ -99,61 +86,80 @@ __global__ __launch_bounds__(kBlock) void k_expert_stub(Dims D, int mode, const 
 
 // ------------------------------------------------------------------ combine
 
-// Shuffle: cs[d][expert_rpos[q]] = y[d][q].  One wave per expert-major row, flattened.
-template <int U>
+// Shuffle: cs[d][expert_rpos[q]] = y[d][q].  kRowsPerBlock expert-major rows per block (a global
+// index over all ranks), one resolved per wave, then streamed.
 __global__ __launch_bounds__(kBlock) void k_combine_pack(Dims D, const uint16_t* __restrict__ expert_y,
                                                          const int32_t* __restrict__ expert_rpos,
                                                          const int32_t* __restrict__ recv_off,
                                                          uint16_t* __restrict__ cs_buf) {
     extern __shared__ int gb[];
+    __shared__ RowDesc rows[kRowsPerBlock];
     const int N = D.N;
-    rank_bases_c(recv_off, N + 1, N, N, gb);
+    rank_bases(recv_off, N + 1, N, N, gb);
     __syncthreads();
-    const long G = (long)blockIdx.x * kWavesPerBlock + wave_id();
-    if (G >= gb[N]) return;
-    const int d = wave_count_le(gb + 1, N, G);
-    const long q = G - gb[d];
-    const long r = expert_rpos[(size_t)d * D.B + q];
-    if (r < 0 || r >= D.B) {
-        set_status(D.status, MOE_EINVAL);
-        return;
+    const long G = (long)blockIdx.x * kRowsPerBlock + wave_id();
+    RowDesc rd = {0, 0, 0, 0};
+    if (G < gb[N]) {
+        const int d = wave_count_le(gb + 1, N, G);
+        const long q = G - gb[d];
+        const long r = expert_rpos[(size_t)d * D.B + q];
+        if (r >= 0 && r < D.B) {
+            rd.src_a = rd.src_b = (uint64_t)(expert_y + ((size_t)d * D.B + q) * D.H);
+            rd.dst_a = rd.dst_b = (uint64_t)(cs_buf + ((size_t)d * D.B + r) * D.H);
+        } else {
+            set_status(D.status, MOE_EINVAL);
+        }
     }
-    wave_copy_row<U>(reinterpret_cast<const u32x4*>(expert_y + ((size_t)d * D.B + q) * D.H),
-                     reinterpret_cast<u32x4*>(cs_buf + ((size_t)d * D.B + r) * D.H), D.Y16);
+    if (lane_id() == 0) rows[wave_id()] = rd;
+    __syncthreads();
+    block_stream_rows(rows, kRowsPerBlock, D.Y16, D.Y16, D.Y16);
 }
 
-// Network back: row i of rank s's combine receive buffer comes from segment (d -> s) of rank
-// d's combine send buffer.  One wave per row of cr.
-template <int U>
+// Network back: rank d's combine send buffer is read in order (a global index over all ranks);
+// row r of segment (s -> d) lands at send_off[s][d] + (r - recv_off[d][s]) in rank s's combine
+// receive buffer, where s's dispatch send buffer had it.
 __global__ __launch_bounds__(kBlock) void k_combine_net(Dims D, const uint16_t* __restrict__ cs_buf,
                                                         const int32_t* __restrict__ recv_off,
                                                         const int32_t* __restrict__ send_off,
                                                         uint16_t* __restrict__ cr_buf) {
-    const long g = (long)blockIdx.x * kWavesPerBlock + wave_id();
+    extern __shared__ int gb[];
+    __shared__ RowDesc rows[kRowsPerBlock];
     const int N = D.N;
-    if (g >= (long)N * D.TR) return;
-    const long s = g / D.TR;
-    const int i = (int)(g - s * D.TR);
-    const int32_t* so = send_off + s * (N + 1);
-    if (i >= so[N]) return;
-    const int d = wave_count_le(so, N, i) - 1;
-    const long r = recv_off[(long)d * (N + 1) + s] + (i - so[d]);
-    if (d < 0 || r < 0 || r >= D.B) {
-        set_status(D.status, MOE_EINVAL);
-        return;
+    rank_bases(recv_off, N + 1, N, N, gb);
+    __syncthreads();
+    const long G = (long)blockIdx.x * kRowsPerBlock + wave_id();
+    RowDesc rd = {0, 0, 0, 0};
+    if (G < gb[N]) {
+        const int d = wave_count_le(gb + 1, N, G);
+        const long r = G - gb[d];
+        const int32_t* ro = recv_off + (long)d * (N + 1);
+        const int s = wave_count_le(ro, N, r) - 1;
+        const long i = s >= 0 ? send_off[(long)s * (N + 1) + d] + (r - ro[s]) : -1;
+        if (i >= 0 && i < D.TR) {
+            rd.src_a = rd.src_b = (uint64_t)(cs_buf + ((size_t)d * D.B + r) * D.H);
+            rd.dst_a = rd.dst_b = (uint64_t)(cr_buf + ((size_t)s * D.TR + i) * D.H);
+        } else {
+            set_status(D.status, MOE_EINVAL);
+        }
     }
-    wave_copy_row<U>(reinterpret_cast<const u32x4*>(cs_buf + ((size_t)d * D.B + r) * D.H),
-                     reinterpret_cast<u32x4*>(cr_buf + ((size_t)s * D.TR + i) * D.H), D.Y16);
+    if (lane_id() == 0) rows[wave_id()] = rd;
+    __syncthreads();
+    block_stream_rows(rows, kRowsPerBlock, D.Y16, D.Y16, D.Y16);
 }
 
 // Weighted sum: out[s][t] = bf16(sum_k w[k] * cr[s][send_pos[k]]), fp32 fused multiply-adds in
-// slot order k = 0..R-1; dropped slots (send_pos < 0) add nothing.  One wave per token; each
-// lane owns 8 hidden values (one 16-byte chunk) per step, loads up to 8 slots ahead.
+// slot order k = 0..R-1; dropped slots (send_pos < 0) add nothing.  kWsumWaves waves per token,
+// each owning every kWsumWaves-th group of 64 chunks; a lane keeps 2 chunks (16 hidden values)
+// and up to 8 slots' loads in flight.
+constexpr int kWsumWaves = 4;
+
 __global__ __launch_bounds__(kBlock) void k_wsum(Dims D, const uint16_t* __restrict__ cr_buf,
                                                  const int32_t* __restrict__ send_pos,
                                                  const float* __restrict__ topk_w,
                                                  uint16_t* __restrict__ out) {
-    const long tok = (long)blockIdx.x * kWavesPerBlock + wave_id();
+    constexpr int CU = 2;
+    const long tok = ((long)blockIdx.x * kWavesPerBlock + wave_id()) / kWsumWaves;
+    const int part = wave_id() % kWsumWaves;
     if (tok >= (long)D.N * D.T) return;
     const int lane = lane_id();
     const int R = D.R;
@@ -163,12 +169,14 @@ __global__ __launch_bounds__(kBlock) void k_wsum(Dims D, const uint16_t* __restr
     const u32x4* rank_rows = reinterpret_cast<const u32x4*>(cr_buf + (size_t)s * D.TR * D.H);
     u32x4* orow = reinterpret_cast<u32x4*>(out + (size_t)tok * D.H);
     const int n16 = D.Y16;
-    for (int c = lane; c < n16; c += kWave) {
-        float acc[8];
+    for (int c0 = part * kWave + lane; c0 < n16; c0 += kWave * kWsumWaves * CU) {
+        float acc[CU][8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) acc[u] = 0.0f;
+        for (int cu = 0; cu < CU; ++cu)
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc[cu][u] = 0.0f;
         for (int k0 = 0; k0 < R; k0 += 8) {
-            u32x4 v[8];
+            u32x4 v[CU][8];
             float wk[8];
             bool ok[8];
 #pragma unroll
@@ -177,22 +185,35 @@ __global__ __launch_bounds__(kBlock) void k_wsum(Dims D, const uint16_t* __restr
                 const int pos = k < R ? readlane(my_pos, k) : -1;
                 ok[kk] = pos >= 0 && pos < D.TR;
                 wk[kk] = k < R ? readlane_f(my_w, k) : 0.0f;
-                if (ok[kk]) v[kk] = rank_rows[(size_t)pos * n16 + c];
+#pragma unroll
+                for (int cu = 0; cu < CU; ++cu) {
+                    const int c = c0 + cu * kWave * kWsumWaves;
+                    if (ok[kk] && c < n16) v[cu][kk] = ld_nt(rank_rows + (size_t)pos * n16 + c);
+                }
             }
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
                 if (!ok[kk]) continue;
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const float y = bf16_to_f32((v[kk][u >> 1] >> (16 * (u & 1))) & 0xFFFF);
-                    acc[u] = __builtin_fmaf(wk[kk], y, acc[u]);
-                }
+                for (int cu = 0; cu < CU; ++cu)
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const float y = bf16_to_f32((v[cu][kk][u >> 1] >> (16 * (u & 1))) & 0xFFFF);
+                        acc[cu][u] = __builtin_fmaf(wk[kk], y, acc[cu][u]);
+                    }
             }
         }
-        u32x4 o;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) o[u] = f32_to_bf16(acc[2 * u]) | (f32_to_bf16(acc[2 * u + 1]) << 16);
-        orow[c] = o;
+        for (int cu = 0; cu < CU; ++cu) {
+            const int c = c0 + cu * kWave * kWsumWaves;
+            if (c < n16) {
+                u32x4 o;
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    o[u] = f32_to_bf16(acc[cu][2 * u]) | (f32_to_bf16(acc[cu][2 * u + 1]) << 16);
+                st_nt(orow + c, o);
+            }
+        }
     }
 }
 
@@ -211,14 +232,14 @@ hipError_t launch_combine(const Dims& D, const uint16_t* expert_y, const int32_t
                           const int32_t* recv_off, const int32_t* send_off, const int32_t* send_pos,
                           const float* topk_w, uint16_t* cs_buf, uint16_t* cr_buf, uint16_t* out,
                           hipStream_t st) {
-    const long rows = (long)D.N * D.TR;
-    const dim3 grid_rows((rows + kWavesPerBlock - 1) / kWavesPerBlock);
-    hipLaunchKernelGGL(k_combine_pack<8>, grid_rows, dim3(kBlock), (D.N + 1) * 4, st, D, expert_y,
+    const long rows = (long)D.N * D.TR;  // every received row, over all ranks, is one of these
+    const dim3 grid_rows((rows + kRowsPerBlock - 1) / kRowsPerBlock);
+    hipLaunchKernelGGL(k_combine_pack, grid_rows, dim3(kBlock), (D.N + 1) * 4, st, D, expert_y,
                        expert_rpos, recv_off, cs_buf);
-    hipLaunchKernelGGL(k_combine_net<8>, grid_rows, dim3(kBlock), 0, st, D, (const uint16_t*)cs_buf,
-                       recv_off, send_off, cr_buf);
-    const long ntok = (long)D.N * D.T;
-    hipLaunchKernelGGL(k_wsum, dim3((ntok + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock), 0, st, D,
+    hipLaunchKernelGGL(k_combine_net, grid_rows, dim3(kBlock), (D.N + 1) * 4, st, D,
+                       (const uint16_t*)cs_buf, recv_off, send_off, cr_buf);
+    const long waves = (long)D.N * D.T * kWsumWaves;
+    hipLaunchKernelGGL(k_wsum, dim3((waves + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock), 0, st, D,
                        (const uint16_t*)cr_buf, send_pos, topk_w, out);
     return hipGetLastError();
 }

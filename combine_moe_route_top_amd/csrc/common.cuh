@@ -89,52 +89,74 @@ __device__ __forceinline__ int wave_count_le(const int* a, int n, long long x) {
     return c;
 }
 
-// ------------------------------------------------------------------ 16-byte row copies
+// ------------------------------------------------------------------ block row streaming
 
-// Copy n16 chunks of 16 bytes from a row made of two parts (src_a: the first split_src chunks,
-// src_b: the rest) to a row made of two parts (dst_a: first split_dst chunks, dst_b: the rest).
-// One wave; each lane moves chunks lane, lane+64, ...; U loads are issued before their stores.
-template <int U>
-__device__ __forceinline__ void wave_copy_row(const u32x4* __restrict__ src_a,
-                                              const u32x4* __restrict__ src_b, int split_src,
-                                              u32x4* __restrict__ dst_a, u32x4* __restrict__ dst_b,
-                                              int split_dst, int n16) {
-    const int l = lane_id();
-    for (int c0 = 0; c0 < n16; c0 += kWave * U) {
-        u32x4 v[U];
+// Nontemporal 16-byte accesses: streamed data does not stay in the caches, and the stores do not
+// leave dirty lines in the 256 MB memory-side cache for the next kernel to write back.
+__device__ __forceinline__ u32x4 ld_nt(const u32x4* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void st_nt(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
+
+// Rows handled by one 256-thread block of a row-copy kernel: one row per wave is resolved (its
+// source and destination found), then all 256 threads stream the rows' 16-byte chunks.
+constexpr int kRowsPerBlock = 4;
+constexpr int kStreamUnroll = 8;  // 16-byte loads in flight per thread
+
+// A resolved row: the source is src_a (its first split_src chunks) then src_b; the destination
+// dst_a (first split_dst chunks) then dst_b.  dst_a == 0 marks "no row".
+struct RowDesc {
+    uint64_t src_a, src_b, dst_a, dst_b;
+};
+
+// Stream nrows resolved rows of n16 chunks each, flat over (row, chunk) so that every thread has
+// kStreamUnroll loads in flight regardless of the row size.
+__device__ __forceinline__ void block_stream_rows(const RowDesc* rows, int nrows, int n16,
+                                                  int split_src, int split_dst) {
+    const int total = nrows * n16;
+    const float inv = 1.0f / (float)n16;
+    for (int k0 = threadIdx.x; k0 < total; k0 += blockDim.x * kStreamUnroll) {
+        u32x4 v[kStreamUnroll];
+        int rr[kStreamUnroll];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            int c = c0 + u * kWave + l;
-            if (c < n16) v[u] = c < split_src ? src_a[c] : src_b[c - split_src];
+        for (int u = 0; u < kStreamUnroll; ++u) {
+            const int k = k0 + u * blockDim.x;
+            int r = (int)((float)k * inv);  // k / n16, corrected below (k < 2^24)
+            if (r * n16 > k) --r;
+            else if ((r + 1) * n16 <= k) ++r;
+            rr[u] = r;
+            if (k < total && rows[r].dst_a) {
+                const int c = k - r * n16;
+                const u32x4* src = c < split_src ? (const u32x4*)rows[r].src_a + c
+                                                 : (const u32x4*)rows[r].src_b + (c - split_src);
+                v[u] = ld_nt(src);
+            }
         }
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            int c = c0 + u * kWave + l;
-            if (c < n16) {
-                if (c < split_dst) dst_a[c] = v[u];
-                else dst_b[c - split_dst] = v[u];
+        for (int u = 0; u < kStreamUnroll; ++u) {
+            const int k = k0 + u * blockDim.x;
+            const int r = rr[u];
+            if (k < total && rows[r].dst_a) {
+                const int c = k - r * n16;
+                u32x4* dst = c < split_dst ? (u32x4*)rows[r].dst_a + c
+                                           : (u32x4*)rows[r].dst_b + (c - split_dst);
+                st_nt(dst, v[u]);
             }
         }
     }
 }
 
-template <int U>
-__device__ __forceinline__ void wave_copy_row(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
-                                              int n16) {
-    const int l = lane_id();
-    for (int c0 = 0; c0 < n16; c0 += kWave * U) {
-        u32x4 v[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            int c = c0 + u * kWave + l;
-            if (c < n16) v[u] = src[c];
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            int c = c0 + u * kWave + l;
-            if (c < n16) dst[c] = v[u];
-        }
+// Global row bases over ranks, gb[d] = sum over d' < d of table[d' * stride + col], gb[N] = the
+// total; computed by wave 0 into LDS (the caller synchronises).
+__device__ __forceinline__ void rank_bases(const int32_t* table, int stride, int col, int N, int* gb) {
+    if (wave_id() != 0) return;
+    int carry = 0;
+    for (int b = 0; b < N; b += kWave) {
+        const int dd = b + lane_id();
+        const int v = dd < N ? table[(long)dd * stride + col] : 0;
+        const int inc = wave_incl_scan(v);
+        if (dd < N) gb[dd] = carry + inc - v;
+        carry += readlane(inc, kWave - 1);
     }
+    if (lane_id() == 0) gb[N] = carry;
 }
 
 // ------------------------------------------------------------------ bf16

@@ -216,33 +216,42 @@ __global__ __launch_bounds__(kBlock) void k_net_prep(Dims D, const int32_t* __re
     if (lane_id() == 0) recv_off[(long)d * (N + 1) + N] = carry;
 }
 
-// One wave per send row (s, i): find its destination segment d, land it at
-// recv_off[d][s] + (i - send_off[s][d]) in rank d's receive buffer, metadata alongside.
-template <int U>
+// kRowsPerBlock consecutive send rows (s, i) per block, one resolved per wave: its segment d is
+// found by a ballot over send_off[s] and it lands at recv_off[d][s] + (i - send_off[s][d]) in
+// rank d's receive buffer, metadata alongside; then the block streams the rows.
 __global__ __launch_bounds__(kBlock) void k_net_dispatch(Dims D, const int32_t* __restrict__ send_off,
                                                          const uint8_t* __restrict__ send_buf,
                                                          const int32_t* __restrict__ send_meta,
                                                          const int32_t* __restrict__ recv_off,
                                                          uint8_t* __restrict__ recv_buf,
                                                          int32_t* __restrict__ recv_meta) {
-    const long g = (long)blockIdx.x * kWavesPerBlock + wave_id();
+    static_assert(kRowsPerBlock == kWavesPerBlock, "one row per wave");
+    __shared__ RowDesc rows[kRowsPerBlock];
     const int N = D.N;
-    if (g >= (long)N * D.TR) return;
-    const long s = g / D.TR;
-    const int i = (int)(g - s * D.TR);
-    const int32_t* so = send_off + s * (N + 1);
-    if (i >= so[N]) return;  // dropped slots leave the tail of the send buffer unused
-    const int d = wave_count_le(so, N, i) - 1;
-    const long r = recv_off[(long)d * (N + 1) + s] + (i - so[d]);
-    if (d < 0 || d >= N || r < 0 || r >= D.B) {
-        set_status(D.status, MOE_EINVAL);
-        return;
+    const long g = (long)blockIdx.x * kRowsPerBlock + wave_id();
+    RowDesc rd = {0, 0, 0, 0};
+    if (g < (long)N * D.TR) {
+        const long s = g / D.TR;
+        const int i = (int)(g - s * D.TR);
+        const int32_t* so = send_off + s * (N + 1);
+        if (i < so[N]) {  // dropped slots leave the tail of the send buffer unused
+            const int d = wave_count_le(so, N, i) - 1;
+            const long r = recv_off[(long)d * (N + 1) + s] + (i - so[d]);
+            if (d >= 0 && d < N && r >= 0 && r < D.B) {
+                const size_t src_row = (size_t)s * D.TR + i, dst_row = (size_t)d * D.B + r;
+                if (lane_id() == 0)
+                    reinterpret_cast<int2*>(recv_meta)[dst_row] =
+                        reinterpret_cast<const int2*>(send_meta)[src_row];
+                rd.src_a = rd.src_b = (uint64_t)(send_buf + src_row * D.P);
+                rd.dst_a = rd.dst_b = (uint64_t)(recv_buf + dst_row * D.P);
+            } else {
+                set_status(D.status, MOE_EINVAL);
+            }
+        }
     }
-    const size_t src_row = (size_t)s * D.TR + i, dst_row = (size_t)d * D.B + r;
-    if (lane_id() == 0)
-        reinterpret_cast<int2*>(recv_meta)[dst_row] = reinterpret_cast<const int2*>(send_meta)[src_row];
-    wave_copy_row<U>(reinterpret_cast<const u32x4*>(send_buf + src_row * D.P),
-                     reinterpret_cast<u32x4*>(recv_buf + dst_row * D.P), D.P16);
+    if (lane_id() == 0) rows[wave_id()] = rd;
+    __syncthreads();
+    block_stream_rows(rows, kRowsPerBlock, D.P16, D.P16, D.P16);
 }
 
 // ------------------------------------------------------------------ receive side
@@ -285,24 +294,8 @@ __global__ __launch_bounds__(kBlock) void k_recv_prep(Dims D, const int32_t* __r
         base_tab[(long)d * N * L + idx] = tab[idx] + off[idx % L];
 }
 
-// Global row bases over ranks: gb[d] = rows held by ranks d' < d, from per-rank totals
-// tot_of(d) = table[d * stride + col].  Done by wave 0 into LDS; the caller syncs.
-__device__ __forceinline__ void rank_bases(const int32_t* table, int stride, int col, int N, int* gb) {
-    if (wave_id() != 0) return;
-    int carry = 0;
-    for (int b = 0; b < N; b += kWave) {
-        const int dd = b + lane_id();
-        const int v = dd < N ? table[(long)dd * stride + col] : 0;
-        const int inc = wave_incl_scan(v);
-        if (dd < N) gb[dd] = carry + inc - v;
-        carry += readlane(inc, kWave - 1);
-    }
-    if (lane_id() == 0) gb[N] = carry;
-}
-
-// One wave per received row (flattened over all ranks): its expert-major position is
-// base[d][s][j] + the row's per-expert rank carried in its metadata.
-template <int U>
+// kRowsPerBlock received rows per block (a global index over all ranks), one resolved per wave:
+// its expert-major position is base[d][s][j] + the per-expert rank carried in its metadata.
 __global__ __launch_bounds__(kBlock) void k_unpack(Dims D, const int32_t* __restrict__ recv_off,
                                                    const uint8_t* __restrict__ recv_buf,
                                                    const int32_t* __restrict__ recv_meta,
@@ -312,39 +305,41 @@ __global__ __launch_bounds__(kBlock) void k_unpack(Dims D, const int32_t* __rest
                                                    int32_t* __restrict__ expert_src,
                                                    int32_t* __restrict__ expert_rpos) {
     extern __shared__ int gb[];  // [N + 1]
+    __shared__ RowDesc rows[kRowsPerBlock];
     const int N = D.N;
     rank_bases(recv_off, N + 1, N, N, gb);
     __syncthreads();
-    const long G = (long)blockIdx.x * kWavesPerBlock + wave_id();
-    if (G >= gb[N]) return;
-    const int d = wave_count_le(gb + 1, N, G);  // ranks whose rows all lie before G
-    const long r = G - gb[d];
-    const int32_t* ro = recv_off + (long)d * (N + 1);
-    const int s = wave_count_le(ro, N, r) - 1;
-    const size_t rrow = (size_t)d * D.B + r;
-    const int2 m = reinterpret_cast<const int2*>(recv_meta)[rrow];
-    const int e = m.x / D.TR;
-    const int i = m.x - e * D.TR;
-    const int j = e - d * D.L;
-    if (j < 0 || j >= D.L || s < 0) {
-        set_status(D.status, MOE_EINVAL);
-        return;
+    const long G = (long)blockIdx.x * kRowsPerBlock + wave_id();
+    RowDesc rd = {0, 0, 0, 0};
+    if (G < gb[N]) {
+        const int d = wave_count_le(gb + 1, N, G);  // ranks whose rows all lie before G
+        const long r = G - gb[d];
+        const int32_t* ro = recv_off + (long)d * (N + 1);
+        const int s = wave_count_le(ro, N, r) - 1;
+        const size_t rrow = (size_t)d * D.B + r;
+        const int2 m = reinterpret_cast<const int2*>(recv_meta)[rrow];
+        const int e = m.x / D.TR;
+        const int i = m.x - e * D.TR;
+        const int j = e - d * D.L;
+        const long q = (j >= 0 && j < D.L && s >= 0)
+                           ? (long)base_tab[((long)d * N + s) * D.L + j] + m.y : -1;
+        if (q >= 0 && q < D.B) {
+            const size_t qrow = (size_t)d * D.B + q;
+            if (lane_id() == 0) {
+                expert_src[qrow] = s * D.TR + i;
+                expert_rpos[qrow] = (int32_t)r;
+            }
+            const long xrow = D.fp8 ? D.H : 2L * D.H;
+            rd.src_a = rd.src_b = (uint64_t)(recv_buf + rrow * D.P);
+            rd.dst_a = (uint64_t)(expert_x + qrow * xrow);
+            rd.dst_b = D.fp8 ? (uint64_t)(expert_scale + qrow * D.nsc) : rd.dst_a;
+        } else {
+            set_status(D.status, MOE_EINVAL);
+        }
     }
-    const long q = (long)base_tab[((long)d * N + s) * D.L + j] + m.y;
-    if (q < 0 || q >= D.B) {
-        set_status(D.status, MOE_EINVAL);
-        return;
-    }
-    const size_t qrow = (size_t)d * D.B + q;
-    if (lane_id() == 0) {
-        expert_src[qrow] = s * D.TR + i;
-        expert_rpos[qrow] = (int32_t)r;
-    }
-    const long xrow = D.fp8 ? D.H : 2L * D.H;
-    const u32x4* src = reinterpret_cast<const u32x4*>(recv_buf + rrow * D.P);
-    u32x4* dst_a = reinterpret_cast<u32x4*>(expert_x + qrow * xrow);
-    u32x4* dst_b = D.fp8 ? reinterpret_cast<u32x4*>(expert_scale + qrow * D.nsc) : dst_a;
-    wave_copy_row<U>(src, src, D.P16, dst_a, dst_b, D.X16, D.P16);
+    if (lane_id() == 0) rows[wave_id()] = rd;
+    __syncthreads();
+    block_stream_rows(rows, kRowsPerBlock, D.P16, D.P16, D.X16);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -391,7 +386,7 @@ hipError_t launch_net_dispatch(const Dims& D, const int32_t* send_off, const voi
     hipLaunchKernelGGL(k_net_prep, dim3((D.N + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock), 0, st,
                        D, send_off, recv_off);
     const long rows = (long)D.N * D.TR;
-    hipLaunchKernelGGL(k_net_dispatch<8>, dim3((rows + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock),
+    hipLaunchKernelGGL(k_net_dispatch, dim3((rows + kRowsPerBlock - 1) / kRowsPerBlock), dim3(kBlock),
                        0, st, D, send_off, (const uint8_t*)send_buf, send_meta,
                        (const int32_t*)recv_off, (uint8_t*)recv_buf, recv_meta);
     return hipGetLastError();
@@ -409,7 +404,7 @@ hipError_t launch_dispatch_recv(const Dims& D, const int32_t* counts, const int3
     hipLaunchKernelGGL(k_recv_prep, dim3(D.N), dim3(kBlock), lds, st, D, counts, expert_cnt, expert_off,
                        base_tab);
     const long rows = (long)D.N * D.TR;  // every received row, over all ranks, is one of these
-    hipLaunchKernelGGL(k_unpack<8>, dim3((rows + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock),
+    hipLaunchKernelGGL(k_unpack, dim3((rows + kRowsPerBlock - 1) / kRowsPerBlock), dim3(kBlock),
                        (D.N + 1) * 4, st, D, recv_off, (const uint8_t*)recv_buf, recv_meta,
                        (const int32_t*)base_tab, (uint8_t*)expert_x, expert_scale, expert_src,
                        expert_rpos);
