@@ -178,9 +178,9 @@ int moe_dispatch_recv(const moe_shape* shape, const int32_t* counts, const int32
     if (rc) return rc;
     if (!aligned(counts, 4) || !aligned(recv_off, 4) || !aligned(recv_buf, 16) ||
         !aligned(recv_meta, 8) || !aligned(expert_x, 16) || !aligned(expert_cnt, 4) ||
-        !aligned(expert_off, 4) || !aligned(expert_src, 4) || !aligned(expert_rpos, 4) ||
-        !aligned(workspace, 4))
+        !aligned(expert_off, 4) || !aligned(expert_src, 4) || !aligned(expert_rpos, 4))
         return MOE_EINVAL;
+    if (moe::recv_workspace_bytes(D) > 0 && !aligned(workspace, 4)) return MOE_EINVAL;
     if (D.fp8 && !aligned(expert_scale, 16)) return MOE_EINVAL;
     return hip_status(moe::launch_dispatch_recv(D, counts, recv_off, recv_buf, recv_meta, expert_x,
                                                 expert_scale, expert_cnt, expert_off, expert_src,

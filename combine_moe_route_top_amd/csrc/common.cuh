@@ -89,6 +89,13 @@ __device__ __forceinline__ int wave_count_le(const int* a, int n, long long x) {
     return c;
 }
 
+// Sum of an int over the 64 lanes of a wave (every lane gets the total).
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
 // ------------------------------------------------------------------ block row streaming
 
 // Nontemporal 16-byte accesses: streamed data does not stay in the caches, and the stores do not

@@ -11,6 +11,8 @@
 //    inside a group;
 //  - receive buffer of rank d: the groups (s -> d) one after another by s;
 //  - expert-major tensor of rank d: by local expert j, then (source, token, slot).
+#include <algorithm>
+
 #include "common.cuh"
 
 namespace moe {
@@ -18,15 +20,26 @@ namespace moe {
 // ------------------------------------------------------------------ count and scan
 
 // Slot (t, k) of rank s is valid if its expert id is in range and differs from the ids of the
-// token's earlier slots.  Invalid slots are dropped and flagged in the status word.
-__device__ __forceinline__ bool slot_valid(const int32_t* __restrict__ idx_s, long i, int R, int E,
-                                           int& e) {
-    e = idx_s[i];
+// token's earlier slots.  Invalid slots are dropped and flagged in the status word.  `chunk`
+// holds the ids of slots c0 .. c0 + n - 1 in LDS; earlier slots come from global memory.
+__device__ __forceinline__ bool slot_valid(const int32_t* __restrict__ idx_s, const int* chunk,
+                                           long c0, long n, long i, int R, int E, int& e) {
+    e = chunk[i - c0];
     if (e < 0 || e >= E) return false;
     const long t0 = (i / R) * R;
-    for (long j = t0; j < i; ++j)
-        if (idx_s[j] == e) return false;
+    for (long j = t0; j < i; ++j) {
+        const int o = (j >= c0 && j < c0 + n) ? chunk[j - c0] : idx_s[j];
+        if (o == e) return false;
+    }
     return true;
+}
+
+// Stage the ids of slots c0 .. c0 + blockDim - 1 (those below TR) into LDS; returns how many.
+__device__ __forceinline__ long stage_chunk(const int32_t* __restrict__ idx_s, int* chunk, long c0, long TR) {
+    const long n = min((long)blockDim.x, TR - c0);
+    if ((long)threadIdx.x < n) chunk[threadIdx.x] = idx_s[c0 + threadIdx.x];
+    __syncthreads();
+    return n;
 }
 
 // Stable rank of this lane's key among the active lanes of the wave with the same key (lower
@@ -50,14 +63,18 @@ __device__ __forceinline__ int wave_match_rank(bool active, int key, int* cnt_ro
 // earlier chunks give each chunk's starting ranks.  Grid (C, N), one slot per thread.
 __global__ __launch_bounds__(1024) void k_send_hist(Dims D, const int32_t* __restrict__ topk_idx,
                                                     int32_t* __restrict__ chunk_cnt, int C) {
-    extern __shared__ int hist[];
+    extern __shared__ int lds_h[];
+    int* hist = lds_h;              // [E]
+    int* chunk = lds_h + D.E;       // [blockDim]
     const int s = blockIdx.y, c = blockIdx.x;
     for (int e = threadIdx.x; e < D.E; e += blockDim.x) hist[e] = 0;
-    __syncthreads();
-    const long i = (long)c * blockDim.x + threadIdx.x;
+    const int32_t* idx_s = topk_idx + (long)s * D.TR;
+    const long c0 = (long)c * blockDim.x;
+    const long n = stage_chunk(idx_s, chunk, c0, D.TR);
+    const long i = c0 + threadIdx.x;
     if (i < D.TR) {
         int e;
-        if (slot_valid(topk_idx + (long)s * D.TR, i, D.R, D.E, e)) atomicAdd(&hist[e], 1);
+        if (slot_valid(idx_s, chunk, c0, n, i, D.R, D.E, e)) atomicAdd(&hist[e], 1);
     }
     __syncthreads();
     for (int e = threadIdx.x; e < D.E; e += blockDim.x)
@@ -83,15 +100,17 @@ __global__ __launch_bounds__(1024) void k_send_rank(Dims D, const int32_t* __res
     int* base = wcnt + W * K;
     int* tot = base + K;
     int* soff = tot + K;
+    int* chunk = soff + N + 1;  // [blockDim]
     for (int i = threadIdx.x; i < W * K; i += blockDim.x) wcnt[i] = 0;
-    __syncthreads();
 
     const int32_t* idx_s = topk_idx + (long)s * TR;
-    const long i = (long)c * blockDim.x + threadIdx.x;
+    const long c0 = (long)c * blockDim.x;
+    const long n = stage_chunk(idx_s, chunk, c0, TR);  // also orders the zeroing above
+    const long i = c0 + threadIdx.x;
     int e = -1;
     bool valid = false;
     if (i < TR) {
-        valid = slot_valid(idx_s, i, D.R, E, e);
+        valid = slot_valid(idx_s, chunk, c0, n, i, D.R, E, e);
         if (!valid) set_status(D.status, MOE_EBADIDX);
     }
     const int d = valid ? e / L : 0;
@@ -198,46 +217,52 @@ __global__ __launch_bounds__(kBlock) void k_send_pack(Dims D, const uint8_t* __r
 
 // ------------------------------------------------------------------ network stand-in
 
-// recv_off[d][s] = rows sources s' < s send to d.  One wave per destination d.
-__global__ __launch_bounds__(kBlock) void k_net_prep(Dims D, const int32_t* __restrict__ send_off,
-                                                     int32_t* __restrict__ recv_off) {
-    const int d = blockIdx.x * kWavesPerBlock + wave_id();
-    if (d >= D.N) return;
-    const int N = D.N;
-    int carry = 0;
-    for (int base = 0; base < N; base += kWave) {
-        const int s = base + lane_id();
-        int n = 0;
-        if (s < N) n = send_off[(long)s * (N + 1) + d + 1] - send_off[(long)s * (N + 1) + d];
-        const int inc = wave_incl_scan(n);
-        if (s < N) recv_off[(long)d * (N + 1) + s] = carry + inc - n;
-        carry += readlane(inc, kWave - 1);
+// recv_off[d][s] = rows the sources s' < s send to rank d, from the exchanged table (every
+// source's send_off): a wave sum over s'.
+__device__ __forceinline__ int recv_offset(const int32_t* __restrict__ send_off, int N, int d, int s) {
+    int v = 0;
+    for (int b = 0; b < s; b += kWave) {
+        const int sp = b + lane_id();
+        if (sp < s) v += send_off[(long)sp * (N + 1) + d + 1] - send_off[(long)sp * (N + 1) + d];
     }
-    if (lane_id() == 0) recv_off[(long)d * (N + 1) + N] = carry;
+    return wave_sum(v);
 }
 
 // kRowsPerBlock consecutive send rows (s, i) per block, one resolved per wave: its segment d is
 // found by a ballot over send_off[s] and it lands at recv_off[d][s] + (i - send_off[s][d]) in
-// rank d's receive buffer, metadata alongside; then the block streams the rows.
+// rank d's receive buffer, metadata alongside; then the block streams the rows.  Blocks 0..N-1
+// also write row d = blockIdx of the recv_off output (a wave scan over sources).
 __global__ __launch_bounds__(kBlock) void k_net_dispatch(Dims D, const int32_t* __restrict__ send_off,
                                                          const uint8_t* __restrict__ send_buf,
                                                          const int32_t* __restrict__ send_meta,
-                                                         const int32_t* __restrict__ recv_off,
                                                          uint8_t* __restrict__ recv_buf,
-                                                         int32_t* __restrict__ recv_meta) {
+                                                         int32_t* __restrict__ recv_meta,
+                                                         int32_t* __restrict__ recv_off) {
     static_assert(kRowsPerBlock == kWavesPerBlock, "one row per wave");
     __shared__ RowDesc rows[kRowsPerBlock];
     const int N = D.N;
+    if (blockIdx.x < (unsigned)N && wave_id() == kWavesPerBlock - 1) {
+        const int d = blockIdx.x;
+        int carry = 0;
+        for (int b = 0; b < N; b += kWave) {
+            const int sp = b + lane_id();
+            const int n = sp < N ? send_off[(long)sp * (N + 1) + d + 1] - send_off[(long)sp * (N + 1) + d] : 0;
+            const int inc = wave_incl_scan(n);
+            if (sp < N) recv_off[(long)d * (N + 1) + sp] = carry + inc - n;
+            carry += readlane(inc, kWave - 1);
+        }
+        if (lane_id() == 0) recv_off[(long)d * (N + 1) + N] = carry;
+    }
     const long g = (long)blockIdx.x * kRowsPerBlock + wave_id();
     RowDesc rd = {0, 0, 0, 0};
     if (g < (long)N * D.TR) {
-        const long s = g / D.TR;
-        const int i = (int)(g - s * D.TR);
-        const int32_t* so = send_off + s * (N + 1);
+        const int s = (int)(g / D.TR);
+        const int i = (int)(g - (long)s * D.TR);
+        const int32_t* so = send_off + (long)s * (N + 1);
         if (i < so[N]) {  // dropped slots leave the tail of the send buffer unused
             const int d = wave_count_le(so, N, i) - 1;
-            const long r = recv_off[(long)d * (N + 1) + s] + (i - so[d]);
-            if (d >= 0 && d < N && r >= 0 && r < D.B) {
+            const long r = d >= 0 ? recv_offset(send_off, N, d, s) + (i - so[d]) : -1;
+            if (r >= 0 && r < D.B) {
                 const size_t src_row = (size_t)s * D.TR + i, dst_row = (size_t)d * D.B + r;
                 if (lane_id() == 0)
                     reinterpret_cast<int2*>(recv_meta)[dst_row] =
@@ -256,58 +281,59 @@ __global__ __launch_bounds__(kBlock) void k_net_dispatch(Dims D, const int32_t* 
 
 // ------------------------------------------------------------------ receive side
 
-// Per destination rank d: expert_cnt/expert_off, and base[d][s][j] = expert_off[d][j] + rows of
-// local expert j from sources s' < s (the start of source s's run inside expert j's group).
-// One block per rank; LDS tab[N][L] of counts, scanned over s by one wave per local expert.
-__global__ __launch_bounds__(kBlock) void k_recv_prep(Dims D, const int32_t* __restrict__ counts,
-                                                      int32_t* __restrict__ expert_cnt,
-                                                      int32_t* __restrict__ expert_off,
-                                                      int32_t* __restrict__ base_tab) {
-    extern __shared__ int lds[];
-    const int d = blockIdx.x;
-    const int N = D.N, L = D.L, E = D.E;
-    int* tab = lds;            // [N][L]
-    int* cnt = tab + N * L;    // [L]
-    int* off = cnt + L;        // [L + 1]
-    for (int idx = threadIdx.x; idx < N * L; idx += blockDim.x) {
-        const int s = idx / L, j = idx - s * L;
-        tab[idx] = counts[(long)s * E + d * L + j];
+// Where the rows of source s for local expert j start in rank d's expert-major order:
+// (rows of experts d*L + j' < d*L + j from every source) + (rows of expert d*L + j from sources
+// s' < s).  A wave sum over sources; every lane gets the result.
+__device__ __forceinline__ long expert_base(const int32_t* __restrict__ counts, int N, int E, int L, int d,
+                                            int s, int j) {
+    const int W = j + 1;  // columns d*L .. d*L + j of every source's counts
+    const int total = N * W;
+    int v = 0;
+#pragma unroll 4
+    for (int f = lane_id(); f < total; f += kWave) {
+        const int sp = f / W, jj = f - sp * W;
+        const int c = counts[(long)sp * E + d * L + jj];
+        if (jj < j || sp < s) v += c;
     }
-    __syncthreads();
-    for (int j = wave_id(); j < L; j += kWavesPerBlock) {  // exclusive scan over s of column j
-        int carry = 0;
-        for (int b = 0; b < N; b += kWave) {
-            const int s = b + lane_id();
-            const int v = s < N ? tab[s * L + j] : 0;
-            const int inc = wave_incl_scan(v);
-            if (s < N) tab[s * L + j] = carry + inc - v;
-            carry += readlane(inc, kWave - 1);
-        }
-        if (lane_id() == 0) cnt[j] = carry;
-    }
-    __syncthreads();
-    if (wave_id() == 0) wave_excl_scan_array(cnt, off, L);
-    __syncthreads();
-    for (int j = threadIdx.x; j < L; j += blockDim.x) expert_cnt[(long)d * L + j] = cnt[j];
-    for (int j = threadIdx.x; j <= L; j += blockDim.x) expert_off[(long)d * (L + 1) + j] = off[j];
-    for (int idx = threadIdx.x; idx < N * L; idx += blockDim.x)
-        base_tab[(long)d * N * L + idx] = tab[idx] + off[idx % L];
+    return wave_sum(v);
 }
 
 // kRowsPerBlock received rows per block (a global index over all ranks), one resolved per wave:
-// its expert-major position is base[d][s][j] + the per-expert rank carried in its metadata.
-__global__ __launch_bounds__(kBlock) void k_unpack(Dims D, const int32_t* __restrict__ recv_off,
+// its expert-major position is expert_base(d, s, j) + the per-expert rank carried in its
+// metadata.  Blocks 0..N-1 also write rank d = blockIdx's expert_cnt and expert_off.
+__global__ __launch_bounds__(kBlock) void k_unpack(Dims D, const int32_t* __restrict__ counts,
+                                                   const int32_t* __restrict__ recv_off,
                                                    const uint8_t* __restrict__ recv_buf,
                                                    const int32_t* __restrict__ recv_meta,
-                                                   const int32_t* __restrict__ base_tab,
                                                    uint8_t* __restrict__ expert_x,
                                                    float* __restrict__ expert_scale,
+                                                   int32_t* __restrict__ expert_cnt,
+                                                   int32_t* __restrict__ expert_off,
                                                    int32_t* __restrict__ expert_src,
                                                    int32_t* __restrict__ expert_rpos) {
     extern __shared__ int gb[];  // [N + 1]
     __shared__ RowDesc rows[kRowsPerBlock];
-    const int N = D.N;
+    const int N = D.N, L = D.L, E = D.E;
     rank_bases(recv_off, N + 1, N, N, gb);
+    if (blockIdx.x < (unsigned)N && wave_id() == kWavesPerBlock - 1) {
+        const int d = blockIdx.x;
+        int carry = 0;
+        for (int b = 0; b < L; b += kWave) {
+            const int j = b + lane_id();
+            int c = 0;
+            if (j < L) {
+#pragma unroll 8
+                for (int sp = 0; sp < N; ++sp) c += counts[(long)sp * E + d * L + j];
+            }
+            const int inc = wave_incl_scan(c);
+            if (j < L) {
+                expert_cnt[(long)d * L + j] = c;
+                expert_off[(long)d * (L + 1) + j] = carry + inc - c;
+            }
+            carry += readlane(inc, kWave - 1);
+        }
+        if (lane_id() == 0) expert_off[(long)d * (L + 1) + L] = carry;
+    }
     __syncthreads();
     const long G = (long)blockIdx.x * kRowsPerBlock + wave_id();
     RowDesc rd = {0, 0, 0, 0};
@@ -320,9 +346,8 @@ __global__ __launch_bounds__(kBlock) void k_unpack(Dims D, const int32_t* __rest
         const int2 m = reinterpret_cast<const int2*>(recv_meta)[rrow];
         const int e = m.x / D.TR;
         const int i = m.x - e * D.TR;
-        const int j = e - d * D.L;
-        const long q = (j >= 0 && j < D.L && s >= 0)
-                           ? (long)base_tab[((long)d * N + s) * D.L + j] + m.y : -1;
+        const int j = e - d * L;
+        const long q = (j >= 0 && j < L && s >= 0) ? expert_base(counts, N, E, L, d, s, j) + m.y : -1;
         if (q >= 0 && q < D.B) {
             const size_t qrow = (size_t)d * D.B + q;
             if (lane_id() == 0) {
@@ -346,7 +371,7 @@ __global__ __launch_bounds__(kBlock) void k_unpack(Dims D, const int32_t* __rest
 
 static size_t send_rank_lds(const Dims& D, int CH) {
     const size_t K = (size_t)D.E + D.N;
-    return ((CH / kWave) * K + 2 * K + D.N + 1) * 4;
+    return ((CH / kWave) * K + 2 * K + D.N + 1 + CH) * 4;
 }
 
 static int send_chunk(const Dims& D) {
@@ -369,7 +394,7 @@ hipError_t launch_dispatch_send(const Dims& D, const void* x, const float* x_sca
     const int C = (D.TR + CH - 1) / CH;
     int32_t* chunk_cnt = static_cast<int32_t*>(workspace);
     if (C > 1) {
-        hipLaunchKernelGGL(k_send_hist, dim3(C, D.N), dim3(CH), D.E * 4, st, D, topk_idx, chunk_cnt, C);
+        hipLaunchKernelGGL(k_send_hist, dim3(C, D.N), dim3(CH), (D.E + CH) * 4, st, D, topk_idx, chunk_cnt, C);
     }
     const size_t lds = send_rank_lds(D, CH);
     hipLaunchKernelGGL(k_send_rank, dim3(C, D.N), dim3(CH), lds, st, D, topk_idx,
@@ -383,31 +408,25 @@ hipError_t launch_dispatch_send(const Dims& D, const void* x, const float* x_sca
 hipError_t launch_net_dispatch(const Dims& D, const int32_t* send_off, const void* send_buf,
                                const int32_t* send_meta, void* recv_buf, int32_t* recv_meta,
                                int32_t* recv_off, hipStream_t st) {
-    hipLaunchKernelGGL(k_net_prep, dim3((D.N + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock), 0, st,
-                       D, send_off, recv_off);
     const long rows = (long)D.N * D.TR;
-    hipLaunchKernelGGL(k_net_dispatch, dim3((rows + kRowsPerBlock - 1) / kRowsPerBlock), dim3(kBlock),
-                       0, st, D, send_off, (const uint8_t*)send_buf, send_meta,
-                       (const int32_t*)recv_off, (uint8_t*)recv_buf, recv_meta);
+    const long blocks = std::max<long>((rows + kRowsPerBlock - 1) / kRowsPerBlock, D.N);
+    hipLaunchKernelGGL(k_net_dispatch, dim3(blocks), dim3(kBlock), 0, st, D, send_off,
+                       (const uint8_t*)send_buf, send_meta, (uint8_t*)recv_buf, recv_meta, recv_off);
     return hipGetLastError();
 }
 
-size_t recv_workspace_bytes(const Dims& D) { return (size_t)D.N * D.E * 4; }
+size_t recv_workspace_bytes(const Dims&) { return 0; }
 
 hipError_t launch_dispatch_recv(const Dims& D, const int32_t* counts, const int32_t* recv_off,
                                 const void* recv_buf, const int32_t* recv_meta, void* expert_x,
                                 float* expert_scale, int32_t* expert_cnt, int32_t* expert_off,
-                                int32_t* expert_src, int32_t* expert_rpos, void* workspace,
+                                int32_t* expert_src, int32_t* expert_rpos, void* /*workspace*/,
                                 hipStream_t st) {
-    int32_t* base_tab = static_cast<int32_t*>(workspace);
-    const size_t lds = ((size_t)D.N * D.L + 2 * D.L + 1) * 4;
-    hipLaunchKernelGGL(k_recv_prep, dim3(D.N), dim3(kBlock), lds, st, D, counts, expert_cnt, expert_off,
-                       base_tab);
     const long rows = (long)D.N * D.TR;  // every received row, over all ranks, is one of these
-    hipLaunchKernelGGL(k_unpack, dim3((rows + kRowsPerBlock - 1) / kRowsPerBlock), dim3(kBlock),
-                       (D.N + 1) * 4, st, D, recv_off, (const uint8_t*)recv_buf, recv_meta,
-                       (const int32_t*)base_tab, (uint8_t*)expert_x, expert_scale, expert_src,
-                       expert_rpos);
+    const long blocks = std::max<long>((rows + kRowsPerBlock - 1) / kRowsPerBlock, D.N);
+    hipLaunchKernelGGL(k_unpack, dim3(blocks), dim3(kBlock), (D.N + 1) * 4, st, D, counts, recv_off,
+                       (const uint8_t*)recv_buf, recv_meta, (uint8_t*)expert_x, expert_scale, expert_cnt,
+                       expert_off, expert_src, expert_rpos);
     return hipGetLastError();
 }
 

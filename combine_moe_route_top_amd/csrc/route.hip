@@ -1,4 +1,4 @@
-// route.hip -- top-R expert selection and softmax weights, one wave per token.
+// route.hip -- top-R expert selection and softmax weights, one lane group per token.
 //
 // [DSK] = "Lower latency and higher throughput with multi-node DeepSeek deployment",
 // sections Expert Parallelism and MoE Router: each token is sent to R routed experts picked by a
@@ -7,9 +7,12 @@
 // the weights come from the router's probability distribution.
 //
 // Selection order: descending fp32 (logit + bias), ties to the lower expert id (-0 == +0).
-// Each lane holds experts lane, lane+64, ... as 64-bit keys (ordered score, ~expert); R rounds
-// of a wave max pick the winners.  Weights: softmax over the R selected values in fp64,
-// summed in slot order and rounded once to fp32.
+// A group of G lanes (16, 32 or 64; 64/G tokens per wave) holds a token's experts
+// gl, gl+G, ... as order-preserving score bits.  Each of the R rounds takes the lane's best
+// (score, lowest id) as a 64-bit key (score bits, ~expert id), then a group max: DPP row
+// rotations by 1, 2, 4, 8 inside each 16-lane row (plain VALU moves, no LDS crossbar), and for
+// G > 16 one or two lane swaps across rows.  Weights: softmax over the R selected values in fp64, summed in slot order, rounded
+// once to fp32.
 #include "common.cuh"
 
 namespace moe {
@@ -26,87 +29,127 @@ __device__ __forceinline__ float from_ordered_bits(uint32_t o) {
     return __uint_as_float(u);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        uint32_t lo = __shfl_xor((uint32_t)x, off, kWave);
-        uint32_t hi = __shfl_xor((uint32_t)(x >> 32), off, kWave);
-        uint64_t o = ((uint64_t)hi << 32) | lo;
-        x = o > x ? o : x;
-    }
+// DPP row_ror:n (rotate inside each 16-lane row), n = 1..15: control 0x120 + n.
+template <int N>
+__device__ __forceinline__ uint64_t row_ror_u64(uint64_t x) {
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, 0x120 + N, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), 0x120 + N, 0xF, 0xF, false);
+    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
+    const uint32_t lo = __shfl_xor((uint32_t)x, m, kWave);
+    const uint32_t hi = __shfl_xor((uint32_t)(x >> 32), m, kWave);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Max over each group of G consecutive lanes; every lane of the group gets it.
+template <int G>
+__device__ __forceinline__ uint64_t group_max(uint64_t x) {
+    x = umax64(x, row_ror_u64<1>(x));
+    x = umax64(x, row_ror_u64<2>(x));
+    x = umax64(x, row_ror_u64<4>(x));
+    x = umax64(x, row_ror_u64<8>(x));
+    if constexpr (G >= 32) x = umax64(x, shfl_xor_u64(x, 16));
+    if constexpr (G >= 64) x = umax64(x, shfl_xor_u64(x, 32));
     return x;
 }
 
-template <int VPL>
+template <int G, int VPL>
 __global__ __launch_bounds__(kBlock) void k_route(const float* __restrict__ logits,
                                                   const float* __restrict__ bias,
                                                   int32_t* __restrict__ topk_idx,
                                                   float* __restrict__ topk_w, int ntok, int E,
                                                   int R) {
+    constexpr int TPW = kWave / G;  // tokens per wave
     const int lane = lane_id();
-    const long tok = (long)blockIdx.x * kWavesPerBlock + wave_id();
-    if (tok >= ntok) return;
-    const float* row = logits + tok * E;
+    const int grp = lane / G, gl = lane % G;
+    const long tok = ((long)blockIdx.x * kWavesPerBlock + wave_id()) * TPW + grp;
+    // no early exit: every lane takes part in the DPP rotations and lane swaps
+    const bool active = tok < ntok;
+    const float* row = logits + (active ? tok : 0) * E;
 
-    uint64_t key[VPL];
+    // ordered scores; 0 marks "taken" or "no expert" (every finite score maps above 0).  Within a
+    // lane the expert id grows with m, so a strict '>' scan keeps the lower id on ties.
+    // Loads are unconditional (indices clamped into the row) so that they all issue together.
+    float lv[VPL];
 #pragma unroll
-    for (int m = 0; m < VPL; ++m) {
-        int e = lane + kWave * m;
-        key[m] = 0;
-        if (e < E) {
-            float v = bias ? row[e] + bias[e] : row[e];
-            key[m] = ((uint64_t)ordered_bits(v) << 32) | (uint32_t)(~(uint32_t)e);
-        }
+    for (int m = 0; m < VPL; ++m) lv[m] = row[min(gl + G * m, E - 1)];
+    if (bias) {
+#pragma unroll
+        for (int m = 0; m < VPL; ++m) lv[m] += bias[min(gl + G * m, E - 1)];
     }
+    uint32_t sc[VPL];
+#pragma unroll
+    for (int m = 0; m < VPL; ++m) sc[m] = (active && gl + G * m < E) ? ordered_bits(lv[m]) : 0u;
 
     int my_e = 0;
     float my_v = 0.0f;
+#pragma unroll 1
     for (int k = 0; k < R; ++k) {
-        uint64_t best = 0;
+        uint32_t bs = 0;
+        int bm = 0;
 #pragma unroll
-        for (int m = 0; m < VPL; ++m) best = key[m] > best ? key[m] : best;
-        best = wave_max_u64(best);
+        for (int m = 0; m < VPL; ++m)
+            if (sc[m] > bs) {
+                bs = sc[m];
+                bm = m;
+            }
+        uint64_t best = bs ? (((uint64_t)bs << 32) | (uint32_t)(~(uint32_t)(gl + G * bm))) : 0;
+        best = group_max<G>(best);
         const int e = (int)(~(uint32_t)best);
         const float v = from_ordered_bits((uint32_t)(best >> 32));
 #pragma unroll
         for (int m = 0; m < VPL; ++m)
-            if (lane + kWave * m == e) key[m] = 0;  // taken
-        if (lane == k) {
+            if (gl + G * m == e) sc[m] = 0;  // taken
+        if (gl == k) {
             my_e = e;
             my_v = v;
         }
     }
 
-    // softmax over the selected values, shifted by the largest (slot 0), in fp64
-    const double v0 = (double)readlane_f(my_v, 0);
-    const double z = exp((double)my_v - v0);
+    // softmax over the group's R selected values, shifted by the largest (slot 0), in fp64,
+    // summed in slot order by every lane of the group
+    const int base = grp * G;
+    const double v0 = (double)__shfl(my_v, base, kWave);
     double sum = 0.0;
-    for (int k = 0; k < R; ++k) {
-        int lo = __builtin_amdgcn_readlane((int)(uint32_t)__double_as_longlong(z), k);
-        int hi = __builtin_amdgcn_readlane((int)(uint32_t)(__double_as_longlong(z) >> 32), k);
-        sum += __longlong_as_double(((long long)(uint32_t)hi << 32) | (uint32_t)lo);
+    for (int j = 0; j < R; ++j) sum += exp((double)__shfl(my_v, base + j, kWave) - v0);
+    const double z = exp((double)my_v - v0);
+    if (active && gl < R) {
+        topk_idx[tok * R + gl] = my_e;
+        topk_w[tok * R + gl] = (float)(z / sum);
     }
-    if (lane < R) {
-        topk_idx[tok * R + lane] = my_e;
-        topk_w[tok * R + lane] = (float)(z / sum);
-    }
+}
+
+template <int G>
+static void launch_g(int vpl, dim3 grid, hipStream_t st, const float* logits, const float* bias,
+                     int32_t* topk_idx, float* topk_w, int ntok, int E, int R) {
+    if (vpl <= 1)
+        hipLaunchKernelGGL((k_route<G, 1>), grid, dim3(kBlock), 0, st, logits, bias, topk_idx, topk_w, ntok, E, R);
+    else if (vpl <= 2)
+        hipLaunchKernelGGL((k_route<G, 2>), grid, dim3(kBlock), 0, st, logits, bias, topk_idx, topk_w, ntok, E, R);
+    else if (vpl <= 4)
+        hipLaunchKernelGGL((k_route<G, 4>), grid, dim3(kBlock), 0, st, logits, bias, topk_idx, topk_w, ntok, E, R);
+    else if (vpl <= 8)
+        hipLaunchKernelGGL((k_route<G, 8>), grid, dim3(kBlock), 0, st, logits, bias, topk_idx, topk_w, ntok, E, R);
+    else
+        hipLaunchKernelGGL((k_route<G, 16>), grid, dim3(kBlock), 0, st, logits, bias, topk_idx, topk_w, ntok, E, R);
 }
 
 hipError_t launch_route(const Dims& D, const float* logits, const float* bias, int32_t* topk_idx,
                         float* topk_w, hipStream_t st) {
     const int ntok = D.N * D.T;
-    dim3 grid((ntok + kWavesPerBlock - 1) / kWavesPerBlock), block(kBlock);
-    const int vpl = (D.E + kWave - 1) / kWave;
-    if (vpl <= 1)
-        hipLaunchKernelGGL(k_route<1>, grid, block, 0, st, logits, bias, topk_idx, topk_w, ntok, D.E, D.R);
-    else if (vpl <= 2)
-        hipLaunchKernelGGL(k_route<2>, grid, block, 0, st, logits, bias, topk_idx, topk_w, ntok, D.E, D.R);
-    else if (vpl <= 4)
-        hipLaunchKernelGGL(k_route<4>, grid, block, 0, st, logits, bias, topk_idx, topk_w, ntok, D.E, D.R);
-    else if (vpl <= 8)
-        hipLaunchKernelGGL(k_route<8>, grid, block, 0, st, logits, bias, topk_idx, topk_w, ntok, D.E, D.R);
-    else
-        hipLaunchKernelGGL(k_route<16>, grid, block, 0, st, logits, bias, topk_idx, topk_w, ntok, D.E, D.R);
+    // the smallest group with at most 16 experts per lane and at least R lanes
+    int G = 16;
+    while (G < 64 && (D.E > 16 * G || D.R > G)) G *= 2;
+    const int vpl = (D.E + G - 1) / G;
+    const long waves = ((long)ntok * G + kWave - 1) / kWave;
+    const dim3 grid((waves + kWavesPerBlock - 1) / kWavesPerBlock);
+    if (G == 16) launch_g<16>(vpl, grid, st, logits, bias, topk_idx, topk_w, ntok, D.E, D.R);
+    else if (G == 32) launch_g<32>(vpl, grid, st, logits, bias, topk_idx, topk_w, ntok, D.E, D.R);
+    else launch_g<64>(vpl, grid, st, logits, bias, topk_idx, topk_w, ntok, D.E, D.R);
     return hipGetLastError();
 }
 

@@ -136,7 +136,7 @@ int moe_net_dispatch(const moe_shape* shape, const int32_t* send_off, const void
  *   expert_off   i32[N][L+1] (out)  exclusive scan of expert_cnt
  *   expert_src   i32[N][B] (out)    s*T*R + t*R + k of each expert-major row
  *   expert_rpos  i32[N][B] (out)    the row's index in recv_buf (its receive position)
- *   workspace    as for moe_dispatch_send */
+ *   workspace    reserved; this call needs none (may be NULL) */
 int moe_dispatch_recv(const moe_shape* shape, const int32_t* counts, const int32_t* recv_off,
                       const void* recv_buf, const int32_t* recv_meta, void* expert_x,
                       float* expert_scale, int32_t* expert_cnt, int32_t* expert_off,

@@ -84,7 +84,7 @@ def test_null_and_misaligned_pointers_rejected_before_launch():
         lambda: moe.moe_net_dispatch(sh, good, good, good, bad, good, good, stream=0),
         lambda: moe.moe_dispatch_recv(sh, good, good, good, good, bad, None, good, good, good, good,
                                       good, stream=0),
-        lambda: moe.moe_dispatch_recv(sh, good, good, good, good, good, None, good, good, good, good,
+        lambda: moe.moe_dispatch_recv(sh, None, good, good, good, good, None, good, good, good, good,
                                       None, stream=0),
         lambda: moe.moe_combine(sh, good, good, good, good, good, good, good, good, bad, stream=0),
         lambda: moe.moe_expert_stub(sh, 2, good, None, good, good, stream=0),
