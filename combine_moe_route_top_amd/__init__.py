@@ -18,7 +18,9 @@ from dataclasses import dataclass
 import torch  # noqa: F401  (must precede the CDLL load: shared HIP runtime)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe.so")
+# MOE_LIB names another build of the same sources (e.g. one compiled with different launch-shape
+# constants); default: the in-tree libmoe.so.
+LIB_PATH = os.environ.get("MOE_LIB") or os.path.join(_HERE, "libmoe.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "moe.h")
 
 if not os.path.exists(LIB_PATH):

@@ -22,16 +22,23 @@ def sources():
     return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every csrc/*.hip into libmoe.so (always recompiles)."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), *sources(), "-o", tmp]
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compile every csrc/*.hip into libmoe.so (always recompiles).  `defines` (NAME=VALUE)
+    override launch-shape constants for an alternative build written to `out`."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *FLAGS, *["-D" + d for d in defines], "-I", os.path.join(ROOT, "include"),
+           *sources(), "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import sys
+    args = sys.argv[1:]
+    out = LIB
+    if args and args[0].endswith(".so"):
+        out, args = args[0], args[1:]
+    print(build(verbose=True, out=out, defines=args))

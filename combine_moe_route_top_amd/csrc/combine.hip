@@ -86,20 +86,21 @@ __global__ __launch_bounds__(kBlock) void k_expert_stub(Dims D, int mode, const 
 
 // ------------------------------------------------------------------ combine
 
-// Shuffle: cs[d][expert_rpos[q]] = y[d][q].  kRowsPerBlock expert-major rows per block (a global
+// Shuffle: cs[d][expert_rpos[q]] = y[d][q].  RPB expert-major rows per block (a global
 // index over all ranks), one resolved per wave, then streamed.
+template <int RPB, int U>
 __global__ __launch_bounds__(kBlock) void k_combine_pack(Dims D, const uint16_t* __restrict__ expert_y,
                                                          const int32_t* __restrict__ expert_rpos,
                                                          const int32_t* __restrict__ recv_off,
                                                          uint16_t* __restrict__ cs_buf) {
     extern __shared__ int gb[];
-    __shared__ RowDesc rows[kRowsPerBlock];
+    __shared__ RowDesc rows[RPB];
     const int N = D.N;
     rank_bases(recv_off, N + 1, N, N, gb);
     __syncthreads();
-    const long G = (long)blockIdx.x * kRowsPerBlock + wave_id();
+    const long G = (long)blockIdx.x * RPB + wave_id();
     RowDesc rd = {0, 0, 0, 0};
-    if (G < gb[N]) {
+    if (wave_id() < RPB && G < gb[N]) {
         const int d = wave_count_le(gb + 1, N, G);
         const long q = G - gb[d];
         const long r = expert_rpos[(size_t)d * D.B + q];
@@ -110,26 +111,27 @@ __global__ __launch_bounds__(kBlock) void k_combine_pack(Dims D, const uint16_t*
             set_status(D.status, MOE_EINVAL);
         }
     }
-    if (lane_id() == 0) rows[wave_id()] = rd;
+    if (wave_id() < RPB && lane_id() == 0) rows[wave_id()] = rd;
     __syncthreads();
-    block_stream_rows(rows, kRowsPerBlock, D.Y16, D.Y16, D.Y16);
+    block_stream_rows<U>(rows, RPB, D.Y16, D.Y16, D.Y16);
 }
 
 // Network back: rank d's combine send buffer is read in order (a global index over all ranks);
 // row r of segment (s -> d) lands at send_off[s][d] + (r - recv_off[d][s]) in rank s's combine
 // receive buffer, where s's dispatch send buffer had it.
+template <int RPB, int U>
 __global__ __launch_bounds__(kBlock) void k_combine_net(Dims D, const uint16_t* __restrict__ cs_buf,
                                                         const int32_t* __restrict__ recv_off,
                                                         const int32_t* __restrict__ send_off,
                                                         uint16_t* __restrict__ cr_buf) {
     extern __shared__ int gb[];
-    __shared__ RowDesc rows[kRowsPerBlock];
+    __shared__ RowDesc rows[RPB];
     const int N = D.N;
     rank_bases(recv_off, N + 1, N, N, gb);
     __syncthreads();
-    const long G = (long)blockIdx.x * kRowsPerBlock + wave_id();
+    const long G = (long)blockIdx.x * RPB + wave_id();
     RowDesc rd = {0, 0, 0, 0};
-    if (G < gb[N]) {
+    if (wave_id() < RPB && G < gb[N]) {
         const int d = wave_count_le(gb + 1, N, G);
         const long r = G - gb[d];
         const int32_t* ro = recv_off + (long)d * (N + 1);
@@ -142,9 +144,9 @@ __global__ __launch_bounds__(kBlock) void k_combine_net(Dims D, const uint16_t* 
             set_status(D.status, MOE_EINVAL);
         }
     }
-    if (lane_id() == 0) rows[wave_id()] = rd;
+    if (wave_id() < RPB && lane_id() == 0) rows[wave_id()] = rd;
     __syncthreads();
-    block_stream_rows(rows, kRowsPerBlock, D.Y16, D.Y16, D.Y16);
+    block_stream_rows<U>(rows, RPB, D.Y16, D.Y16, D.Y16);
 }
 
 // Weighted sum: out[s][t] = bf16(sum_k w[k] * cr[s][send_pos[k]]), fp32 fused multiply-adds in
@@ -233,11 +235,20 @@ hipError_t launch_combine(const Dims& D, const uint16_t* expert_y, const int32_t
                           const float* topk_w, uint16_t* cs_buf, uint16_t* cr_buf, uint16_t* out,
                           hipStream_t st) {
     const long rows = (long)D.N * D.TR;  // every received row, over all ranks, is one of these
-    const dim3 grid_rows((rows + kRowsPerBlock - 1) / kRowsPerBlock);
-    hipLaunchKernelGGL(k_combine_pack, grid_rows, dim3(kBlock), (D.N + 1) * 4, st, D, expert_y,
-                       expert_rpos, recv_off, cs_buf);
-    hipLaunchKernelGGL(k_combine_net, grid_rows, dim3(kBlock), (D.N + 1) * 4, st, D,
-                       (const uint16_t*)cs_buf, recv_off, send_off, cr_buf);
+    const StreamShape sp = stream_shape(D.Y16, MOE_CPACK_MIN_CHUNKS);
+    const StreamShape sn = stream_shape(D.Y16, MOE_CNET_MIN_CHUNKS);
+#define MOE_LAUNCH(R_, U_)                                                                          \
+    if (sp.rpb == R_ && sp.u == U_)                                                                 \
+        hipLaunchKernelGGL((k_combine_pack<R_, U_>), dim3((rows + R_ - 1) / R_), dim3(kBlock),       \
+                           (D.N + 1) * 4, st, D, expert_y, expert_rpos, recv_off, cs_buf);
+    MOE_STREAM_SHAPES(MOE_LAUNCH)
+#undef MOE_LAUNCH
+#define MOE_LAUNCH(R_, U_)                                                                          \
+    if (sn.rpb == R_ && sn.u == U_)                                                                 \
+        hipLaunchKernelGGL((k_combine_net<R_, U_>), dim3((rows + R_ - 1) / R_), dim3(kBlock),        \
+                           (D.N + 1) * 4, st, D, (const uint16_t*)cs_buf, recv_off, send_off, cr_buf);
+    MOE_STREAM_SHAPES(MOE_LAUNCH)
+#undef MOE_LAUNCH
     const long waves = (long)D.N * D.T * kWsumWaves;
     hipLaunchKernelGGL(k_wsum, dim3((waves + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock), 0, st, D,
                        (const uint16_t*)cr_buf, send_pos, topk_w, out);

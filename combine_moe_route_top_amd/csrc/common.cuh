@@ -103,10 +103,10 @@ __device__ __forceinline__ int wave_sum(int v) {
 __device__ __forceinline__ u32x4 ld_nt(const u32x4* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void st_nt(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
 
-// Rows handled by one 256-thread block of a row-copy kernel: one row per wave is resolved (its
-// source and destination found), then all 256 threads stream the rows' 16-byte chunks.
-constexpr int kRowsPerBlock = 4;
-constexpr int kStreamUnroll = 8;  // 16-byte loads in flight per thread
+// A row-copy kernel block (256 threads) handles RPB consecutive rows of its source: one row is
+// resolved per wave (its source and destination found), then all 256 threads stream the rows'
+// 16-byte chunks, U loads in flight per thread.  Launchers pick (RPB, U) from the row size:
+// one row per block with just enough loads per thread to cover it measured best on gfx950.
 
 // A resolved row: the source is src_a (its first split_src chunks) then src_b; the destination
 // dst_a (first split_dst chunks) then dst_b.  dst_a == 0 marks "no row".
@@ -114,17 +114,17 @@ struct RowDesc {
     uint64_t src_a, src_b, dst_a, dst_b;
 };
 
-// Stream nrows resolved rows of n16 chunks each, flat over (row, chunk) so that every thread has
-// kStreamUnroll loads in flight regardless of the row size.
+// Stream nrows resolved rows of n16 chunks each, flat over (row, chunk).
+template <int U>
 __device__ __forceinline__ void block_stream_rows(const RowDesc* rows, int nrows, int n16,
                                                   int split_src, int split_dst) {
     const int total = nrows * n16;
     const float inv = 1.0f / (float)n16;
-    for (int k0 = threadIdx.x; k0 < total; k0 += blockDim.x * kStreamUnroll) {
-        u32x4 v[kStreamUnroll];
-        int rr[kStreamUnroll];
+    for (int k0 = threadIdx.x; k0 < total; k0 += blockDim.x * U) {
+        u32x4 v[U];
+        int rr[U];
 #pragma unroll
-        for (int u = 0; u < kStreamUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {
             const int k = k0 + u * blockDim.x;
             int r = (int)((float)k * inv);  // k / n16, corrected below (k < 2^24)
             if (r * n16 > k) --r;
@@ -138,7 +138,7 @@ __device__ __forceinline__ void block_stream_rows(const RowDesc* rows, int nrows
             }
         }
 #pragma unroll
-        for (int u = 0; u < kStreamUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {
             const int k = k0 + u * blockDim.x;
             const int r = rr[u];
             if (k < total && rows[r].dst_a) {
@@ -149,6 +149,48 @@ __device__ __forceinline__ void block_stream_rows(const RowDesc* rows, int nrows
             }
         }
     }
+}
+
+// (rows per block, loads per thread) for rows of n16 chunks: the fewest rows (1, 2 or 4) whose
+// chunks reach min_chunks -- enough bytes per block to hide the row-resolve latency -- and just
+// enough loads per thread for the block's 256 threads to cover them in one pass (at most 8).
+struct StreamShape {
+    int rpb, u;
+};
+inline StreamShape stream_shape(int n16, int min_chunks) {
+    int rpb = 1;
+    while (rpb < kWavesPerBlock && rpb * n16 < min_chunks) rpb *= 2;
+    const int per_thread = (rpb * n16 + kBlock - 1) / kBlock;
+    int u = 1;
+    while (u < per_thread && u < 8) u *= 2;
+    return {rpb, u};
+}
+
+// Minimum chunks per block, per kernel (a row-resolve costs 2-4 dependent memory round trips;
+// the unpack's, with its expert-base reduction, is the heaviest).
+#ifndef MOE_NET_MIN_CHUNKS
+#define MOE_NET_MIN_CHUNKS 1792
+#endif
+#ifndef MOE_UNPACK_MIN_CHUNKS
+#define MOE_UNPACK_MIN_CHUNKS 1792
+#endif
+#ifndef MOE_CPACK_MIN_CHUNKS
+#define MOE_CPACK_MIN_CHUNKS 896
+#endif
+#ifndef MOE_CNET_MIN_CHUNKS
+#define MOE_CNET_MIN_CHUNKS 896
+#endif
+
+// The (RPB, U) instances a launcher may pick.
+#define MOE_STREAM_SHAPES(X) \
+    X(1, 1) X(1, 2) X(1, 4) X(1, 8) X(2, 1) X(2, 2) X(2, 4) X(2, 8) X(4, 1) X(4, 2) X(4, 4) X(4, 8)
+inline StreamShape stream_shape(int n16) {
+    int rpb = 1;
+    while (rpb < kWavesPerBlock && (rpb * 2) * n16 <= kBlock) rpb *= 2;
+    const int per_thread = (rpb * n16 + kBlock - 1) / kBlock;
+    int u = 1;
+    while (u < per_thread && u < 8) u *= 2;
+    return {rpb, u};
 }
 
 // Global row bases over ranks, gb[d] = sum over d' < d of table[d' * stride + col], gb[N] = the

@@ -228,18 +228,19 @@ __device__ __forceinline__ int recv_offset(const int32_t* __restrict__ send_off,
     return wave_sum(v);
 }
 
-// kRowsPerBlock consecutive send rows (s, i) per block, one resolved per wave: its segment d is
+// RPB consecutive send rows (s, i) per block, one resolved per wave: its segment d is
 // found by a ballot over send_off[s] and it lands at recv_off[d][s] + (i - send_off[s][d]) in
 // rank d's receive buffer, metadata alongside; then the block streams the rows.  Blocks 0..N-1
 // also write row d = blockIdx of the recv_off output (a wave scan over sources).
+template <int RPB, int U>
 __global__ __launch_bounds__(kBlock) void k_net_dispatch(Dims D, const int32_t* __restrict__ send_off,
                                                          const uint8_t* __restrict__ send_buf,
                                                          const int32_t* __restrict__ send_meta,
                                                          uint8_t* __restrict__ recv_buf,
                                                          int32_t* __restrict__ recv_meta,
                                                          int32_t* __restrict__ recv_off) {
-    static_assert(kRowsPerBlock == kWavesPerBlock, "one row per wave");
-    __shared__ RowDesc rows[kRowsPerBlock];
+    static_assert(RPB <= kWavesPerBlock, "one row per wave");
+    __shared__ RowDesc rows[RPB];
     const int N = D.N;
     if (blockIdx.x < (unsigned)N && wave_id() == kWavesPerBlock - 1) {
         const int d = blockIdx.x;
@@ -253,9 +254,9 @@ __global__ __launch_bounds__(kBlock) void k_net_dispatch(Dims D, const int32_t* 
         }
         if (lane_id() == 0) recv_off[(long)d * (N + 1) + N] = carry;
     }
-    const long g = (long)blockIdx.x * kRowsPerBlock + wave_id();
+    const long g = (long)blockIdx.x * RPB + wave_id();
     RowDesc rd = {0, 0, 0, 0};
-    if (g < (long)N * D.TR) {
+    if (wave_id() < RPB && g < (long)N * D.TR) {
         const int s = (int)(g / D.TR);
         const int i = (int)(g - (long)s * D.TR);
         const int32_t* so = send_off + (long)s * (N + 1);
@@ -274,9 +275,9 @@ __global__ __launch_bounds__(kBlock) void k_net_dispatch(Dims D, const int32_t* 
             }
         }
     }
-    if (lane_id() == 0) rows[wave_id()] = rd;
+    if (wave_id() < RPB && lane_id() == 0) rows[wave_id()] = rd;
     __syncthreads();
-    block_stream_rows(rows, kRowsPerBlock, D.P16, D.P16, D.P16);
+    block_stream_rows<U>(rows, RPB, D.P16, D.P16, D.P16);
 }
 
 // ------------------------------------------------------------------ receive side
@@ -298,9 +299,10 @@ __device__ __forceinline__ long expert_base(const int32_t* __restrict__ counts, 
     return wave_sum(v);
 }
 
-// kRowsPerBlock received rows per block (a global index over all ranks), one resolved per wave:
+// RPB received rows per block (a global index over all ranks), one resolved per wave:
 // its expert-major position is expert_base(d, s, j) + the per-expert rank carried in its
 // metadata.  Blocks 0..N-1 also write rank d = blockIdx's expert_cnt and expert_off.
+template <int RPB, int U>
 __global__ __launch_bounds__(kBlock) void k_unpack(Dims D, const int32_t* __restrict__ counts,
                                                    const int32_t* __restrict__ recv_off,
                                                    const uint8_t* __restrict__ recv_buf,
@@ -312,7 +314,7 @@ __global__ __launch_bounds__(kBlock) void k_unpack(Dims D, const int32_t* __rest
                                                    int32_t* __restrict__ expert_src,
                                                    int32_t* __restrict__ expert_rpos) {
     extern __shared__ int gb[];  // [N + 1]
-    __shared__ RowDesc rows[kRowsPerBlock];
+    __shared__ RowDesc rows[RPB];
     const int N = D.N, L = D.L, E = D.E;
     rank_bases(recv_off, N + 1, N, N, gb);
     if (blockIdx.x < (unsigned)N && wave_id() == kWavesPerBlock - 1) {
@@ -335,9 +337,9 @@ __global__ __launch_bounds__(kBlock) void k_unpack(Dims D, const int32_t* __rest
         if (lane_id() == 0) expert_off[(long)d * (L + 1) + L] = carry;
     }
     __syncthreads();
-    const long G = (long)blockIdx.x * kRowsPerBlock + wave_id();
+    const long G = (long)blockIdx.x * RPB + wave_id();
     RowDesc rd = {0, 0, 0, 0};
-    if (G < gb[N]) {
+    if (wave_id() < RPB && G < gb[N]) {
         const int d = wave_count_le(gb + 1, N, G);  // ranks whose rows all lie before G
         const long r = G - gb[d];
         const int32_t* ro = recv_off + (long)d * (N + 1);
@@ -362,9 +364,9 @@ __global__ __launch_bounds__(kBlock) void k_unpack(Dims D, const int32_t* __rest
             set_status(D.status, MOE_EINVAL);
         }
     }
-    if (lane_id() == 0) rows[wave_id()] = rd;
+    if (wave_id() < RPB && lane_id() == 0) rows[wave_id()] = rd;
     __syncthreads();
-    block_stream_rows(rows, kRowsPerBlock, D.P16, D.P16, D.X16);
+    block_stream_rows<U>(rows, RPB, D.P16, D.P16, D.X16);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -409,9 +411,14 @@ hipError_t launch_net_dispatch(const Dims& D, const int32_t* send_off, const voi
                                const int32_t* send_meta, void* recv_buf, int32_t* recv_meta,
                                int32_t* recv_off, hipStream_t st) {
     const long rows = (long)D.N * D.TR;
-    const long blocks = std::max<long>((rows + kRowsPerBlock - 1) / kRowsPerBlock, D.N);
-    hipLaunchKernelGGL(k_net_dispatch, dim3(blocks), dim3(kBlock), 0, st, D, send_off,
-                       (const uint8_t*)send_buf, send_meta, (uint8_t*)recv_buf, recv_meta, recv_off);
+    const StreamShape sh = stream_shape(D.P16, MOE_NET_MIN_CHUNKS);
+    const long blocks = std::max<long>((rows + sh.rpb - 1) / sh.rpb, D.N);
+#define MOE_LAUNCH(R_, U_)                                                                         \
+    if (sh.rpb == R_ && sh.u == U_)                                                                \
+        hipLaunchKernelGGL((k_net_dispatch<R_, U_>), dim3(blocks), dim3(kBlock), 0, st, D, send_off, \
+                           (const uint8_t*)send_buf, send_meta, (uint8_t*)recv_buf, recv_meta, recv_off);
+    MOE_STREAM_SHAPES(MOE_LAUNCH)
+#undef MOE_LAUNCH
     return hipGetLastError();
 }
 
@@ -423,10 +430,15 @@ hipError_t launch_dispatch_recv(const Dims& D, const int32_t* counts, const int3
                                 int32_t* expert_src, int32_t* expert_rpos, void* /*workspace*/,
                                 hipStream_t st) {
     const long rows = (long)D.N * D.TR;  // every received row, over all ranks, is one of these
-    const long blocks = std::max<long>((rows + kRowsPerBlock - 1) / kRowsPerBlock, D.N);
-    hipLaunchKernelGGL(k_unpack, dim3(blocks), dim3(kBlock), (D.N + 1) * 4, st, D, counts, recv_off,
-                       (const uint8_t*)recv_buf, recv_meta, (uint8_t*)expert_x, expert_scale, expert_cnt,
-                       expert_off, expert_src, expert_rpos);
+    const StreamShape sh = stream_shape(D.P16, MOE_UNPACK_MIN_CHUNKS);
+    const long blocks = std::max<long>((rows + sh.rpb - 1) / sh.rpb, D.N);
+#define MOE_LAUNCH(R_, U_)                                                                          \
+    if (sh.rpb == R_ && sh.u == U_)                                                                 \
+        hipLaunchKernelGGL((k_unpack<R_, U_>), dim3(blocks), dim3(kBlock), (D.N + 1) * 4, st, D, counts, \
+                           recv_off, (const uint8_t*)recv_buf, recv_meta, (uint8_t*)expert_x,       \
+                           expert_scale, expert_cnt, expert_off, expert_src, expert_rpos);
+    MOE_STREAM_SHAPES(MOE_LAUNCH)
+#undef MOE_LAUNCH
     return hipGetLastError();
 }
 
