@@ -245,6 +245,103 @@ def copy_calibration(nbytes=1 << 30, reps=10) -> dict:
             "gbs": round(2 * nbytes / (us * 1e-6) / 1e9, 1)}
 
 
+def overlap_leg(name, steps=10, warmup=2, inter=2048) -> dict:
+    """Send/receive split in use: a stand-in shared expert (one MLP, hidden H -> inter -> H, bf16
+    GEMMs through torch) runs on a second stream while (a) the dispatch transfer (network
+    stand-in + receive) and (b) the combine send half run on the first.  Reports serial and
+    overlapped time and the part of the shared expert hidden behind the transfer."""
+    import numpy as np
+    import torch
+    import torch.nn.functional as F
+
+    import combine_moe_route_top_amd as moe
+    import moe_synth as ms
+
+    c = ms.CONFIGS[name]
+    assert not c.fp8, "the overlap leg runs on a bf16 workload"
+    inp = ms.config_inputs(c)
+    b = moe.alloc_buffers(c.N, c.T, c.H, c.E, c.R, c.fp8)
+    b.logits.copy_(torch.from_numpy(inp["logits"]))
+    use_bias = inp["bias"] is not None
+    if use_bias:
+        b.bias.copy_(torch.from_numpy(inp["bias"]))
+    b.x.copy_(torch.from_numpy(inp["x"].view(np.int16)))
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    wg = (torch.randn(c.H, inter, device="cuda", generator=gen) * c.H ** -0.5).to(torch.bfloat16)
+    wu = (torch.randn(c.H, inter, device="cuda", generator=gen) * c.H ** -0.5).to(torch.bfloat16)
+    wd = (torch.randn(inter, c.H, device="cuda", generator=gen) * inter ** -0.5).to(torch.bfloat16)
+    xs = b.x.view(torch.bfloat16).view(c.N * c.T, c.H)
+    ys = torch.empty_like(xs)
+    s1 = torch.cuda.current_stream()
+    s2 = torch.cuda.Stream()   # default priority
+    sh = b.shape
+
+    def shared(st):
+        with torch.cuda.stream(st):
+            torch.matmul(F.silu(xs @ wg) * (xs @ wu), wd, out=ys)
+
+    def d_send():
+        moe.moe_route(sh, b.logits, b.bias if use_bias else None, b.topk_idx, b.topk_w, s1)
+        moe.moe_dispatch_send(sh, b.x, b.x_scale, b.topk_idx, b.counts, b.send_off, b.send_pos,
+                              b.send_buf, b.send_meta, b.workspace, s1)
+
+    def d_transfer():
+        moe.moe_net_dispatch(sh, b.send_off, b.send_buf, b.send_meta, b.recv_buf, b.recv_meta,
+                             b.recv_off, s1)
+        moe.moe_dispatch_recv(sh, b.counts, b.recv_off, b.recv_buf, b.recv_meta, b.expert_x,
+                              b.expert_scale, b.expert_cnt, b.expert_off, b.expert_src,
+                              b.expert_rpos, b.workspace, s1)
+
+    def c_send():
+        moe.moe_combine_send(sh, b.expert_x, b.expert_rpos, b.recv_off, b.send_off, b.cs_buf,
+                             b.cr_buf, s1)
+
+    def c_recv():
+        moe.moe_combine_recv(sh, b.cr_buf, b.send_pos, b.topk_w, b.out, s1)
+
+    def fork_join(first, second):
+        """first() on s1, then the shared expert on s2 concurrently with second() on s1."""
+        first()
+        ev = torch.cuda.Event()
+        ev.record(s1)
+        s2.wait_event(ev)
+        shared(s2)
+        second()
+        s1.wait_stream(s2)
+
+    variants = {
+        "shared_alone": lambda: shared(s1),
+        "dispatch_alone": lambda: (d_send(), d_transfer()),
+        "dispatch_then_shared": lambda: (d_send(), d_transfer(), shared(s1)),
+        "dispatch_overlap": lambda: fork_join(d_send, d_transfer),
+        "combine_alone": lambda: (c_send(), c_recv()),
+        "combine_then_shared": lambda: (c_send(), shared(s1), c_recv()),
+        "combine_overlap": lambda: (fork_join(c_send, lambda: None), c_recv()),
+    }
+    us = {}
+    for k, fn in variants.items():
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s1)
+        for _ in range(steps):
+            fn()
+        e1.record(s1)
+        torch.cuda.synchronize()
+        us[k] = round(e0.elapsed_time(e1) * 1e3 / steps, 2)
+    res = {"workload": name, "shared_expert": f"bf16 MLP {c.H}->{inter}->{c.H} on {c.N * c.T} tokens "
+                                               f"(torch GEMMs on a second stream)", "us": us}
+    for ph in ("dispatch", "combine"):
+        serial = us[f"{ph}_then_shared"]
+        hidden = serial - us[f"{ph}_overlap"]
+        res[f"{ph}_hidden_us"] = round(hidden, 2)
+        res[f"{ph}_hidden_frac_of_shared"] = round(hidden / us["shared_alone"], 3)
+    del b
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -256,6 +353,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--no-copy-calibration", action="store_true")
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="skip the send/receive-split overlap leg")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the N expert-parallel ranks are simulated inside one "
@@ -303,6 +402,8 @@ def main():
         "roofline": dominant_kernel(head),
         "other_workloads": extras,
     }
+    if not args.no_overlap:
+        line["overlap"] = overlap_leg(HEADLINE)
     if calib is not None:
         line["plain_copy"] = calib
         line["frac_of_plain_copy"] = round(head["gbs"] / calib["gbs"], 4)

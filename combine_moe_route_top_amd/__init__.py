@@ -58,6 +58,8 @@ _SIGS = {
     "moe_net_dispatch": [ctypes.POINTER(moe_shape)] + [_vp] * 7,
     "moe_dispatch_recv": [ctypes.POINTER(moe_shape)] + [_vp] * 12,
     "moe_combine": [ctypes.POINTER(moe_shape)] + [_vp] * 10,
+    "moe_combine_send": [ctypes.POINTER(moe_shape)] + [_vp] * 7,
+    "moe_combine_recv": [ctypes.POINTER(moe_shape)] + [_vp] * 5,
     "moe_expert_stub": [ctypes.POINTER(moe_shape), ctypes.c_int32] + [_vp] * 5,
     "moe_strerror": [ctypes.c_int],
     "moe_abi_version": [],
@@ -150,6 +152,19 @@ def moe_combine(shape, expert_y, expert_rpos, recv_off, send_off, send_pos, topk
     _check("moe_combine", _lib.moe_combine(
         ctypes.byref(shape), _ptr(expert_y), _ptr(expert_rpos), _ptr(recv_off), _ptr(send_off),
         _ptr(send_pos), _ptr(topk_w), _ptr(cs_buf), _ptr(cr_buf), _ptr(out), _stream(stream)))
+
+
+def moe_combine_send(shape, expert_y, expert_rpos, recv_off, send_off, cs_buf, cr_buf,
+                     stream=None):
+    _check("moe_combine_send", _lib.moe_combine_send(
+        ctypes.byref(shape), _ptr(expert_y), _ptr(expert_rpos), _ptr(recv_off), _ptr(send_off),
+        _ptr(cs_buf), _ptr(cr_buf), _stream(stream)))
+
+
+def moe_combine_recv(shape, cr_buf, send_pos, topk_w, out, stream=None):
+    _check("moe_combine_recv", _lib.moe_combine_recv(
+        ctypes.byref(shape), _ptr(cr_buf), _ptr(send_pos), _ptr(topk_w), _ptr(out),
+        _stream(stream)))
 
 
 def moe_expert_stub(shape, mode, expert_x, expert_scale, expert_off, expert_y, stream=None):

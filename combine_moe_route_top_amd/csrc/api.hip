@@ -19,9 +19,10 @@ hipError_t launch_dispatch_recv(const Dims&, const int32_t*, const int32_t*, con
                                 int32_t*, void*, hipStream_t);
 hipError_t launch_expert_stub(const Dims&, int, const void*, const float*, const int32_t*,
                               uint16_t*, hipStream_t);
-hipError_t launch_combine(const Dims&, const uint16_t*, const int32_t*, const int32_t*,
-                          const int32_t*, const int32_t*, const float*, uint16_t*, uint16_t*,
-                          uint16_t*, hipStream_t);
+hipError_t launch_combine_send(const Dims&, const uint16_t*, const int32_t*, const int32_t*,
+                               const int32_t*, uint16_t*, uint16_t*, hipStream_t);
+hipError_t launch_combine_recv(const Dims&, const uint16_t*, const int32_t*, const float*, uint16_t*,
+                               hipStream_t);
 }  // namespace moe
 
 using moe::Dims;
@@ -187,18 +188,44 @@ int moe_dispatch_recv(const moe_shape* shape, const int32_t* counts, const int32
                                                 expert_rpos, workspace, (hipStream_t)stream));
 }
 
+int moe_combine_send(const moe_shape* shape, const uint16_t* expert_y, const int32_t* expert_rpos,
+                     const int32_t* recv_off, const int32_t* send_off, uint16_t* cs_buf,
+                     uint16_t* cr_buf, void* stream) {
+    Dims D;
+    int rc = make_dims(shape, &D);
+    if (rc) return rc;
+    if (!aligned(expert_y, 16) || !aligned(expert_rpos, 4) || !aligned(recv_off, 4) ||
+        !aligned(send_off, 4) || !aligned(cs_buf, 16) || !aligned(cr_buf, 16))
+        return MOE_EINVAL;
+    return hip_status(moe::launch_combine_send(D, expert_y, expert_rpos, recv_off, send_off, cs_buf,
+                                               cr_buf, (hipStream_t)stream));
+}
+
+int moe_combine_recv(const moe_shape* shape, const uint16_t* cr_buf, const int32_t* send_pos,
+                     const float* topk_w, uint16_t* out, void* stream) {
+    Dims D;
+    int rc = make_dims(shape, &D);
+    if (rc) return rc;
+    if (!aligned(cr_buf, 16) || !aligned(send_pos, 4) || !aligned(topk_w, 4) || !aligned(out, 16))
+        return MOE_EINVAL;
+    return hip_status(moe::launch_combine_recv(D, cr_buf, send_pos, topk_w, out, (hipStream_t)stream));
+}
+
 int moe_combine(const moe_shape* shape, const uint16_t* expert_y, const int32_t* expert_rpos,
                 const int32_t* recv_off, const int32_t* send_off, const int32_t* send_pos,
                 const float* topk_w, uint16_t* cs_buf, uint16_t* cr_buf, uint16_t* out, void* stream) {
     Dims D;
     int rc = make_dims(shape, &D);
     if (rc) return rc;
+    // validate both halves before launching either
     if (!aligned(expert_y, 16) || !aligned(expert_rpos, 4) || !aligned(recv_off, 4) ||
         !aligned(send_off, 4) || !aligned(send_pos, 4) || !aligned(topk_w, 4) ||
         !aligned(cs_buf, 16) || !aligned(cr_buf, 16) || !aligned(out, 16))
         return MOE_EINVAL;
-    return hip_status(moe::launch_combine(D, expert_y, expert_rpos, recv_off, send_off, send_pos,
-                                          topk_w, cs_buf, cr_buf, out, (hipStream_t)stream));
+    rc = hip_status(moe::launch_combine_send(D, expert_y, expert_rpos, recv_off, send_off, cs_buf,
+                                             cr_buf, (hipStream_t)stream));
+    if (rc) return rc;
+    return hip_status(moe::launch_combine_recv(D, cr_buf, send_pos, topk_w, out, (hipStream_t)stream));
 }
 
 int moe_expert_stub(const moe_shape* shape, int32_t mode, const void* expert_x,

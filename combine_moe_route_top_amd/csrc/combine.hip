@@ -230,10 +230,9 @@ hipError_t launch_expert_stub(const Dims& D, int mode, const void* expert_x, con
     return hipGetLastError();
 }
 
-hipError_t launch_combine(const Dims& D, const uint16_t* expert_y, const int32_t* expert_rpos,
-                          const int32_t* recv_off, const int32_t* send_off, const int32_t* send_pos,
-                          const float* topk_w, uint16_t* cs_buf, uint16_t* cr_buf, uint16_t* out,
-                          hipStream_t st) {
+hipError_t launch_combine_send(const Dims& D, const uint16_t* expert_y, const int32_t* expert_rpos,
+                               const int32_t* recv_off, const int32_t* send_off, uint16_t* cs_buf,
+                               uint16_t* cr_buf, hipStream_t st) {
     const long rows = (long)D.N * D.TR;  // every received row, over all ranks, is one of these
     const StreamShape sp = stream_shape(D.Y16, MOE_CPACK_MIN_CHUNKS);
     const StreamShape sn = stream_shape(D.Y16, MOE_CNET_MIN_CHUNKS);
@@ -249,9 +248,14 @@ hipError_t launch_combine(const Dims& D, const uint16_t* expert_y, const int32_t
                            (D.N + 1) * 4, st, D, (const uint16_t*)cs_buf, recv_off, send_off, cr_buf);
     MOE_STREAM_SHAPES(MOE_LAUNCH)
 #undef MOE_LAUNCH
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_recv(const Dims& D, const uint16_t* cr_buf, const int32_t* send_pos,
+                               const float* topk_w, uint16_t* out, hipStream_t st) {
     const long waves = (long)D.N * D.T * kWsumWaves;
     hipLaunchKernelGGL(k_wsum, dim3((waves + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock), 0, st, D,
-                       (const uint16_t*)cr_buf, send_pos, topk_w, out);
+                       cr_buf, send_pos, topk_w, out);
     return hipGetLastError();
 }
 

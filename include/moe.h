@@ -156,7 +156,22 @@ int moe_dispatch_recv(const moe_shape* shape, const int32_t* counts, const int32
 int moe_combine(const moe_shape* shape, const uint16_t* expert_y, const int32_t* expert_rpos,
                 const int32_t* recv_off, const int32_t* send_off, const int32_t* send_pos,
                 const float* topk_w, uint16_t* cs_buf, uint16_t* cr_buf, uint16_t* out,
-                void* stream);
+                void* stream);  /* = moe_combine_send then moe_combine_recv */
+
+/* Combine, send half: the shuffle and the network back (the first two steps of moe_combine).
+ * [PORT] Portable kernels: send halves only issue writes, so other work (the shared expert,
+ * attention) can run while the transfer is in flight; [EFA] combine paragraphs.
+ *   expert_y, expert_rpos, recv_off, send_off, cs_buf, cr_buf   as for moe_combine */
+int moe_combine_send(const moe_shape* shape, const uint16_t* expert_y, const int32_t* expert_rpos,
+                     const int32_t* recv_off, const int32_t* send_off, uint16_t* cs_buf,
+                     uint16_t* cr_buf, void* stream);
+
+/* Combine, receive half: the router-weighted sum from the combine receive buffer (the last step
+ * of moe_combine).  [PORT] Combine: the receiver computes the weighted average of all expert
+ * contributions into an externally allocated tensor.
+ *   cr_buf, send_pos, topk_w, out   as for moe_combine */
+int moe_combine_recv(const moe_shape* shape, const uint16_t* cr_buf, const int32_t* send_pos,
+                     const float* topk_w, uint16_t* out, void* stream);
 
 /* Stand-in for the grouped GEMM between dispatch and combine (not part of dispatch/combine;
  * [EFA] overview: the grouped GEMM multiplies tokens by expert weights in between).

@@ -35,7 +35,7 @@ def upload_inputs(b, inp):
 
 
 def gpu_run(N, T, H, E, R, fp8, inp, expert_mode=0, capacity=0, y=None, topk_idx=None,
-            poison=True):
+            poison=True, split_combine=False):
     """The whole path on the GPU.  Returns (buffers, host copies of every valid output)."""
     import combine_moe_route_top_amd as moe
     b = moe.alloc_buffers(N, T, H, E, R, fp8, capacity)
@@ -63,7 +63,17 @@ def gpu_run(N, T, H, E, R, fp8, inp, expert_mode=0, capacity=0, y=None, topk_idx
                             b.expert_y)
     else:
         b.expert_y.copy_(torch.from_numpy(y.view(np.int16)))
-    moe.run_combine(b)
+    if split_combine:  # the two halves, with a second stream between them
+        moe.moe_combine_send(b.shape, b.expert_y, b.expert_rpos, b.recv_off, b.send_off, b.cs_buf,
+                             b.cr_buf)
+        ev = torch.cuda.Event()
+        ev.record()
+        side = torch.cuda.Stream()
+        side.wait_event(ev)
+        moe.moe_combine_recv(b.shape, b.cr_buf, b.send_pos, b.topk_w, b.out, side)
+        torch.cuda.current_stream().wait_stream(side)
+    else:
+        moe.run_combine(b)
     torch.cuda.synchronize()
     return b, fetch(b, N, T, R)
 

@@ -15,7 +15,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def test_exports_every_declared_symbol():
     names = moe.header_functions()
     assert {"moe_route", "moe_dispatch_send", "moe_net_dispatch", "moe_dispatch_recv",
-            "moe_combine", "moe_sizes", "moe_strerror"} <= set(names)
+            "moe_combine", "moe_combine_send", "moe_combine_recv", "moe_sizes",
+            "moe_strerror"} <= set(names)
     for n in names:
         assert hasattr(moe._lib, n), n
     # and they are exported C symbols of libmoe.so (nm -D), not C++-mangled
@@ -88,6 +89,10 @@ def test_null_and_misaligned_pointers_rejected_before_launch():
                                       None, stream=0),
         lambda: moe.moe_combine(sh, good, good, good, good, good, good, good, good, bad, stream=0),
         lambda: moe.moe_expert_stub(sh, 2, good, None, good, good, stream=0),
+        lambda: moe.moe_combine_send(sh, good, good, good, good, bad, good, stream=0),
+        lambda: moe.moe_combine_send(sh, good, None, good, good, good, good, stream=0),
+        lambda: moe.moe_combine_recv(sh, good, good, good, bad, stream=0),
+        lambda: moe.moe_combine_recv(sh, good, good, None, good, stream=0),
     ]
     for fn in cases:
         with pytest.raises(moe.MoeError) as ex:

@@ -80,6 +80,56 @@ def test_random_expert_outputs(case):
     parity.compare(g, o, N, T, H, E, R, fp8, check_stub=False, check_ulp=False)
 
 
+@pytest.mark.parametrize("case", [SMALL[0], SMALL[2], SMALL[3]], ids=lambda c: _case_id(c))
+def test_split_combine(case):
+    # moe_combine_send then moe_combine_recv (on another stream) == moe_combine == the oracle
+    N, T, H, E, R, fp8, bias = case
+    print(f"\ncase split-combine {_case_id(case)}", flush=True)
+    inp = ms.make_inputs(N, T, H, E, R, fp8, bias, 6)
+    _, g = parity.gpu_run(N, T, H, E, R, fp8, inp, split_combine=True)
+    _, f = parity.gpu_run(N, T, H, E, R, fp8, inp)
+    assert np.array_equal(g["out"], f["out"])
+    o = parity.oracle_run(N, T, H, E, R, fp8, inp)
+    parity.compare(g, o, N, T, H, E, R, fp8)
+
+
+def test_overlap_with_second_stream():
+    # dispatch send on stream 1; GEMMs on stream 2 while the transfer and receive run on
+    # stream 1; then combine: every output still matches the oracle
+    import combine_moe_route_top_amd as moe
+    N, T, H, E, R = 8, 129, 1024, 64, 8
+    print("\ncase overlap", flush=True)
+    inp = ms.make_inputs(N, T, H, E, R, False, "zipf", 1)
+    b = moe.alloc_buffers(N, T, H, E, R)
+    parity.upload_inputs(b, inp)
+    s1 = torch.cuda.current_stream()
+    s2 = torch.cuda.Stream()
+    a = torch.randn(2048, 2048, device="cuda", dtype=torch.bfloat16)
+    moe.moe_route(b.shape, b.logits, b.bias, b.topk_idx, b.topk_w, s1)
+    moe.moe_dispatch_send(b.shape, b.x, None, b.topk_idx, b.counts, b.send_off, b.send_pos,
+                          b.send_buf, b.send_meta, b.workspace, s1)
+    ev = torch.cuda.Event()
+    ev.record(s1)
+    s2.wait_event(ev)
+    with torch.cuda.stream(s2):
+        for _ in range(4):
+            a = (a @ a) * 0.01
+    moe.moe_net_dispatch(b.shape, b.send_off, b.send_buf, b.send_meta, b.recv_buf, b.recv_meta,
+                         b.recv_off, s1)
+    moe.moe_dispatch_recv(b.shape, b.counts, b.recv_off, b.recv_buf, b.recv_meta, b.expert_x,
+                          None, b.expert_cnt, b.expert_off, b.expert_src, b.expert_rpos,
+                          b.workspace, s1)
+    moe.moe_expert_stub(b.shape, 0, b.expert_x, None, b.expert_off, b.expert_y, s1)
+    moe.moe_combine_send(b.shape, b.expert_y, b.expert_rpos, b.recv_off, b.send_off, b.cs_buf,
+                         b.cr_buf, s1)
+    s1.wait_stream(s2)
+    moe.moe_combine_recv(b.shape, b.cr_buf, b.send_pos, b.topk_w, b.out, s1)
+    torch.cuda.synchronize()
+    g = parity.fetch(b, N, T, R)
+    o = parity.oracle_run(N, T, H, E, R, False, inp)
+    parity.compare(g, o, N, T, H, E, R, False)
+
+
 def test_tight_capacity():
     # receive buffers sized to the tight bound N*T*min(R, E/N) instead of N*T*max(R, E/N)
     N, T, H, E, R = 4, 40, 64, 32, 8
