@@ -363,6 +363,77 @@ def overlap_leg(name, steps=10, warmup=2, inter=2048) -> dict:
     return res
 
 
+def rank_leg(name, steps=20, warmup=3) -> dict:
+    """One rank's share at its real shape: every call restricted to a single rank (as each GPU of
+    an expert-parallel deployment runs it), timed with HIP events, for the rank that receives the
+    most rows and for the median rank (by rows received).  The other ranks' data are in place
+    from a full step first; the network time between GPUs is not part of this."""
+    import numpy as np
+    import torch
+
+    import combine_moe_route_top_amd as moe
+    import moe_synth as ms
+
+    c = ms.CONFIGS[name]
+    inp = ms.config_inputs(c)
+    b = moe.alloc_buffers(c.N, c.T, c.H, c.E, c.R, c.fp8)
+    b.logits.copy_(torch.from_numpy(inp["logits"]))
+    use_bias = inp["bias"] is not None
+    if use_bias:
+        b.bias.copy_(torch.from_numpy(inp["bias"]))
+    x = inp["x"]
+    b.x.copy_(torch.from_numpy(x.view(np.int16) if x.dtype == np.uint16 else x))
+    if c.fp8:
+        b.x_scale.copy_(torch.from_numpy(inp["x_scale"]))
+    st = torch.cuda.current_stream()
+    moe.run_dispatch(b, bias=use_bias)
+    moe.moe_expert_stub(b.shape, 0, b.expert_x, b.expert_scale, b.expert_off, b.expert_y)
+    y = b.expert_y
+    moe.run_combine(b, y)
+    torch.cuda.synchronize()
+    recv = b.recv_off[:, c.N].cpu().numpy()
+    order = np.argsort(recv, kind="stable")
+    picks = {"max_rank": int(order[-1]), "median_rank": int(order[len(order) // 2])}
+    calls = ["route", "dispatch_send", "net_dispatch", "dispatch_recv", "combine_send", "combine_recv"]
+    out = {"workload": name, "rows_received": {}}
+    for label, r in picks.items():
+        sh = moe.for_ranks(b.shape, r, 1)
+        fns = [
+            lambda: moe.moe_route(sh, b.logits, b.bias if use_bias else None, b.topk_idx, b.topk_w, st),
+            lambda: moe.moe_dispatch_send(sh, b.x, b.x_scale, b.topk_idx, b.counts, b.send_off,
+                                          b.send_pos, b.send_buf, b.send_meta, b.workspace, st),
+            lambda: moe.moe_net_dispatch(sh, b.send_off, b.send_buf, b.send_meta, b.recv_buf,
+                                         b.recv_meta, b.recv_off, st),
+            lambda: moe.moe_dispatch_recv(sh, b.counts, b.recv_off, b.recv_buf, b.recv_meta,
+                                          b.expert_x, b.expert_scale, b.expert_cnt, b.expert_off,
+                                          b.expert_src, b.expert_rpos, b.workspace, st),
+            lambda: moe.moe_combine_send(sh, y, b.expert_rpos, b.recv_off, b.send_off, b.cs_buf,
+                                         b.cr_buf, st),
+            lambda: moe.moe_combine_recv(sh, b.cr_buf, b.send_pos, b.topk_w, b.out, st),
+        ]
+        for _ in range(warmup):
+            for f in fns:
+                f()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(steps)]
+        for k in range(steps):
+            for i, f in enumerate(fns):
+                evs[k][i].record(st)
+                f()
+            evs[k][len(fns)].record(st)
+        torch.cuda.synchronize()
+        per = {n: round(sum(evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(steps)) * 1e3 / steps, 2)
+               for i, n in enumerate(calls)}
+        out[label] = {"rank": r, "rows_received": int(recv[r]), "us_per_layer": round(sum(per.values()), 2),
+                      "per_call_us": per}
+    status = int(b.status.item())
+    if status != 0:
+        raise RuntimeError(f"device status word {status}")
+    del b
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -376,6 +447,8 @@ def main():
     ap.add_argument("--no-copy-calibration", action="store_true")
     ap.add_argument("--no-overlap", action="store_true",
                     help="skip the send/receive-split overlap leg")
+    ap.add_argument("--no-rank-leg", action="store_true",
+                    help="skip the one-rank-share timing leg")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the N expert-parallel ranks are simulated inside one "
@@ -426,6 +499,8 @@ def main():
     }
     if not args.no_overlap:
         line["overlap"] = overlap_leg(HEADLINE)
+    if not args.no_rank_leg:
+        line["one_rank_share"] = [rank_leg(w) for w in (HEADLINE, "kimi_k2_worst")]
     if calib is not None:
         line["plain_copy"] = calib
         line["frac_of_plain_copy"] = round(head["gbs"] / calib["gbs"], 4)

@@ -37,6 +37,7 @@ MOE_BF16, MOE_FP8_E4M3 = 0, 1
 class moe_shape(ctypes.Structure):
     _fields_ = [("N", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
                 ("E", ctypes.c_int32), ("R", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("rank_begin", ctypes.c_int32), ("rank_count", ctypes.c_int32),
                 ("capacity", ctypes.c_int64), ("status", ctypes.c_void_p)]
 
 
@@ -109,8 +110,16 @@ def _check(name, rc):
         raise MoeError(name, rc)
 
 
-def make_shape(N, T, H, E, R, fp8=False, capacity=0, status=None) -> moe_shape:
-    return moe_shape(N, T, H, E, R, MOE_FP8_E4M3 if fp8 else MOE_BF16, capacity, _ptr(status))
+def make_shape(N, T, H, E, R, fp8=False, capacity=0, status=None, rank_begin=0,
+               rank_count=0) -> moe_shape:
+    return moe_shape(N, T, H, E, R, MOE_FP8_E4M3 if fp8 else MOE_BF16, rank_begin, rank_count,
+                     capacity, _ptr(status))
+
+
+def for_ranks(shape: moe_shape, rank_begin: int, rank_count: int) -> moe_shape:
+    """The same shape restricted to ranks [rank_begin, rank_begin + rank_count)."""
+    return moe_shape(shape.N, shape.T, shape.H, shape.E, shape.R, shape.dtype, rank_begin,
+                     rank_count, shape.capacity, shape.status)
 
 
 def moe_sizes(shape: moe_shape) -> dict:

@@ -67,6 +67,11 @@ int make_dims(const moe_shape* sh, Dims* D) {
     D->X16 = fp8 ? (int)(H / 16) : (int)(2 * H / 16);
     D->nsc = (int)(H / 128);
     D->Y16 = (int)(2 * H / 16);
+    if (sh->rank_begin < 0 || sh->rank_count < 0) return MOE_EINVAL;
+    if (sh->rank_count == 0 && sh->rank_begin != 0) return MOE_EINVAL;
+    if ((long long)sh->rank_begin + sh->rank_count > N) return MOE_EINVAL;
+    D->rb = sh->rank_begin;
+    D->rc = sh->rank_count == 0 ? (int)N : sh->rank_count;
     D->status = sh->status;
     return MOE_OK;
 }

@@ -43,13 +43,14 @@ __global__ __launch_bounds__(kBlock) void k_expert_stub(Dims D, int mode, const 
                                                         const int32_t* __restrict__ expert_off,
                                                         uint16_t* __restrict__ expert_y) {
     extern __shared__ int gb[];
-    const int N = D.N, L = D.L;
-    rank_bases(expert_off, L + 1, L, N, gb);
+    const int L = D.L;
+    rank_bases(expert_off + (long)D.rb * (L + 1), L + 1, L, D.rc, gb);
     __syncthreads();
     const long G = (long)blockIdx.x * kWavesPerBlock + wave_id();
-    if (G >= gb[N]) return;
-    const int d = wave_count_le(gb + 1, N, G);
-    const long q = G - gb[d];
+    if (G >= gb[D.rc]) return;
+    const int dl = wave_count_le(gb + 1, D.rc, G);
+    const int d = D.rb + dl;
+    const long q = G - gb[dl];
     const int j = wave_count_le(expert_off + (long)d * (L + 1) + 1, L, q);
     const int e = d * L + j;
     const double tag = mode == 1 ? (double)(64 + e % 64) / 64.0 : 1.0;
@@ -96,13 +97,14 @@ __global__ __launch_bounds__(kBlock) void k_combine_pack(Dims D, const uint16_t*
     extern __shared__ int gb[];
     __shared__ RowDesc rows[RPB];
     const int N = D.N;
-    rank_bases(recv_off, N + 1, N, N, gb);
+    rank_bases(recv_off + (long)D.rb * (N + 1), N + 1, N, D.rc, gb);
     __syncthreads();
     const long G = (long)blockIdx.x * RPB + wave_id();
     RowDesc rd = {0, 0, 0, 0};
-    if (wave_id() < RPB && G < gb[N]) {
-        const int d = wave_count_le(gb + 1, N, G);
-        const long q = G - gb[d];
+    if (wave_id() < RPB && G < gb[D.rc]) {
+        const int dl = wave_count_le(gb + 1, D.rc, G);
+        const int d = D.rb + dl;
+        const long q = G - gb[dl];
         const long r = expert_rpos[(size_t)d * D.B + q];
         if (r >= 0 && r < D.B) {
             rd.src_a = rd.src_b = (uint64_t)(expert_y + ((size_t)d * D.B + q) * D.H);
@@ -116,9 +118,9 @@ __global__ __launch_bounds__(kBlock) void k_combine_pack(Dims D, const uint16_t*
     block_stream_rows<U>(rows, RPB, D.Y16, D.Y16, D.Y16);
 }
 
-// Network back: rank d's combine send buffer is read in order (a global index over all ranks);
-// row r of segment (s -> d) lands at send_off[s][d] + (r - recv_off[d][s]) in rank s's combine
-// receive buffer, where s's dispatch send buffer had it.
+// Network back: the call's ranks d push their combine send buffers, read in order (a global
+// index over those ranks); row r of segment (s -> d) lands at send_off[s][d] + (r - recv_off[d][s])
+// in rank s's combine receive buffer, where s's dispatch send buffer had it.
 template <int RPB, int U>
 __global__ __launch_bounds__(kBlock) void k_combine_net(Dims D, const uint16_t* __restrict__ cs_buf,
                                                         const int32_t* __restrict__ recv_off,
@@ -127,13 +129,14 @@ __global__ __launch_bounds__(kBlock) void k_combine_net(Dims D, const uint16_t* 
     extern __shared__ int gb[];
     __shared__ RowDesc rows[RPB];
     const int N = D.N;
-    rank_bases(recv_off, N + 1, N, N, gb);
+    rank_bases(recv_off + (long)D.rb * (N + 1), N + 1, N, D.rc, gb);
     __syncthreads();
     const long G = (long)blockIdx.x * RPB + wave_id();
     RowDesc rd = {0, 0, 0, 0};
-    if (wave_id() < RPB && G < gb[N]) {
-        const int d = wave_count_le(gb + 1, N, G);
-        const long r = G - gb[d];
+    if (wave_id() < RPB && G < gb[D.rc]) {
+        const int dl = wave_count_le(gb + 1, D.rc, G);
+        const int d = D.rb + dl;
+        const long r = G - gb[dl];
         const int32_t* ro = recv_off + (long)d * (N + 1);
         const int s = wave_count_le(ro, N, r) - 1;
         const long i = s >= 0 ? send_off[(long)s * (N + 1) + d] + (r - ro[s]) : -1;
@@ -160,9 +163,9 @@ __global__ __launch_bounds__(kBlock) void k_wsum(Dims D, const uint16_t* __restr
                                                  const float* __restrict__ topk_w,
                                                  uint16_t* __restrict__ out) {
     constexpr int CU = 2;
-    const long tok = ((long)blockIdx.x * kWavesPerBlock + wave_id()) / kWsumWaves;
+    const long tok = ((long)blockIdx.x * kWavesPerBlock + wave_id()) / kWsumWaves;  // call's ranks
     const int part = wave_id() % kWsumWaves;
-    if (tok >= (long)D.N * D.T) return;
+    if (tok >= (long)D.rc * D.T) return;
     const int lane = lane_id();
     const int R = D.R;
     const long s = tok / D.T;
@@ -223,9 +226,9 @@ __global__ __launch_bounds__(kBlock) void k_wsum(Dims D, const uint16_t* __restr
 
 hipError_t launch_expert_stub(const Dims& D, int mode, const void* expert_x, const float* expert_scale,
                               const int32_t* expert_off, uint16_t* expert_y, hipStream_t st) {
-    const long rows = (long)D.N * D.TR;
+    const long rows = recv_rows_bound(D);
     hipLaunchKernelGGL(k_expert_stub, dim3((rows + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock),
-                       (D.N + 1) * 4, st, D, mode, (const uint8_t*)expert_x, expert_scale, expert_off,
+                       (D.rc + 1) * 4, st, D, mode, (const uint8_t*)expert_x, expert_scale, expert_off,
                        expert_y);
     return hipGetLastError();
 }
@@ -233,19 +236,19 @@ hipError_t launch_expert_stub(const Dims& D, int mode, const void* expert_x, con
 hipError_t launch_combine_send(const Dims& D, const uint16_t* expert_y, const int32_t* expert_rpos,
                                const int32_t* recv_off, const int32_t* send_off, uint16_t* cs_buf,
                                uint16_t* cr_buf, hipStream_t st) {
-    const long rows = (long)D.N * D.TR;  // every received row, over all ranks, is one of these
+    const long rows = recv_rows_bound(D);  // rows the call's ranks received
     const StreamShape sp = stream_shape(D.Y16, MOE_CPACK_MIN_CHUNKS);
     const StreamShape sn = stream_shape(D.Y16, MOE_CNET_MIN_CHUNKS);
 #define MOE_LAUNCH(R_, U_)                                                                          \
     if (sp.rpb == R_ && sp.u == U_)                                                                 \
         hipLaunchKernelGGL((k_combine_pack<R_, U_>), dim3((rows + R_ - 1) / R_), dim3(kBlock),       \
-                           (D.N + 1) * 4, st, D, expert_y, expert_rpos, recv_off, cs_buf);
+                           (D.rc + 1) * 4, st, D, expert_y, expert_rpos, recv_off, cs_buf);
     MOE_STREAM_SHAPES(MOE_LAUNCH)
 #undef MOE_LAUNCH
 #define MOE_LAUNCH(R_, U_)                                                                          \
     if (sn.rpb == R_ && sn.u == U_)                                                                 \
         hipLaunchKernelGGL((k_combine_net<R_, U_>), dim3((rows + R_ - 1) / R_), dim3(kBlock),        \
-                           (D.N + 1) * 4, st, D, (const uint16_t*)cs_buf, recv_off, send_off, cr_buf);
+                           (D.rc + 1) * 4, st, D, (const uint16_t*)cs_buf, recv_off, send_off, cr_buf);
     MOE_STREAM_SHAPES(MOE_LAUNCH)
 #undef MOE_LAUNCH
     return hipGetLastError();
@@ -253,7 +256,13 @@ hipError_t launch_combine_send(const Dims& D, const uint16_t* expert_y, const in
 
 hipError_t launch_combine_recv(const Dims& D, const uint16_t* cr_buf, const int32_t* send_pos,
                                const float* topk_w, uint16_t* out, hipStream_t st) {
-    const long waves = (long)D.N * D.T * kWsumWaves;
+    // the tokens of ranks [rb, rb + rc)
+    const long rb = D.rb;
+    cr_buf += rb * D.TR * D.H;
+    send_pos += rb * D.TR;
+    topk_w += rb * D.T * D.R;
+    out += rb * D.T * D.H;
+    const long waves = (long)D.rc * D.T * kWsumWaves;
     hipLaunchKernelGGL(k_wsum, dim3((waves + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock), 0, st, D,
                        cr_buf, send_pos, topk_w, out);
     return hipGetLastError();

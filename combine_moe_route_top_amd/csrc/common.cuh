@@ -24,6 +24,7 @@ struct Dims {
     int X16;           // payload part of a row in 16-byte chunks (2H/16 or H/16)
     int nsc;           // fp8 scales per token (H / 128)
     int Y16;           // a bf16 combine row in 16-byte chunks (2H / 16)
+    int rb, rc;        // ranks this call works for: [rb, rb + rc)
     int32_t* status;
 };
 
@@ -94,6 +95,16 @@ __device__ __forceinline__ int wave_sum(int v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
     return v;
+}
+
+// At most how many rows the call's ranks receive in total: every rank receives at most
+// N*T*min(R, L) rows (one per routed slot, distinct experts per token), and all ranks together
+// exactly the N*T*R routed rows.
+inline long recv_rows_bound(const Dims& D) {
+    const long per_rank = (long)D.N * D.T * (D.R < D.L ? D.R : D.L);
+    const long all = (long)D.N * D.TR;
+    const long b = (long)D.rc * per_rank;
+    return b < all ? b : all;
 }
 
 // ------------------------------------------------------------------ block row streaming

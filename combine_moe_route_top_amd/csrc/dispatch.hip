@@ -184,8 +184,8 @@ __global__ __launch_bounds__(kBlock) void k_send_pack(Dims D, const uint8_t* __r
                                                       const float* __restrict__ x_scale,
                                                       const int32_t* __restrict__ send_pos,
                                                       uint8_t* __restrict__ send_buf) {
-    const long tok = (long)blockIdx.x * kWavesPerBlock + wave_id();
-    if (tok >= (long)D.N * D.T) return;
+    const long tok = (long)blockIdx.x * kWavesPerBlock + wave_id();  // within the call's ranks
+    if (tok >= (long)D.rc * D.T) return;
     const int lane = lane_id();
     const long s = tok / D.T;
     const int R = D.R;
@@ -242,8 +242,8 @@ __global__ __launch_bounds__(kBlock) void k_net_dispatch(Dims D, const int32_t* 
     static_assert(RPB <= kWavesPerBlock, "one row per wave");
     __shared__ RowDesc rows[RPB];
     const int N = D.N;
-    if (blockIdx.x < (unsigned)N && wave_id() == kWavesPerBlock - 1) {
-        const int d = blockIdx.x;
+    if (blockIdx.x < (unsigned)D.rc && wave_id() == kWavesPerBlock - 1) {
+        const int d = D.rb + blockIdx.x;
         int carry = 0;
         for (int b = 0; b < N; b += kWave) {
             const int sp = b + lane_id();
@@ -254,11 +254,11 @@ __global__ __launch_bounds__(kBlock) void k_net_dispatch(Dims D, const int32_t* 
         }
         if (lane_id() == 0) recv_off[(long)d * (N + 1) + N] = carry;
     }
-    const long g = (long)blockIdx.x * RPB + wave_id();
+    const long g = (long)blockIdx.x * RPB + wave_id();  // a send row of the call's ranks
     RowDesc rd = {0, 0, 0, 0};
-    if (wave_id() < RPB && g < (long)N * D.TR) {
-        const int s = (int)(g / D.TR);
-        const int i = (int)(g - (long)s * D.TR);
+    if (wave_id() < RPB && g < (long)D.rc * D.TR) {
+        const int s = D.rb + (int)(g / D.TR);
+        const int i = (int)(g - (long)(s - D.rb) * D.TR);
         const int32_t* so = send_off + (long)s * (N + 1);
         if (i < so[N]) {  // dropped slots leave the tail of the send buffer unused
             const int d = wave_count_le(so, N, i) - 1;
@@ -301,7 +301,8 @@ __device__ __forceinline__ long expert_base(const int32_t* __restrict__ counts, 
 
 // RPB received rows per block (a global index over all ranks), one resolved per wave:
 // its expert-major position is expert_base(d, s, j) + the per-expert rank carried in its
-// metadata.  Blocks 0..N-1 also write rank d = blockIdx's expert_cnt and expert_off.
+// metadata.  The rows are those received by the call's ranks; block b < rank_count also writes
+// the expert_cnt and expert_off of rank rank_begin + b.
 template <int RPB, int U>
 __global__ __launch_bounds__(kBlock) void k_unpack(Dims D, const int32_t* __restrict__ counts,
                                                    const int32_t* __restrict__ recv_off,
@@ -313,12 +314,12 @@ __global__ __launch_bounds__(kBlock) void k_unpack(Dims D, const int32_t* __rest
                                                    int32_t* __restrict__ expert_off,
                                                    int32_t* __restrict__ expert_src,
                                                    int32_t* __restrict__ expert_rpos) {
-    extern __shared__ int gb[];  // [N + 1]
+    extern __shared__ int gb[];  // [rank_count + 1]
     __shared__ RowDesc rows[RPB];
     const int N = D.N, L = D.L, E = D.E;
-    rank_bases(recv_off, N + 1, N, N, gb);
-    if (blockIdx.x < (unsigned)N && wave_id() == kWavesPerBlock - 1) {
-        const int d = blockIdx.x;
+    rank_bases(recv_off + (long)D.rb * (N + 1), N + 1, N, D.rc, gb);
+    if (blockIdx.x < (unsigned)D.rc && wave_id() == kWavesPerBlock - 1) {
+        const int d = D.rb + blockIdx.x;
         int carry = 0;
         for (int b = 0; b < L; b += kWave) {
             const int j = b + lane_id();
@@ -339,9 +340,10 @@ __global__ __launch_bounds__(kBlock) void k_unpack(Dims D, const int32_t* __rest
     __syncthreads();
     const long G = (long)blockIdx.x * RPB + wave_id();
     RowDesc rd = {0, 0, 0, 0};
-    if (wave_id() < RPB && G < gb[N]) {
-        const int d = wave_count_le(gb + 1, N, G);  // ranks whose rows all lie before G
-        const long r = G - gb[d];
+    if (wave_id() < RPB && G < gb[D.rc]) {
+        const int dl = wave_count_le(gb + 1, D.rc, G);  // ranks whose rows all lie before G
+        const int d = D.rb + dl;
+        const long r = G - gb[dl];
         const int32_t* ro = recv_off + (long)d * (N + 1);
         const int s = wave_count_le(ro, N, r) - 1;
         const size_t rrow = (size_t)d * D.B + r;
@@ -395,13 +397,24 @@ hipError_t launch_dispatch_send(const Dims& D, const void* x, const float* x_sca
     const int CH = send_chunk(D);
     const int C = (D.TR + CH - 1) / CH;
     int32_t* chunk_cnt = static_cast<int32_t*>(workspace);
+    // the call's ranks [rb, rb + rc): per-rank arrays start at rank rb
+    const long rb = D.rb;
+    const long xrow = D.fp8 ? D.H : 2L * D.H;
+    x = static_cast<const uint8_t*>(x) + rb * D.T * xrow;
+    if (x_scale) x_scale += rb * D.T * D.nsc;
+    topk_idx += rb * D.TR;
+    counts += rb * D.E;
+    send_off += rb * (D.N + 1);
+    send_pos += rb * D.TR;
+    send_buf = static_cast<uint8_t*>(send_buf) + rb * D.TR * D.P;
+    send_meta += rb * D.TR * 2;
     if (C > 1) {
-        hipLaunchKernelGGL(k_send_hist, dim3(C, D.N), dim3(CH), (D.E + CH) * 4, st, D, topk_idx, chunk_cnt, C);
+        hipLaunchKernelGGL(k_send_hist, dim3(C, D.rc), dim3(CH), (D.E + CH) * 4, st, D, topk_idx, chunk_cnt, C);
     }
     const size_t lds = send_rank_lds(D, CH);
-    hipLaunchKernelGGL(k_send_rank, dim3(C, D.N), dim3(CH), lds, st, D, topk_idx,
+    hipLaunchKernelGGL(k_send_rank, dim3(C, D.rc), dim3(CH), lds, st, D, topk_idx,
                        (const int32_t*)chunk_cnt, C, counts, send_off, send_pos, send_meta);
-    const long ntok = (long)D.N * D.T;
+    const long ntok = (long)D.rc * D.T;
     hipLaunchKernelGGL(k_send_pack<8>, dim3((ntok + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock), 0,
                        st, D, (const uint8_t*)x, x_scale, (const int32_t*)send_pos, (uint8_t*)send_buf);
     return hipGetLastError();
@@ -410,9 +423,9 @@ hipError_t launch_dispatch_send(const Dims& D, const void* x, const float* x_sca
 hipError_t launch_net_dispatch(const Dims& D, const int32_t* send_off, const void* send_buf,
                                const int32_t* send_meta, void* recv_buf, int32_t* recv_meta,
                                int32_t* recv_off, hipStream_t st) {
-    const long rows = (long)D.N * D.TR;
+    const long rows = (long)D.rc * D.TR;  // the send rows of the call's ranks
     const StreamShape sh = stream_shape(D.P16, MOE_NET_MIN_CHUNKS);
-    const long blocks = std::max<long>((rows + sh.rpb - 1) / sh.rpb, D.N);
+    const long blocks = std::max<long>((rows + sh.rpb - 1) / sh.rpb, D.rc);
 #define MOE_LAUNCH(R_, U_)                                                                         \
     if (sh.rpb == R_ && sh.u == U_)                                                                \
         hipLaunchKernelGGL((k_net_dispatch<R_, U_>), dim3(blocks), dim3(kBlock), 0, st, D, send_off, \
@@ -429,12 +442,12 @@ hipError_t launch_dispatch_recv(const Dims& D, const int32_t* counts, const int3
                                 float* expert_scale, int32_t* expert_cnt, int32_t* expert_off,
                                 int32_t* expert_src, int32_t* expert_rpos, void* /*workspace*/,
                                 hipStream_t st) {
-    const long rows = (long)D.N * D.TR;  // every received row, over all ranks, is one of these
+    const long rows = recv_rows_bound(D);
     const StreamShape sh = stream_shape(D.P16, MOE_UNPACK_MIN_CHUNKS);
-    const long blocks = std::max<long>((rows + sh.rpb - 1) / sh.rpb, D.N);
+    const long blocks = std::max<long>((rows + sh.rpb - 1) / sh.rpb, D.rc);
 #define MOE_LAUNCH(R_, U_)                                                                          \
     if (sh.rpb == R_ && sh.u == U_)                                                                 \
-        hipLaunchKernelGGL((k_unpack<R_, U_>), dim3(blocks), dim3(kBlock), (D.N + 1) * 4, st, D, counts, \
+        hipLaunchKernelGGL((k_unpack<R_, U_>), dim3(blocks), dim3(kBlock), (D.rc + 1) * 4, st, D, counts, \
                            recv_off, (const uint8_t*)recv_buf, recv_meta, (uint8_t*)expert_x,       \
                            expert_scale, expert_cnt, expert_off, expert_src, expert_rpos);
     MOE_STREAM_SHAPES(MOE_LAUNCH)

@@ -140,7 +140,12 @@ static void launch_g(int vpl, dim3 grid, hipStream_t st, const float* logits, co
 
 hipError_t launch_route(const Dims& D, const float* logits, const float* bias, int32_t* topk_idx,
                         float* topk_w, hipStream_t st) {
-    const int ntok = D.N * D.T;
+    // the tokens of ranks [rb, rb + rc)
+    const long t0 = (long)D.rb * D.T;
+    const int ntok = D.rc * D.T;
+    logits += t0 * D.E;
+    topk_idx += t0 * D.R;
+    topk_w += t0 * D.R;
     // the smallest group with at most 16 experts per lane and at least R lanes
     int G = 16;
     while (G < 64 && (D.E > 16 * G || D.R > G)) G *= 2;

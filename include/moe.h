@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum {
     MOE_OK = 0,
@@ -60,6 +60,12 @@ typedef struct {
     int32_t E;          /* experts, multiple of N, at most 1024 */
     int32_t R;          /* experts per token, 1..min(E, 64) */
     int32_t dtype;      /* moe_dtype of the dispatch payload; combine is always bf16 */
+    int32_t rank_begin; /* the ranks whose work this call does: [rank_begin, rank_begin + rank_count); */
+    int32_t rank_count; /*   0, 0 = all N.  A rank owns its tokens (route, dispatch send, weighted
+                             sum), the pushes of its own rows to every peer (both network steps) and
+                             its receive side (dispatch receive, combine shuffle, stand-in expert).
+                             Running every rank's calls, each step for all ranks before the next,
+                             gives exactly the all-ranks result.  Arrays stay full-size [N][...]. */
     int64_t capacity;   /* receive-side rows per rank; 0 = N*T*max(R, E/N), the [EFA] bound.
                            Must be at least N*T*min(R, E/N), the most any rank can receive. */
     int32_t* status;    /* device int32 sticky error word, or NULL */

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strerror():
-    assert moe.moe_abi_version() == 1
+    assert moe.moe_abi_version() == 2
     for code in (0, -1, -2, -3, -5, 42):
         assert isinstance(moe.moe_strerror(code), str)
 
@@ -63,6 +63,18 @@ def test_bad_shapes(args, code):
     with pytest.raises(moe.MoeError) as ex:
         moe.moe_sizes(moe.make_shape(*args))
     assert ex.value.code == code
+
+
+@pytest.mark.parametrize("rb,rc", [(-1, 1), (0, -1), (3, 0), (2, 3), (4, 1)])
+def test_bad_rank_ranges(rb, rc):
+    with pytest.raises(moe.MoeError) as ex:
+        moe.moe_sizes(moe.make_shape(4, 16, 256, 8, 2, rank_begin=rb, rank_count=rc))
+    assert ex.value.code == moe.MOE_EINVAL
+
+
+def test_good_rank_ranges():
+    for rb, rc in [(0, 0), (0, 4), (3, 1), (1, 2)]:
+        moe.moe_sizes(moe.make_shape(4, 16, 256, 8, 2, rank_begin=rb, rank_count=rc))
 
 
 def test_bad_fp8_hidden_and_capacity():

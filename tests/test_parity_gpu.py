@@ -130,6 +130,55 @@ def test_overlap_with_second_stream():
     parity.compare(g, o, N, T, H, E, R, False)
 
 
+@pytest.mark.parametrize("case", [SMALL[3], SMALL[7], SMALL[8], SMALL[11]], ids=lambda c: _case_id(c))
+def test_rank_subrange_calls_compose(case):
+    # every step called once per rank (as each GPU of a real deployment would), each step for all
+    # ranks before the next, gives exactly the all-ranks result; ranges of 2 ranks as well
+    import combine_moe_route_top_amd as moe
+    N, T, H, E, R, fp8, bias = case
+    print(f"\ncase rank-subrange {_case_id(case)}", flush=True)
+    inp = ms.make_inputs(N, T, H, E, R, fp8, bias, 3)
+    _, full = parity.gpu_run(N, T, H, E, R, fp8, inp, expert_mode=1)
+    for width in (1, 2):
+        b = moe.alloc_buffers(N, T, H, E, R, fp8)
+        for t in b.t.values():
+            if t is not None:
+                t.view(torch.uint8).fill_(0x5A)
+        b.status.zero_()
+        parity.upload_inputs(b, inp)
+        ranges = [(r0, min(width, N - r0)) for r0 in range(0, N, width)]
+        sub = [moe.for_ranks(b.shape, r0, n) for r0, n in ranges]
+        use_bias = inp["bias"] is not None
+        for sh in sub:
+            moe.moe_route(sh, b.logits, b.bias if use_bias else None, b.topk_idx, b.topk_w)
+        for sh in sub:
+            moe.moe_dispatch_send(sh, b.x, b.x_scale, b.topk_idx, b.counts, b.send_off, b.send_pos,
+                                  b.send_buf, b.send_meta, b.workspace)
+        for sh in sub:
+            moe.moe_net_dispatch(sh, b.send_off, b.send_buf, b.send_meta, b.recv_buf, b.recv_meta,
+                                 b.recv_off)
+        for sh in sub:
+            moe.moe_dispatch_recv(sh, b.counts, b.recv_off, b.recv_buf, b.recv_meta, b.expert_x,
+                                  b.expert_scale, b.expert_cnt, b.expert_off, b.expert_src,
+                                  b.expert_rpos, b.workspace)
+        for sh in sub:
+            moe.moe_expert_stub(sh, 1, b.expert_x, b.expert_scale, b.expert_off, b.expert_y)
+        for sh in sub:
+            moe.moe_combine_send(sh, b.expert_y, b.expert_rpos, b.recv_off, b.send_off, b.cs_buf,
+                                 b.cr_buf)
+        for sh in sub:
+            moe.moe_combine_recv(sh, b.cr_buf, b.send_pos, b.topk_w, b.out)
+        torch.cuda.synchronize()
+        g = parity.fetch(b, N, T, R)
+        for k in ("topk_idx", "topk_w", "counts", "send_off", "send_pos", "recv_off", "expert_cnt",
+                  "expert_off", "out", "status"):
+            assert np.array_equal(g[k], full[k]), (width, k)
+        for k in ("send_rows", "send_meta", "recv_rows", "recv_meta", "expert_x", "expert_src",
+                  "expert_rpos", "expert_y", "cs_buf", "cr_buf"):
+            for d in range(N):
+                assert np.array_equal(g[k][d], full[k][d]), (width, k, d)
+
+
 def test_tight_capacity():
     # receive buffers sized to the tight bound N*T*min(R, E/N) instead of N*T*max(R, E/N)
     N, T, H, E, R = 4, 40, 64, 32, 8
