@@ -36,18 +36,12 @@ __device__ __forceinline__ uint32_t f64_to_bf16(double x) {
     return f32_to_bf16(f);
 }
 
-// One wave per expert-major row (flattened over ranks).  mode 0: identity; mode 1: times
-// (64 + e % 64) / 64.  The product is formed exactly in fp64 and rounded once to bf16.
-__global__ __launch_bounds__(kBlock) void k_expert_stub(Dims D, int mode, const uint8_t* __restrict__ expert_x,
-                                                        const float* __restrict__ expert_scale,
-                                                        const int32_t* __restrict__ expert_off,
-                                                        uint16_t* __restrict__ expert_y) {
-    extern __shared__ int gb[];
+// The stand-in expert for one expert-major row G (a global index over the call's ranks).
+__device__ __forceinline__ void stub_row(Dims D, int mode, const uint8_t* __restrict__ expert_x,
+                                         const float* __restrict__ expert_scale,
+                                         const int32_t* __restrict__ expert_off,
+                                         uint16_t* __restrict__ expert_y, const int* gb, long G) {
     const int L = D.L;
-    rank_bases(expert_off + (long)D.rb * (L + 1), L + 1, L, D.rc, gb);
-    __syncthreads();
-    const long G = (long)blockIdx.x * kWavesPerBlock + wave_id();
-    if (G >= gb[D.rc]) return;
     const int dl = wave_count_le(gb + 1, D.rc, G);
     const int d = D.rb + dl;
     const long q = G - gb[dl];
@@ -85,11 +79,28 @@ __global__ __launch_bounds__(kBlock) void k_expert_stub(Dims D, int mode, const 
     }
 }
 
+// One wave per expert-major row (a global index over the call's ranks; waves stride over the
+// rows).  mode 0: identity; mode 1: times (64 + e % 64) / 64.  The product is formed exactly in
+// fp64 and rounded once to bf16.
+__global__ __launch_bounds__(kBlock) void k_expert_stub(Dims D, int mode, const uint8_t* __restrict__ expert_x,
+                                                        const float* __restrict__ expert_scale,
+                                                        const int32_t* __restrict__ expert_off,
+                                                        uint16_t* __restrict__ expert_y) {
+    extern __shared__ int gb[];
+    const int L = D.L;
+    rank_bases(expert_off + (long)D.rb * (L + 1), L + 1, L, D.rc, gb);
+    __syncthreads();
+    for (long G = (long)blockIdx.x * kWavesPerBlock + wave_id(); G < gb[D.rc];
+         G += (long)gridDim.x * kWavesPerBlock)
+        stub_row(D, mode, expert_x, expert_scale, expert_off, expert_y, gb, G);
+}
+
 // ------------------------------------------------------------------ combine
 
 // Shuffle: cs[d][expert_rpos[q]] = y[d][q].  RPB expert-major rows per block (a global
-// index over all ranks), one resolved per wave, then streamed.
-template <int RPB, int U>
+// index over all ranks), one resolved per wave, then streamed.  STRIDE: blocks stride over the
+// rows of a capped grid (calls on a subset of ranks); otherwise one pass covers every row.
+template <int RPB, int U, bool STRIDE>
 __global__ __launch_bounds__(kBlock) void k_combine_pack(Dims D, const uint16_t* __restrict__ expert_y,
                                                          const int32_t* __restrict__ expert_rpos,
                                                          const int32_t* __restrict__ recv_off,
@@ -99,29 +110,41 @@ __global__ __launch_bounds__(kBlock) void k_combine_pack(Dims D, const uint16_t*
     const int N = D.N;
     rank_bases(recv_off + (long)D.rb * (N + 1), N + 1, N, D.rc, gb);
     __syncthreads();
-    const long G = (long)blockIdx.x * RPB + wave_id();
-    RowDesc rd = {0, 0, 0, 0};
-    if (wave_id() < RPB && G < gb[D.rc]) {
-        const int dl = wave_count_le(gb + 1, D.rc, G);
-        const int d = D.rb + dl;
-        const long q = G - gb[dl];
-        const long r = expert_rpos[(size_t)d * D.B + q];
-        if (r >= 0 && r < D.B) {
-            rd.src_a = rd.src_b = (uint64_t)(expert_y + ((size_t)d * D.B + q) * D.H);
-            rd.dst_a = rd.dst_b = (uint64_t)(cs_buf + ((size_t)d * D.B + r) * D.H);
-        } else {
-            set_status(D.status, MOE_EINVAL);
+    const long total = gb[D.rc];
+    auto pass = [&](long base) {
+        const long G = base + wave_id();
+        RowDesc rd = {0, 0, 0, 0};
+        if (wave_id() < RPB && G < total) {
+            const int dl = wave_count_le(gb + 1, D.rc, G);
+            const int d = D.rb + dl;
+            const long q = G - gb[dl];
+            const long r = expert_rpos[(size_t)d * D.B + q];
+            if (r >= 0 && r < D.B) {
+                rd.src_a = rd.src_b = (uint64_t)(expert_y + ((size_t)d * D.B + q) * D.H);
+                rd.dst_a = rd.dst_b = (uint64_t)(cs_buf + ((size_t)d * D.B + r) * D.H);
+            } else {
+                set_status(D.status, MOE_EINVAL);
+            }
         }
+        if (wave_id() < RPB && lane_id() == 0) rows[wave_id()] = rd;
+        __syncthreads();
+        block_stream_rows<U>(rows, RPB, D.Y16, D.Y16, D.Y16);
+    };
+    if constexpr (STRIDE) {
+        for (long base = (long)blockIdx.x * RPB; base < total; base += (long)gridDim.x * RPB) {
+            pass(base);
+            if (base + (long)gridDim.x * RPB < total) __syncthreads();  // rows[] is rewritten
+        }
+    } else {
+        pass((long)blockIdx.x * RPB);
     }
-    if (wave_id() < RPB && lane_id() == 0) rows[wave_id()] = rd;
-    __syncthreads();
-    block_stream_rows<U>(rows, RPB, D.Y16, D.Y16, D.Y16);
 }
 
 // Network back: the call's ranks d push their combine send buffers, read in order (a global
 // index over those ranks); row r of segment (s -> d) lands at send_off[s][d] + (r - recv_off[d][s])
-// in rank s's combine receive buffer, where s's dispatch send buffer had it.
-template <int RPB, int U>
+// in rank s's combine receive buffer, where s's dispatch send buffer had it.  STRIDE as for the
+// shuffle.
+template <int RPB, int U, bool STRIDE>
 __global__ __launch_bounds__(kBlock) void k_combine_net(Dims D, const uint16_t* __restrict__ cs_buf,
                                                         const int32_t* __restrict__ recv_off,
                                                         const int32_t* __restrict__ send_off,
@@ -131,25 +154,36 @@ __global__ __launch_bounds__(kBlock) void k_combine_net(Dims D, const uint16_t* 
     const int N = D.N;
     rank_bases(recv_off + (long)D.rb * (N + 1), N + 1, N, D.rc, gb);
     __syncthreads();
-    const long G = (long)blockIdx.x * RPB + wave_id();
-    RowDesc rd = {0, 0, 0, 0};
-    if (wave_id() < RPB && G < gb[D.rc]) {
-        const int dl = wave_count_le(gb + 1, D.rc, G);
-        const int d = D.rb + dl;
-        const long r = G - gb[dl];
-        const int32_t* ro = recv_off + (long)d * (N + 1);
-        const int s = wave_count_le(ro, N, r) - 1;
-        const long i = s >= 0 ? send_off[(long)s * (N + 1) + d] + (r - ro[s]) : -1;
-        if (i >= 0 && i < D.TR) {
-            rd.src_a = rd.src_b = (uint64_t)(cs_buf + ((size_t)d * D.B + r) * D.H);
-            rd.dst_a = rd.dst_b = (uint64_t)(cr_buf + ((size_t)s * D.TR + i) * D.H);
-        } else {
-            set_status(D.status, MOE_EINVAL);
+    const long total = gb[D.rc];
+    auto pass = [&](long base) {
+        const long G = base + wave_id();
+        RowDesc rd = {0, 0, 0, 0};
+        if (wave_id() < RPB && G < total) {
+            const int dl = wave_count_le(gb + 1, D.rc, G);
+            const int d = D.rb + dl;
+            const long r = G - gb[dl];
+            const int32_t* ro = recv_off + (long)d * (N + 1);
+            const int s = wave_count_le(ro, N, r) - 1;
+            const long i = s >= 0 ? send_off[(long)s * (N + 1) + d] + (r - ro[s]) : -1;
+            if (i >= 0 && i < D.TR) {
+                rd.src_a = rd.src_b = (uint64_t)(cs_buf + ((size_t)d * D.B + r) * D.H);
+                rd.dst_a = rd.dst_b = (uint64_t)(cr_buf + ((size_t)s * D.TR + i) * D.H);
+            } else {
+                set_status(D.status, MOE_EINVAL);
+            }
         }
+        if (wave_id() < RPB && lane_id() == 0) rows[wave_id()] = rd;
+        __syncthreads();
+        block_stream_rows<U>(rows, RPB, D.Y16, D.Y16, D.Y16);
+    };
+    if constexpr (STRIDE) {
+        for (long base = (long)blockIdx.x * RPB; base < total; base += (long)gridDim.x * RPB) {
+            pass(base);
+            if (base + (long)gridDim.x * RPB < total) __syncthreads();  // rows[] is rewritten
+        }
+    } else {
+        pass((long)blockIdx.x * RPB);
     }
-    if (wave_id() < RPB && lane_id() == 0) rows[wave_id()] = rd;
-    __syncthreads();
-    block_stream_rows<U>(rows, RPB, D.Y16, D.Y16, D.Y16);
 }
 
 // Weighted sum: out[s][t] = bf16(sum_k w[k] * cr[s][send_pos[k]]), fp32 fused multiply-adds in
@@ -227,7 +261,7 @@ __global__ __launch_bounds__(kBlock) void k_wsum(Dims D, const uint16_t* __restr
 hipError_t launch_expert_stub(const Dims& D, int mode, const void* expert_x, const float* expert_scale,
                               const int32_t* expert_off, uint16_t* expert_y, hipStream_t st) {
     const long rows = recv_rows_bound(D);
-    hipLaunchKernelGGL(k_expert_stub, dim3((rows + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock),
+    hipLaunchKernelGGL(k_expert_stub, dim3(row_blocks(D, rows, kWavesPerBlock)), dim3(kBlock),
                        (D.rc + 1) * 4, st, D, mode, (const uint8_t*)expert_x, expert_scale, expert_off,
                        expert_y);
     return hipGetLastError();
@@ -239,18 +273,29 @@ hipError_t launch_combine_send(const Dims& D, const uint16_t* expert_y, const in
     const long rows = recv_rows_bound(D);  // rows the call's ranks received
     const StreamShape sp = stream_shape(D.Y16, MOE_CPACK_MIN_CHUNKS);
     const StreamShape sn = stream_shape(D.Y16, MOE_CNET_MIN_CHUNKS);
+    // blocks stride over the rows only when the grid was capped (calls on a subset of ranks)
+#define MOE_LAUNCH_S(K_, R_, U_, S_, ...)                                                            \
+    hipLaunchKernelGGL((K_<R_, U_, S_>), dim3(row_blocks(D, rows, R_)), dim3(kBlock), (D.rc + 1) * 4, \
+                       st, D, __VA_ARGS__);
 #define MOE_LAUNCH(R_, U_)                                                                          \
-    if (sp.rpb == R_ && sp.u == U_)                                                                 \
-        hipLaunchKernelGGL((k_combine_pack<R_, U_>), dim3((rows + R_ - 1) / R_), dim3(kBlock),       \
-                           (D.rc + 1) * 4, st, D, expert_y, expert_rpos, recv_off, cs_buf);
+    if (sp.rpb == R_ && sp.u == U_) {                                                               \
+        if (row_blocks(D, rows, R_) * R_ < rows)                                                    \
+            MOE_LAUNCH_S(k_combine_pack, R_, U_, true, expert_y, expert_rpos, recv_off, cs_buf)     \
+        else                                                                                        \
+            MOE_LAUNCH_S(k_combine_pack, R_, U_, false, expert_y, expert_rpos, recv_off, cs_buf)    \
+    }
     MOE_STREAM_SHAPES(MOE_LAUNCH)
 #undef MOE_LAUNCH
 #define MOE_LAUNCH(R_, U_)                                                                          \
-    if (sn.rpb == R_ && sn.u == U_)                                                                 \
-        hipLaunchKernelGGL((k_combine_net<R_, U_>), dim3((rows + R_ - 1) / R_), dim3(kBlock),        \
-                           (D.rc + 1) * 4, st, D, (const uint16_t*)cs_buf, recv_off, send_off, cr_buf);
+    if (sn.rpb == R_ && sn.u == U_) {                                                               \
+        if (row_blocks(D, rows, R_) * R_ < rows)                                                    \
+            MOE_LAUNCH_S(k_combine_net, R_, U_, true, (const uint16_t*)cs_buf, recv_off, send_off, cr_buf) \
+        else                                                                                        \
+            MOE_LAUNCH_S(k_combine_net, R_, U_, false, (const uint16_t*)cs_buf, recv_off, send_off, cr_buf) \
+    }
     MOE_STREAM_SHAPES(MOE_LAUNCH)
 #undef MOE_LAUNCH
+#undef MOE_LAUNCH_S
     return hipGetLastError();
 }
 

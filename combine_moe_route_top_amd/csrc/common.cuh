@@ -107,6 +107,16 @@ inline long recv_rows_bound(const Dims& D) {
     return b < all ? b : all;
 }
 
+// Blocks for a row kernel whose rows are only known on the device: one block per RPB rows of
+// the bound when the call covers all ranks (every row exists), at most kSubrangeBlocks when it
+// covers a subset (most of the bound is usually empty; blocks then stride over the rows).
+constexpr long kSubrangeBlocks = 4096;
+inline long row_blocks(const Dims& D, long rows_bound, int rpb) {
+    long b = (rows_bound + rpb - 1) / rpb;
+    if (D.rc < D.N && b > kSubrangeBlocks) b = kSubrangeBlocks;
+    return b > D.rc ? b : D.rc;
+}
+
 // ------------------------------------------------------------------ block row streaming
 
 // Nontemporal 16-byte accesses: streamed data does not stay in the caches, and the stores do not

@@ -177,14 +177,17 @@ __global__ __launch_bounds__(1024) void k_send_rank(Dims D, const int32_t* __res
 
 // ------------------------------------------------------------------ pack
 
-// One wave per token: its payload (and fp8 scales) is read once and written to each of the
-// token's R send rows.
+// WPT waves per token (WPT > 1 only when the call has few tokens): the token's payload (and fp8
+// scales) is read once and written to each of its R send rows; wave `part` of a token owns the
+// chunk groups part, part + WPT, ... of 64 chunks.
 template <int U>
-__global__ __launch_bounds__(kBlock) void k_send_pack(Dims D, const uint8_t* __restrict__ x,
+__global__ __launch_bounds__(kBlock) void k_send_pack(Dims D, int WPT, const uint8_t* __restrict__ x,
                                                       const float* __restrict__ x_scale,
                                                       const int32_t* __restrict__ send_pos,
                                                       uint8_t* __restrict__ send_buf) {
-    const long tok = (long)blockIdx.x * kWavesPerBlock + wave_id();  // within the call's ranks
+    const long gw = (long)blockIdx.x * kWavesPerBlock + wave_id();
+    const long tok = gw / WPT;  // within the call's ranks
+    const int part = (int)(gw - tok * WPT);
     if (tok >= (long)D.rc * D.T) return;
     const int lane = lane_id();
     const long s = tok / D.T;
@@ -195,11 +198,12 @@ __global__ __launch_bounds__(kBlock) void k_send_pack(Dims D, const uint8_t* __r
     const u32x4* src_b = D.fp8 ? reinterpret_cast<const u32x4*>(x_scale + tok * D.nsc) : src_a;
     uint8_t* rank_base = send_buf + (size_t)s * D.TR * D.P;
     const int n16 = D.P16, split = D.X16;
-    for (int c0 = 0; c0 < n16; c0 += kWave * U) {
+    const int stride = kWave * WPT;
+    for (int c0 = part * kWave; c0 < n16; c0 += stride * U) {
         u32x4 v[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int c = c0 + u * kWave + lane;
+            const int c = c0 + u * stride + lane;
             if (c < n16) v[u] = c < split ? src_a[c] : src_b[c - split];
         }
         for (int k = 0; k < R; ++k) {
@@ -208,7 +212,7 @@ __global__ __launch_bounds__(kBlock) void k_send_pack(Dims D, const uint8_t* __r
             u32x4* dst = reinterpret_cast<u32x4*>(rank_base + (size_t)pos * D.P);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int c = c0 + u * kWave + lane;
+                const int c = c0 + u * stride + lane;
                 if (c < n16) dst[c] = v[u];
             }
         }
@@ -302,8 +306,10 @@ __device__ __forceinline__ long expert_base(const int32_t* __restrict__ counts, 
 // RPB received rows per block (a global index over all ranks), one resolved per wave:
 // its expert-major position is expert_base(d, s, j) + the per-expert rank carried in its
 // metadata.  The rows are those received by the call's ranks; block b < rank_count also writes
-// the expert_cnt and expert_off of rank rank_begin + b.
-template <int RPB, int U>
+// the expert_cnt and expert_off of rank rank_begin + b.  STRIDE: blocks stride over the rows
+// (a capped grid, for calls on a subset of ranks); otherwise the grid covers every row once, a
+// shape that keeps fewer registers live.
+template <int RPB, int U, bool STRIDE>
 __global__ __launch_bounds__(kBlock) void k_unpack(Dims D, const int32_t* __restrict__ counts,
                                                    const int32_t* __restrict__ recv_off,
                                                    const uint8_t* __restrict__ recv_buf,
@@ -338,37 +344,48 @@ __global__ __launch_bounds__(kBlock) void k_unpack(Dims D, const int32_t* __rest
         if (lane_id() == 0) expert_off[(long)d * (L + 1) + L] = carry;
     }
     __syncthreads();
-    const long G = (long)blockIdx.x * RPB + wave_id();
-    RowDesc rd = {0, 0, 0, 0};
-    if (wave_id() < RPB && G < gb[D.rc]) {
-        const int dl = wave_count_le(gb + 1, D.rc, G);  // ranks whose rows all lie before G
-        const int d = D.rb + dl;
-        const long r = G - gb[dl];
-        const int32_t* ro = recv_off + (long)d * (N + 1);
-        const int s = wave_count_le(ro, N, r) - 1;
-        const size_t rrow = (size_t)d * D.B + r;
-        const int2 m = reinterpret_cast<const int2*>(recv_meta)[rrow];
-        const int e = m.x / D.TR;
-        const int i = m.x - e * D.TR;
-        const int j = e - d * L;
-        const long q = (j >= 0 && j < L && s >= 0) ? expert_base(counts, N, E, L, d, s, j) + m.y : -1;
-        if (q >= 0 && q < D.B) {
-            const size_t qrow = (size_t)d * D.B + q;
-            if (lane_id() == 0) {
-                expert_src[qrow] = s * D.TR + i;
-                expert_rpos[qrow] = (int32_t)r;
+    const long total = gb[D.rc];
+    auto pass = [&](long base) {
+        const long G = base + wave_id();
+        RowDesc rd = {0, 0, 0, 0};
+        if (wave_id() < RPB && G < total) {
+            const int dl = wave_count_le(gb + 1, D.rc, G);  // ranks whose rows all lie before G
+            const int d = D.rb + dl;
+            const long r = G - gb[dl];
+            const int32_t* ro = recv_off + (long)d * (N + 1);
+            const int s = wave_count_le(ro, N, r) - 1;
+            const size_t rrow = (size_t)d * D.B + r;
+            const int2 m = reinterpret_cast<const int2*>(recv_meta)[rrow];
+            const int e = m.x / D.TR;
+            const int i = m.x - e * D.TR;
+            const int j = e - d * L;
+            const long q = (j >= 0 && j < L && s >= 0) ? expert_base(counts, N, E, L, d, s, j) + m.y : -1;
+            if (q >= 0 && q < D.B) {
+                const size_t qrow = (size_t)d * D.B + q;
+                if (lane_id() == 0) {
+                    expert_src[qrow] = s * D.TR + i;
+                    expert_rpos[qrow] = (int32_t)r;
+                }
+                const long xrow = D.fp8 ? D.H : 2L * D.H;
+                rd.src_a = rd.src_b = (uint64_t)(recv_buf + rrow * D.P);
+                rd.dst_a = (uint64_t)(expert_x + qrow * xrow);
+                rd.dst_b = D.fp8 ? (uint64_t)(expert_scale + qrow * D.nsc) : rd.dst_a;
+            } else {
+                set_status(D.status, MOE_EINVAL);
             }
-            const long xrow = D.fp8 ? D.H : 2L * D.H;
-            rd.src_a = rd.src_b = (uint64_t)(recv_buf + rrow * D.P);
-            rd.dst_a = (uint64_t)(expert_x + qrow * xrow);
-            rd.dst_b = D.fp8 ? (uint64_t)(expert_scale + qrow * D.nsc) : rd.dst_a;
-        } else {
-            set_status(D.status, MOE_EINVAL);
         }
+        if (wave_id() < RPB && lane_id() == 0) rows[wave_id()] = rd;
+        __syncthreads();
+        block_stream_rows<U>(rows, RPB, D.P16, D.P16, D.X16);
+    };
+    if constexpr (STRIDE) {
+        for (long base = (long)blockIdx.x * RPB; base < total; base += (long)gridDim.x * RPB) {
+            pass(base);
+            if (base + (long)gridDim.x * RPB < total) __syncthreads();  // rows[] is rewritten
+        }
+    } else {
+        pass((long)blockIdx.x * RPB);
     }
-    if (wave_id() < RPB && lane_id() == 0) rows[wave_id()] = rd;
-    __syncthreads();
-    block_stream_rows<U>(rows, RPB, D.P16, D.P16, D.X16);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -415,8 +432,12 @@ hipError_t launch_dispatch_send(const Dims& D, const void* x, const float* x_sca
     hipLaunchKernelGGL(k_send_rank, dim3(C, D.rc), dim3(CH), lds, st, D, topk_idx,
                        (const int32_t*)chunk_cnt, C, counts, send_off, send_pos, send_meta);
     const long ntok = (long)D.rc * D.T;
-    hipLaunchKernelGGL(k_send_pack<8>, dim3((ntok + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock), 0,
-                       st, D, (const uint8_t*)x, x_scale, (const int32_t*)send_pos, (uint8_t*)send_buf);
+    // up to 8 waves per token when there are fewer than 4096 tokens to keep the chip busy
+    int wpt = 1;
+    while (wpt < 8 && ntok * wpt < 4096 && (long)kWave * wpt * 2 <= D.P16) wpt *= 2;
+    const long waves = ntok * wpt;
+    hipLaunchKernelGGL(k_send_pack<8>, dim3((waves + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock), 0,
+                       st, D, wpt, (const uint8_t*)x, x_scale, (const int32_t*)send_pos, (uint8_t*)send_buf);
     return hipGetLastError();
 }
 
@@ -444,14 +465,19 @@ hipError_t launch_dispatch_recv(const Dims& D, const int32_t* counts, const int3
                                 hipStream_t st) {
     const long rows = recv_rows_bound(D);
     const StreamShape sh = stream_shape(D.P16, MOE_UNPACK_MIN_CHUNKS);
-    const long blocks = std::max<long>((rows + sh.rpb - 1) / sh.rpb, D.rc);
+    const long blocks = row_blocks(D, rows, sh.rpb);
+    const bool stride = blocks * sh.rpb < rows;
+#define MOE_LAUNCH_S(R_, U_, S_)                                                                    \
+    hipLaunchKernelGGL((k_unpack<R_, U_, S_>), dim3(blocks), dim3(kBlock), (D.rc + 1) * 4, st, D, counts, \
+                       recv_off, (const uint8_t*)recv_buf, recv_meta, (uint8_t*)expert_x, expert_scale,  \
+                       expert_cnt, expert_off, expert_src, expert_rpos);
 #define MOE_LAUNCH(R_, U_)                                                                          \
-    if (sh.rpb == R_ && sh.u == U_)                                                                 \
-        hipLaunchKernelGGL((k_unpack<R_, U_>), dim3(blocks), dim3(kBlock), (D.rc + 1) * 4, st, D, counts, \
-                           recv_off, (const uint8_t*)recv_buf, recv_meta, (uint8_t*)expert_x,       \
-                           expert_scale, expert_cnt, expert_off, expert_src, expert_rpos);
+    if (sh.rpb == R_ && sh.u == U_) {                                                               \
+        if (stride) MOE_LAUNCH_S(R_, U_, true) else MOE_LAUNCH_S(R_, U_, false)                     \
+    }
     MOE_STREAM_SHAPES(MOE_LAUNCH)
 #undef MOE_LAUNCH
+#undef MOE_LAUNCH_S
     return hipGetLastError();
 }
 
