@@ -52,6 +52,8 @@ def lib():
         _lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
         _lib.oracle_e4m3_to_double.restype = ctypes.c_double
         _lib.oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
+        _lib.oracle_e4m3_from_float_sat.restype = ctypes.c_uint8
+        _lib.oracle_e4m3_from_float_sat.argtypes = [ctypes.c_float]
         _lib.oracle_row_bytes.restype = ctypes.c_long
     return _lib
 
@@ -59,11 +61,27 @@ def lib():
 class Shape(ctypes.Structure):
     _fields_ = [("N", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int),
                 ("E", ctypes.c_int), ("R", ctypes.c_int), ("fp8", ctypes.c_int),
-                ("B", ctypes.c_long), ("rbase", ctypes.c_void_p)]
+                ("B", ctypes.c_long), ("rbase", ctypes.c_void_p), ("tokens", ctypes.c_void_p)]
 
     # With rbase set (an int64 array of N+1 row bases kept alive here), receive-side arrays are
     # packed: rank d owns rows rbase[d] .. rbase[d+1]-1 of one [rows][...] array.
     _rbase_arr = None
+    # With tokens set (an int32 array of N token counts kept alive here), rank s dispatches only
+    # its first tokens[s] tokens.
+    _tokens_arr = None
+
+    def set_tokens(self, tokens):
+        if tokens is None:
+            self.tokens, self._tokens_arr = None, None
+        else:
+            t = np.ascontiguousarray(tokens, np.int32)
+            assert t.shape == (self.N,) and t.min() >= 0 and t.max() <= self.T
+            self._tokens_arr = t
+            self.tokens = t.ctypes.data
+        return self
+
+    def ntok(self, s) -> int:
+        return self.T if self._tokens_arr is None else int(self._tokens_arr[s])
 
     def rows(self) -> int:
         return int(self._rbase_arr[-1]) if self._rbase_arr is not None else self.N * self.B
@@ -80,13 +98,14 @@ class Shape(ctypes.Structure):
         return arr[b0:b1] if n is None else arr[b0:b0 + n]
 
 
-def packed_shape(N, T, H, E, R, fp8, rows_per_rank) -> Shape:
+def packed_shape(N, T, H, E, R, fp8, rows_per_rank, tokens=None) -> Shape:
     """A shape whose receive-side arrays hold exactly rows_per_rank[d] rows for rank d."""
     rb = np.zeros(N + 1, np.int64)
     rb[1:] = np.cumsum(np.asarray(rows_per_rank, np.int64))
-    sh = Shape(N, T, H, E, R, int(bool(fp8)), int(max(1, np.max(rows_per_rank))), rb.ctypes.data)
+    sh = Shape(N, T, H, E, R, int(bool(fp8)), int(max(1, np.max(rows_per_rank))), rb.ctypes.data,
+               None)
     sh._rbase_arr = rb
-    return sh
+    return sh.set_tokens(tokens)
 
 
 def _p(a):
@@ -96,10 +115,10 @@ def _p(a):
     return a.ctypes.data_as(ctypes.c_void_p)
 
 
-def shape(N, T, H, E, R, fp8=False, B=None) -> Shape:
+def shape(N, T, H, E, R, fp8=False, B=None, tokens=None) -> Shape:
     if B is None:
         B = N * T * max(R, E // N)
-    return Shape(N, T, H, E, R, int(bool(fp8)), B, None)
+    return Shape(N, T, H, E, R, int(bool(fp8)), B, None, None).set_tokens(tokens)
 
 
 def row_bytes(sh: Shape) -> int:
@@ -116,6 +135,21 @@ def bf16_to_double(b: int) -> float:
 
 def e4m3_to_double(b: int) -> float:
     return float(lib().oracle_e4m3_to_double(int(b)))
+
+
+def e4m3_from_float_sat(v: float) -> int:
+    return int(lib().oracle_e4m3_from_float_sat(float(v)))
+
+
+def quantize_e4m3(x_bf16: np.ndarray):
+    """bf16 bits uint16[..., H] -> (e4m3 codes uint8[..., H], scales f32[..., H/128])."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    H = x.shape[-1]
+    n = x.size // H
+    q = np.empty(x.shape, np.uint8)
+    sc = np.empty(x.shape[:-1] + (H // 128,), np.float32)
+    lib().oracle_quantize_e4m3(ctypes.c_long(n), ctypes.c_int(H), _p(x), _p(q), _p(sc))
+    return q, sc
 
 
 def route(logits: np.ndarray, bias, R: int):
@@ -139,7 +173,7 @@ def dispatch_send(sh: Shape, x: np.ndarray, x_scale, topk_idx: np.ndarray):
     idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
     counts = np.empty((N, E), np.int32)
     send_off = np.empty((N, N + 1), np.int32)
-    send_pos = np.empty((N, T * R), np.int32)
+    send_pos = np.full((N, T * R), -1, np.int32)
     send_buf = np.zeros((N, T * R, P), np.uint8)
     send_meta = np.zeros((N, T * R, 2), np.int32)
     lib().oracle_dispatch_send(ctypes.byref(sh), _p(x), _p(xs), _p(idx), _p(counts), _p(send_off),
@@ -191,7 +225,7 @@ def combine(sh: Shape, mode: int, expert_y, expert_rpos, recv_off, send_off, sen
     N, H, T, R = sh.N, sh.H, sh.T, sh.R
     cs = np.zeros(sh.lead() + (H,), np.uint16)
     cr = np.zeros((N, T * R, H), np.uint16)
-    out = np.empty((N, T, H), np.uint16)
+    out = np.zeros((N, T, H), np.uint16)   # rows of absent tokens stay zero (not written)
     w = np.ascontiguousarray(topk_w, dtype=np.float32)
     lib().oracle_combine(ctypes.byref(sh), ctypes.c_int(mode), _p(expert_y), _p(expert_rpos),
                          _p(recv_off), _p(send_off), _p(send_pos), _p(w), _p(cs), _p(cr),
@@ -212,7 +246,7 @@ def run_all(sh: Shape, inp: dict, expert_mode: int = 0, combine_mode: int = 0,
     res.update(dispatch_send(sh, inp["x"], inp.get("x_scale"), idx.reshape(sh.N, sh.T * sh.R)))
     if tight:
         n = np.diff(res["send_off"], axis=1)          # n[s][d]
-        sh = packed_shape(sh.N, sh.T, sh.H, sh.E, sh.R, sh.fp8, n.sum(axis=0))
+        sh = packed_shape(sh.N, sh.T, sh.H, sh.E, sh.R, sh.fp8, n.sum(axis=0), sh._tokens_arr)
     res["shape"] = sh
     res.update(net_dispatch(sh, res["send_off"], res["send_buf"], res["send_meta"]))
     res.update(dispatch_recv(sh, res["counts"], res["recv_off"], res["recv_buf"],

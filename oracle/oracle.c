@@ -35,6 +35,13 @@ static long rcap(const oracle_shape* sh, int d) {
     return sh->rbase ? sh->rbase[d + 1] - sh->rbase[d] : sh->B;
 }
 
+/* Tokens rank s dispatches. */
+static int ntok(const oracle_shape* sh, int s) {
+    if (!sh->tokens) return sh->T;
+    assert(sh->tokens[s] >= 0 && sh->tokens[s] <= sh->T);
+    return sh->tokens[s];
+}
+
 long oracle_row_bytes(const oracle_shape* sh) {
     if (!sh->fp8) return 2L * sh->H;
     return (long)sh->H + 4L * (sh->H / 128);
@@ -80,6 +87,56 @@ double oracle_e4m3_to_double(uint8_t b) {
     if (e == 15 && m == 7) return NAN;
     double v = (e == 0) ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
     return s ? -v : v;
+}
+
+/* Nearest e4m3 value to v, ties to the even code, magnitudes above 448 clamped to 448.  The
+ * spacing of e4m3 values at |v| is 2^(floor(log2|v|) - 3) for |v| >= 2^-6 (three mantissa bits)
+ * and 2^-9 below (subnormals); v / spacing is exact (a power-of-two scaling) and nearbyint
+ * rounds it to the nearest integer, ties to even, whose parity is the code's last bit. */
+uint8_t oracle_e4m3_from_float_sat(float v) {
+    assert(isfinite(v));
+    const uint8_t sign = signbit(v) ? 0x80 : 0;
+    double a = fabs((double)v);
+    int ex;
+    frexp(a, &ex);                       /* a = m * 2^ex, 0.5 <= m < 1, so floor(log2 a) = ex - 1 */
+    int sp = (a >= ldexp(1.0, -6)) ? ex - 1 - 3 : -9;
+    double r = ldexp(nearbyint(ldexp(a, -sp)), sp);
+    if (r > 448.0) r = 448.0;
+    if (r == 0.0) return sign;
+    uint8_t code;
+    if (r < ldexp(1.0, -6)) {
+        code = (uint8_t)ldexp(r, 9);     /* subnormal: r = m * 2^-9, m = 1..7 */
+    } else {
+        frexp(r, &ex);                   /* rounding may have carried into the next binade */
+        int e = ex - 1;                  /* r = (8 + m) / 8 * 2^e */
+        int m = (int)ldexp(r, 3 - e) - 8;
+        code = (uint8_t)(((e + 7) << 3) | m);
+    }
+    return sign | code;
+}
+
+/* [DSK] Implementation, Quantization and the activation-kernel paragraph after it: activations
+ * are quantised on the fly with one scaling factor per 128-element vector, found from the
+ * block's largest absolute value.  The fp8 format (OCP E4M3, largest finite 448) and
+ * scale = amax / 448 are readings; both divisions are single fp32 operations. */
+void oracle_quantize_e4m3(long n_rows, int H, const uint16_t* x, uint8_t* q, float* scale) {
+    assert(H % 128 == 0);
+    const int nb = H / 128;
+    for (long n = 0; n < n_rows; ++n) {
+        for (int b = 0; b < nb; ++b) {
+            const uint16_t* xb = x + n * H + b * 128;
+            float amax = 0.0f;
+            for (int i = 0; i < 128; ++i) {
+                float a = fabsf((float)oracle_bf16_to_double(xb[i]));
+                if (a > amax) amax = a;
+            }
+            float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+            scale[n * nb + b] = sc;
+            for (int i = 0; i < 128; ++i)
+                q[n * H + b * 128 + i] =
+                    oracle_e4m3_from_float_sat((float)oracle_bf16_to_double(xb[i]) / sc);
+        }
+    }
 }
 
 /* ---------------------------------------------------------------- routing */
@@ -149,9 +206,11 @@ void oracle_dispatch_send(const oracle_shape* sh, const uint8_t* x, const float*
         const int32_t* idx = topk_idx + s * TR;
         int32_t* cnt = counts + (long)s * E;
         int32_t* off = send_off + (long)s * (N + 1);
+        const int Ts = ntok(sh, s);
         /* per-expert token counts */
         for (int e = 0; e < E; ++e) cnt[e] = 0;
-        for (long i = 0; i < TR; ++i) {
+        for (long i = (long)Ts * R; i < TR; ++i) send_pos[s * TR + i] = -1; /* absent tokens */
+        for (long i = 0; i < (long)Ts * R; ++i) {
             int e = idx[i];
             assert(e >= 0 && e < E);
             cnt[e] += 1;
@@ -166,7 +225,7 @@ void oracle_dispatch_send(const oracle_shape* sh, const uint8_t* x, const float*
         /* pack in (token, slot) order */
         for (int d = 0; d < N; ++d) fill[d] = 0;
         for (int e = 0; e < E; ++e) seen[e] = 0;
-        for (int t = 0; t < T; ++t) {
+        for (int t = 0; t < Ts; ++t) {
             for (int k = 0; k < R; ++k) {
                 long i = (long)t * R + k;
                 int e = idx[i];
@@ -336,7 +395,7 @@ void oracle_combine(const oracle_shape* sh, int mode, const uint16_t* expert_y,
     }
     /* weighted sum over the token's R slots */
     for (int s = 0; s < N; ++s) {
-        for (int t = 0; t < T; ++t) {
+        for (int t = 0; t < ntok(sh, s); ++t) {
             const long base = (long)s * TR + (long)t * R;
             for (int h = 0; h < H; ++h) {
                 double acc = 0.0;

@@ -30,6 +30,8 @@ typedef struct {
     long B;    /* receive-side rows per rank (row stride of every [N][B][...] array) */
     const long* rbase; /* optional: rank d's receive-side rows start at row rbase[d] and it has
                           rbase[d+1] - rbase[d] of them (N+1 entries); NULL means d * B and B */
+    const int32_t* tokens; /* optional: rank s dispatches only its first tokens[s] <= T tokens
+                              (N entries); NULL means T for every rank */
 } oracle_shape;
 
 /* Bytes of one dispatched row: the payload, then (fp8 only) its block scales. */
@@ -39,12 +41,19 @@ long oracle_row_bytes(const oracle_shape* sh);
 uint16_t oracle_bf16_from_double(double x);  /* round to nearest, ties to even */
 double oracle_bf16_to_double(uint16_t b);
 double oracle_e4m3_to_double(uint8_t b);
+uint8_t oracle_e4m3_from_float_sat(float v); /* nearest, ties to even, clamped to +-448 */
+
+/* Block quantisation of bf16 activations to e4m3 with one fp32 scale per 128 values:
+ * scale = amax / 448 (1 when amax = 0), code = e4m3(x / scale).  x: bf16 bits [n_rows][H];
+ * q: [n_rows][H]; scale: [n_rows][H / 128]. */
+void oracle_quantize_e4m3(long n_rows, int H, const uint16_t* x, uint8_t* q, float* scale);
 
 /* Router: top-R experts of fp32 (logits + bias) and softmax weights over the selected R. */
 void oracle_route(int n_tokens, int E, int R, const float* logits, const float* bias,
                   int32_t* topk_idx, float* topk_w);
 
-/* Dispatch send: counts, exclusive-scan offsets, positions, packed send rows and metadata. */
+/* Dispatch send: counts, exclusive-scan offsets, positions, packed send rows and metadata.
+ * Slots of tokens t >= tokens[s] take no part: their send_pos is -1. */
 void oracle_dispatch_send(const oracle_shape* sh, const uint8_t* x, const float* x_scale,
                           const int32_t* topk_idx, int32_t* counts, int32_t* send_off,
                           int32_t* send_pos, uint8_t* send_buf, int32_t* send_meta);
@@ -66,7 +75,8 @@ void oracle_expert(const oracle_shape* sh, int mode, const uint8_t* expert_x,
 
 /* Combine: rows back to their source slots, then the router-weighted sum.
  * mode 0: the sum in fp64, rounded once to bf16.
- * mode 1: an fp32 fused-multiply-add chain in slot order 0..R-1, then rounded to bf16. */
+ * mode 1: an fp32 fused-multiply-add chain in slot order 0..R-1, then rounded to bf16.
+ * Output rows of tokens t >= tokens[s] are not written. */
 void oracle_combine(const oracle_shape* sh, int mode, const uint16_t* expert_y,
                     const int32_t* expert_rpos, const int32_t* recv_off, const int32_t* send_off,
                     const int32_t* send_pos, const float* topk_w, uint16_t* cs_buf, uint16_t* cr_buf,

@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import bisect
 import decimal
+import math
 from fractions import Fraction
 
 import numpy as np
@@ -94,6 +95,21 @@ def e4m3_table():
     return out
 
 
+def e4m3_nearest(v) -> int:
+    """The e4m3 code nearest to the rational v by search over every finite code, ties to the
+    even code, magnitudes beyond 448 clamped to 448."""
+    tab = e4m3_table()
+    X = Fraction(float(v))
+    sign = 0x80 if (X < 0 or (X == 0 and math.copysign(1.0, float(v)) < 0)) else 0
+    a = min(abs(X), Fraction(448))
+    best = None
+    for code in range(0x7F):          # +0 .. 448
+        d = abs(tab[code] - a)
+        if best is None or d < best[0] or (d == best[0] and code % 2 == 0):
+            best = (d, code)
+    return sign | best[1] if best[1] else sign
+
+
 # ------------------------------------------------------------------ routing
 
 
@@ -120,20 +136,22 @@ def route(logits: np.ndarray, bias, R: int):
 # ------------------------------------------------------------------ dispatch / combine
 
 
-def dispatch(N, T, E, R, idx):
-    """Sort-based layout of every (source, token, slot) entry.
+def dispatch(N, T, E, R, idx, tokens=None):
+    """Sort-based layout of every (source, token, slot) entry.  With ``tokens``, source s has
+    only its first tokens[s] tokens (the other slots get send_pos -1).
 
     Returns a dict with counts, send_off, send_pos, the send order per source, the receive
     order per destination, the expert-major order per destination and rank_e per entry."""
     L = E // N
     idx = np.asarray(idx).reshape(N, T, R)
+    nt = [T] * N if tokens is None else [int(v) for v in tokens]
     counts = np.zeros((N, E), np.int64)
     send_off = np.zeros((N, N + 1), np.int64)
-    send_pos = np.zeros((N, T * R), np.int64)
+    send_pos = np.full((N, T * R), -1, np.int64)
     send_order = []
     rank_e = {}
     for s in range(N):
-        ent = [(int(idx[s, t, k]) // L, t, k, int(idx[s, t, k])) for t in range(T) for k in range(R)]
+        ent = [(int(idx[s, t, k]) // L, t, k, int(idx[s, t, k])) for t in range(nt[s]) for k in range(R)]
         for (_, t, k, e) in ent:
             counts[s, e] += 1
         # rank among earlier entries of this source with the same expert
@@ -147,7 +165,7 @@ def dispatch(N, T, E, R, idx):
             send_off[s, d + 1] = sum(1 for z in order if z[0] <= d)
     recv_order, expert_order = [], []
     for d in range(N):
-        ent = [(s, t, k, int(idx[s, t, k])) for s in range(N) for t in range(T) for k in range(R)
+        ent = [(s, t, k, int(idx[s, t, k])) for s in range(N) for t in range(nt[s]) for k in range(R)
                if int(idx[s, t, k]) // L == d]
         recv_order.append(sorted(ent, key=lambda z: (z[0], z[1], z[2])))
         expert_order.append(sorted(ent, key=lambda z: (z[3] - d * L, z[0], z[1], z[2])))

@@ -42,6 +42,19 @@ MUTANTS = {
     "bf16_truncates": ("double q = nearbyint(ldexp(a, -ulp_exp));", "double q = floor(ldexp(a, -ulp_exp));"),
     "bf16_one_bit_short": ("int ulp_exp = ex - 8;", "int ulp_exp = ex - 7;"),
     "e4m3_wrong_bias": ("ldexp((double)(8 + m), e - 10)", "ldexp((double)(8 + m), e - 9)"),
+    "quant_scale_fnuz_max": ("amax / 448.0f", "amax / 240.0f"),
+    "quant_ties_away_from_zero": ("double r = ldexp(nearbyint(ldexp(a, -sp)), sp);",
+                                  "double r = ldexp(round(ldexp(a, -sp)), sp);"),
+    "quant_truncates": ("double r = ldexp(nearbyint(ldexp(a, -sp)), sp);",
+                        "double r = ldexp(floor(ldexp(a, -sp)), sp);"),
+    "quant_no_saturation": ("if (r > 448.0) r = 448.0;", ""),
+    "quant_subnormal_spacing": ("? ex - 1 - 3 : -9;", "? ex - 1 - 3 : -10;"),
+    "quant_two_mantissa_bits": ("? ex - 1 - 3 : -9;", "? ex - 1 - 2 : -9;"),
+    "quant_amax_signed": ("float a = fabsf((float)oracle_bf16_to_double(xb[i]));",
+                          "float a = (float)oracle_bf16_to_double(xb[i]);"),
+    "send_counts_absent_tokens": ("for (long i = 0; i < (long)Ts * R; ++i) {",
+                                  "for (long i = 0; i < TR; ++i) {"),
+    "send_packs_absent_tokens": ("for (int t = 0; t < Ts; ++t) {", "for (int t = 0; t < T; ++t) {"),
 }
 
 

@@ -173,9 +173,13 @@ def token_row_bytes(inp, s, t, fp8):
 def test_dispatch_matches_brute_force(case, seed):
     N, T, H, E, R, fp8 = case
     res = run_small(*case, seed=seed)
+    check_layout_brute(res, case, brute.dispatch(N, T, E, R, res["idx"]))
+
+
+def check_layout_brute(res, case, bf):
+    N, T, H, E, R, fp8 = case
     inp = res["inp"]
     L = E // N
-    bf = brute.dispatch(N, T, E, R, res["idx"])
     assert np.array_equal(res["counts"], bf["counts"])
     assert np.array_equal(res["send_off"], bf["send_off"])
     assert np.array_equal(res["send_pos"], bf["send_pos"])
@@ -207,6 +211,133 @@ def test_dispatch_matches_brute_force(case, seed):
             else:
                 assert res["expert_x"][d, q].tobytes() == inp["x"][s, t].tobytes()
         assert len(eorder) <= N * T * min(R, L) <= B
+
+
+@pytest.mark.parametrize("case", [SMALL[1], SMALL[3], SMALL[6], SMALL[8]])
+def test_variable_tokens_brute(case):
+    # rank s dispatches only its first tokens[s] tokens: the layout is the brute-force layout
+    # of those tokens alone, absent slots get send_pos -1, and combine leaves absent rows alone
+    N, T, H, E, R, fp8 = case
+    rng = np.random.default_rng(21)
+    tokens = rng.integers(0, T + 1, N)
+    tokens[0], tokens[-1] = 0, T
+    inp = ms.make_inputs(N, T, H, E, R, fp8, "none", 4)
+    sh = oracle.shape(N, T, H, E, R, fp8, tokens=tokens)
+    idx, w = oracle.route(inp["logits"], inp["bias"], R)
+    idx = idx.reshape(N, T * R)
+    res = oracle.dispatch_send(sh, inp["x"], inp["x_scale"], idx)
+    res.update(oracle.net_dispatch(sh, res["send_off"], res["send_buf"], res["send_meta"]))
+    res.update(oracle.dispatch_recv(sh, res["counts"], res["recv_off"], res["recv_buf"],
+                                    res["recv_meta"]))
+    res["w"], res["idx"], res["inp"], res["sh"] = w, idx, inp, sh
+    bf = brute.dispatch(N, T, E, R, idx, tokens)
+    check_layout_brute(res, case, bf)
+    assert res["counts"].sum() == int(tokens.sum()) * R
+    _, out = _combine(res, 0, 0)
+    for s in range(N):
+        assert not out["out"][s, tokens[s]:].any(), "rows of absent tokens were written"
+        for t in range(tokens[s]):
+            y = _dequant_bf16(inp, s, t, fp8)
+            sw = sum(Fraction(float(w[s * T + t, k])) for k in range(R))
+            want = [brute.bf16_round_exact(brute.bf16_bits_to_fraction(int(v) & 0x7FFF) * sw *
+                                           (-1 if int(v) & 0x8000 else 1)) for v in y]
+            assert list(out["out"][s, t]) == want
+
+
+def test_all_tokens_present_equals_fixed_count():
+    case = SMALL[6]
+    N, T, H, E, R, fp8 = case
+    a = run_small(*case, seed=3)
+    sh = oracle.shape(N, T, H, E, R, fp8, tokens=np.full(N, T))
+    b = oracle.dispatch_send(sh, a["inp"]["x"], a["inp"]["x_scale"], a["idx"])
+    for k in ("counts", "send_off", "send_pos", "send_buf", "send_meta"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+# ------------------------------------------------------------------ fp8 block quantisation
+
+
+def _e4m3_probe_values():
+    """fp32 values at every e4m3 value, at the midpoints between neighbours and one fp32 step
+    either side of each midpoint, beyond 448, and random over the range; both signs."""
+    tab = brute.e4m3_table()
+    pos = sorted(float(tab[c]) for c in range(0x7F))
+    vals = []
+    for a, b in zip(pos, pos[1:] + [480.0]):
+        m = np.float32((a + b) / 2)   # exact: neighbours have at most 4 significant bits
+        vals += [a, m, np.nextafter(m, np.float32(0)), np.nextafter(m, np.float32(1e9))]
+    vals += [470.0, 1e6]
+    rng = np.random.default_rng(5)
+    vals += list(rng.uniform(0, 448, 2000))
+    vals += list(np.exp(rng.uniform(np.log(1e-5), np.log(448), 2000)))
+    v = np.array(vals, np.float32)
+    return np.concatenate([v, -v])
+
+
+def test_e4m3_encode_matches_torch():
+    # torch's float8_e4m3fn conversion is round-to-nearest-even (it has no saturation: clamp first)
+    v = _e4m3_probe_values()
+    mine = np.array([oracle.e4m3_from_float_sat(x) for x in v], np.uint8)
+    ref = torch.from_numpy(np.clip(v, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    bad = np.nonzero(mine != ref)[0]
+    assert bad.size == 0, [(float(v[i]), int(mine[i]), int(ref[i])) for i in bad[:5]]
+
+
+def test_e4m3_encode_brute_nearest():
+    v = _e4m3_probe_values()
+    pick = np.concatenate([np.arange(0, 4 * 127 + 2), np.arange(4 * 127 + 2, v.size, 37)])
+    for i in pick:
+        assert oracle.e4m3_from_float_sat(v[i]) == brute.e4m3_nearest(v[i]), float(v[i])
+
+
+def _spacing_e4m3(a: Fraction) -> Fraction:
+    """Distance between adjacent e4m3 values around the magnitude a (<= 448)."""
+    if a < Fraction(1, 64):
+        return Fraction(1, 512)
+    e = 0
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    while Fraction(2) ** e > a:
+        e -= 1
+    return Fraction(2) ** (e - 3)
+
+
+@pytest.mark.parametrize("scale_exp", [0, -24, 30])
+def test_quantize_blocks(scale_exp):
+    rng = np.random.default_rng(100 + scale_exp)
+    xf = (rng.standard_normal((6, 512)) * 2.0 ** scale_exp).astype(np.float32)
+    xf[1, 128:256] = 0.0                                   # an all-zero block
+    xf[2, 256:384] = -np.abs(xf[2, 256:384])               # largest magnitude negative
+    xf[3, 0:128] = xf[3, 0:128] * (2.0 ** -12)             # subnormal-range codes in a block
+    xf[3, 5] = 3.0 * 2.0 ** scale_exp
+    xb = ms.to_bf16_bits(xf)
+    xv = ms.bf16_bits_to_f32(xb)
+    q, sc = oracle.quantize_e4m3(xb)
+    tab = brute.e4m3_table()
+    for n in range(6):
+        for b in range(4):
+            blk = xv[n, b * 128:(b + 1) * 128]
+            qb = q[n, b * 128:(b + 1) * 128]
+            amax = float(np.abs(blk).max())
+            if amax == 0.0:
+                assert sc[n, b] == 1.0 and not qb.any()
+                continue
+            # the scale is amax / 448 to within one fp32 rounding
+            assert abs(Fraction(float(sc[n, b])) * 448 - Fraction(amax)) <= Fraction(amax) / 2 ** 23
+            # the largest magnitude lands on +-448
+            i = int(np.argmax(np.abs(blk)))
+            assert qb[i] & 0x7F == 0x7E and (qb[i] >> 7) == int(blk[i] < 0)
+            # every code is within half an e4m3 step of x / scale (plus the quotient's rounding)
+            S = Fraction(float(sc[n, b]))
+            for h in range(128):
+                x = Fraction(float(blk[h]))
+                v = x / S
+                err = abs(tab[int(qb[h])] - v)
+                assert err <= _spacing_e4m3(min(abs(v), Fraction(448))) / 2 + abs(v) / 2 ** 23, (n, b, h)
+                assert (int(qb[h]) >> 7) == int(blk[h] < 0) or qb[h] & 0x7F == 0
+    # an independent implementation (numpy division and torch's conversion) agrees bit for bit
+    q2, sc2 = ms.quantize_e4m3(xv)
+    assert np.array_equal(sc, sc2) and np.array_equal(q, q2)
 
 
 def test_dispatch_invariants_at_scale():
