@@ -22,16 +22,21 @@ sys.path.insert(0, ROOT)
 METRIC = "dispatch+combine µs/layer and effective HBM GB/s (fraction of MI355X peak)"
 PEAK_HBM_GBS = 8000.0
 HEADLINE = "deepseek_v3_decode"
-EXTRA = ["deepseek_v3_decode_fp8", "kimi_k2_worst"]
+EXTRA = ["deepseek_v3_decode_fp8", "kimi_k2_worst", "deepseek_v3_decode_fp8q",
+         "deepseek_v3_decode_ragged"]
 
 
 def alg_bytes(c) -> dict:
-    """Compulsory bytes each ABI call reads and writes (every routed row is valid)."""
+    """Compulsory bytes each ABI call reads and writes (every routed row is valid).  With token
+    counts per rank only the present tokens count: absent ones are neither read nor written."""
+    import moe_synth as ms
     N, T, H, E, R, L = c.N, c.T, c.H, c.E, c.R, c.L
-    NT, M = N * T, N * T * R
-    xrow = (H + 4 * (H // 128)) if c.fp8 else 2 * H   # a token's payload (+ scales)
-    P = xrow                                          # one dispatched row
-    Pc = 2 * H                                        # one combine row (bf16)
+    tok = ms.config_tokens(c)
+    NT = N * T if tok is None else int(tok.sum())
+    M = NT * R
+    P = (H + 4 * (H // 128)) if c.rows_fp8 else 2 * H    # one dispatched row (codes + scales)
+    xrow = 2 * H if c.quant else P                      # one input token (bf16, or codes + scales)
+    Pc = 2 * H                                          # one combine row (bf16)
     bias = E * 4 if c.bias != "none" else 0
     b = {}
     b["route"] = NT * E * 4 + bias + M * 8
@@ -56,7 +61,10 @@ def run_workload(name, steps, warmup, check=True):
 
     c = ms.CONFIGS[name]
     inp = ms.config_inputs(c)
-    b = moe.alloc_buffers(c.N, c.T, c.H, c.E, c.R, c.fp8)
+    tok = ms.config_tokens(c)
+    b = moe.alloc_buffers(c.N, c.T, c.H, c.E, c.R, c.fp8, quant=c.quant, tokens=tok is not None)
+    if tok is not None:
+        b.tokens.copy_(torch.from_numpy(tok))
     b.logits.copy_(torch.from_numpy(inp["logits"]))
     use_bias = inp["bias"] is not None
     if use_bias:
@@ -67,7 +75,7 @@ def run_workload(name, steps, warmup, check=True):
         b.x_scale.copy_(torch.from_numpy(inp["x_scale"]))
     stream = torch.cuda.current_stream()
     sh = b.shape
-    y = b.expert_y if c.fp8 else b.expert_x   # identity expert: bf16 combine reads expert_x
+    y = b.expert_y if c.rows_fp8 else b.expert_x   # identity expert: bf16 combine reads expert_x
 
     names = ["route", "dispatch_send", "net_dispatch", "dispatch_recv", "stub", "combine"]
 
@@ -90,7 +98,7 @@ def run_workload(name, steps, warmup, check=True):
                               b.expert_scale, b.expert_cnt, b.expert_off, b.expert_src,
                               b.expert_rpos, b.workspace, st)
         rec(4)
-        if c.fp8:
+        if c.rows_fp8:
             moe.moe_expert_stub(sh, 0, b.expert_x, b.expert_scale, b.expert_off, b.expert_y, st)
         rec(5)
         moe.moe_combine(sh, y, b.expert_rpos, b.recv_off, b.send_off, b.send_pos, b.topk_w,
@@ -153,9 +161,31 @@ def run_workload(name, steps, warmup, check=True):
 
 def closed_form_check(b, c) -> str:
     """Identity experts: out == bf16(y * sum_k w_k) up to 1 bf16 ulp for every token (y the
-    dispatched value), and each rank's counts sum to T*R.  A property check at full size; the
-    element-wise oracle comparison lives in the GPU parity tests."""
+    dispatched value), and each rank's counts sum to T_s*R.  A property check at full size; the
+    element-wise oracle comparison lives in the GPU parity tests.  Tokens quantised by the send
+    pack: out is within e4m3 rounding of x * sum_k w_k instead."""
     import torch
+
+    import moe_synth as ms
+    tok = ms.config_tokens(c)
+    nt = torch.full((c.N,), c.T, dtype=torch.int64) if tok is None else torch.from_numpy(tok).long()
+    present = (torch.arange(c.T)[None, :] < nt[:, None]).to(b.out.device)     # [N][T]
+    counts_ok = bool((b.counts.sum(1).cpu() == nt * c.R).all().item())
+    if c.quant:
+        # |e4m3(v) - v| <= 2^-4 |v| (3 mantissa bits) above 2^-6, <= 2^-10 below, in units of
+        # the block scale; then one bf16 rounding of the weighted sum (2^-8 relative)
+        xv = b.x.view(torch.bfloat16).float()
+        sc = xv.abs().view(c.N, c.T, c.H // 128, 128).amax(-1) / 448.0
+        sc = sc.repeat_interleave(128, dim=2)
+        sw = b.topk_w.float().sum(1).view(c.N, c.T, 1)
+        got = b.out.view(torch.bfloat16).float()
+        err = (got - xv * sw).abs()
+        bound = (xv.abs() * (2.0 ** -4) + sc * (2.0 ** -10)) * sw * 1.01 + got.abs() * 2.0 ** -8
+        bad = int(((err > bound) & present[..., None]).sum().item())
+        if bad or not counts_ok:
+            raise RuntimeError(f"closed-form check failed: {bad} values outside the e4m3 bound, "
+                               f"counts ok {counts_ok}")
+        return "ok (every value within e4m3 + bf16 rounding of x * sum w; counts sum to T_s*R)"
     sw = b.topk_w.double().sum(1).view(c.N, c.T, 1)
     if c.fp8:
         xv = b.x.view(torch.float8_e4m3fn).double() * b.x_scale.double().repeat_interleave(128, dim=2)
@@ -167,11 +197,10 @@ def closed_form_check(b, c) -> str:
     a = want.view(torch.int16).int()
     g = got.view(torch.int16).int()
     key = lambda u: torch.where(u < 0, -(u & 0x7FFF), u & 0x7FFF)  # noqa: E731
-    ulp = (key(a) - key(g)).abs().max().item()
-    counts_ok = bool((b.counts.sum(1) == c.T * c.R).all().item())
+    ulp = ((key(a) - key(g)).abs() * present[..., None]).max().item()
     if ulp > 2 or not counts_ok:  # the torch reference itself rounds twice (fp64->fp32->bf16)
         raise RuntimeError(f"closed-form check failed: max {ulp} bf16 ulp, counts ok {counts_ok}")
-    return f"ok (max {ulp} bf16 ulp vs identity closed form; counts sum to T*R)"
+    return f"ok (max {ulp} bf16 ulp vs identity closed form; counts sum to T_s*R)"
 
 
 def traffic_record(kernel, workload):
@@ -216,16 +245,20 @@ def cpu_baseline(name, budget_s=25.0) -> dict:
     import oracle
     c = ms.CONFIGS[name]
     inp = ms.config_inputs(c)
+    tok = ms.config_tokens(c)
     ab = alg_bytes(c)
     times = []
     t_start = time.perf_counter()
     while True:
         t0 = time.perf_counter()
-        sh = oracle.shape(c.N, c.T, c.H, c.E, c.R, c.fp8)
+        x, xs = inp["x"], inp["x_scale"]
+        if c.quant:
+            x, xs = oracle.quantize_e4m3(x)
+        sh = oracle.shape(c.N, c.T, c.H, c.E, c.R, c.rows_fp8, tokens=tok)
         idx, w = oracle.route(inp["logits"], inp["bias"], c.R)
-        r = oracle.dispatch_send(sh, inp["x"], inp["x_scale"], idx.reshape(c.N, -1))
-        sh = oracle.packed_shape(c.N, c.T, c.H, c.E, c.R, c.fp8,
-                                 np.diff(r["send_off"], axis=1).sum(axis=0))
+        r = oracle.dispatch_send(sh, x, xs, idx.reshape(c.N, -1))
+        sh = oracle.packed_shape(c.N, c.T, c.H, c.E, c.R, c.rows_fp8,
+                                 np.diff(r["send_off"], axis=1).sum(axis=0), tok)
         r.update(oracle.net_dispatch(sh, r["send_off"], r["send_buf"], r["send_meta"]))
         r.update(oracle.dispatch_recv(sh, r["counts"], r["recv_off"], r["recv_buf"], r["recv_meta"]))
         t1 = time.perf_counter()

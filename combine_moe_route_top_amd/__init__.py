@@ -31,14 +31,15 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP, MOE_EBADIDX = 0, -1, -2, -3, -5
-MOE_BF16, MOE_FP8_E4M3 = 0, 1
+MOE_BF16, MOE_FP8_E4M3, MOE_BF16_TO_FP8 = 0, 1, 2
 
 
 class moe_shape(ctypes.Structure):
     _fields_ = [("N", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
                 ("E", ctypes.c_int32), ("R", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("rank_begin", ctypes.c_int32), ("rank_count", ctypes.c_int32),
-                ("capacity", ctypes.c_int64), ("status", ctypes.c_void_p)]
+                ("capacity", ctypes.c_int64), ("status", ctypes.c_void_p),
+                ("tokens", ctypes.c_void_p)]
 
 
 _SIZE_FIELDS = ["capacity", "row_bytes", "logits", "bias", "topk_idx", "topk_w", "x", "x_scale",
@@ -111,15 +112,18 @@ def _check(name, rc):
 
 
 def make_shape(N, T, H, E, R, fp8=False, capacity=0, status=None, rank_begin=0,
-               rank_count=0) -> moe_shape:
-    return moe_shape(N, T, H, E, R, MOE_FP8_E4M3 if fp8 else MOE_BF16, rank_begin, rank_count,
-                     capacity, _ptr(status))
+               rank_count=0, quant=False, tokens=None) -> moe_shape:
+    """quant: bf16 tokens quantised to e4m3 rows by the send pack (MOE_BF16_TO_FP8);
+    tokens: a device int32[N] tensor of per-rank token counts, or None."""
+    dtype = MOE_BF16_TO_FP8 if quant else (MOE_FP8_E4M3 if fp8 else MOE_BF16)
+    return moe_shape(N, T, H, E, R, dtype, rank_begin, rank_count, capacity, _ptr(status),
+                     _ptr(tokens))
 
 
 def for_ranks(shape: moe_shape, rank_begin: int, rank_count: int) -> moe_shape:
     """The same shape restricted to ranks [rank_begin, rank_begin + rank_count)."""
     return moe_shape(shape.N, shape.T, shape.H, shape.E, shape.R, shape.dtype, rank_begin,
-                     rank_count, shape.capacity, shape.status)
+                     rank_count, shape.capacity, shape.status, shape.tokens)
 
 
 def moe_sizes(shape: moe_shape) -> dict:
@@ -201,9 +205,13 @@ class Buffers:
             raise AttributeError(k) from ex
 
 
-def alloc_buffers(N, T, H, E, R, fp8=False, capacity=0, device="cuda", with_status=True) -> Buffers:
-    """Allocate every buffer of the path for one shape (torch.empty; contents undefined)."""
-    shape = make_shape(N, T, H, E, R, fp8, capacity)
+def alloc_buffers(N, T, H, E, R, fp8=False, capacity=0, device="cuda", with_status=True,
+                  quant=False, tokens=False) -> Buffers:
+    """Allocate every buffer of the path for one shape (torch.empty; contents undefined).
+    quant: bf16 tokens, e4m3 rows made by the send pack.  tokens: also allocate the per-rank
+    token counts (int32[N], filled with T) and point the shape at them."""
+    fp8 = fp8 or quant
+    shape = make_shape(N, T, H, E, R, fp8, capacity, quant=quant)
     sz = moe_sizes(shape)
     B, P = sz["capacity"], sz["row_bytes"]
     L = E // N
@@ -215,8 +223,8 @@ def alloc_buffers(N, T, H, E, R, fp8=False, capacity=0, device="cuda", with_stat
         bias=torch.zeros((E,), dtype=f32, device=dev),
         topk_idx=torch.empty((N, T * R), dtype=i32, device=dev),
         topk_w=torch.empty((N * T, R), dtype=f32, device=dev),
-        x=torch.empty((N, T, H), dtype=xdt, device=dev),
-        x_scale=torch.empty((N, T, H // 128), dtype=f32, device=dev) if fp8 else None,
+        x=torch.empty((N, T, H), dtype=i16 if quant else xdt, device=dev),
+        x_scale=torch.empty((N, T, H // 128), dtype=f32, device=dev) if fp8 and not quant else None,
         counts=torch.empty((N, E), dtype=i32, device=dev),
         send_off=torch.empty((N, N + 1), dtype=i32, device=dev),
         send_pos=torch.empty((N, T * R), dtype=i32, device=dev),
@@ -237,9 +245,12 @@ def alloc_buffers(N, T, H, E, R, fp8=False, capacity=0, device="cuda", with_stat
         out=torch.empty((N, T, H), dtype=i16, device=dev),
         workspace=torch.empty((max(sz["workspace"], 16),), dtype=u8, device=dev),
         status=torch.zeros((1,), dtype=i32, device=dev) if with_status else None,
+        tokens=torch.full((N,), T, dtype=i32, device=dev) if tokens else None,
     )
     if with_status:
         shape.status = t["status"].data_ptr()
+    if tokens:
+        shape.tokens = t["tokens"].data_ptr()
     return Buffers(shape, sz, t)
 
 

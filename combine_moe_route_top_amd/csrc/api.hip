@@ -39,9 +39,10 @@ int make_dims(const moe_shape* sh, Dims* D) {
     const long long N = sh->N, T = sh->T, H = sh->H, E = sh->E, R = sh->R;
     if (N < 1 || T < 1 || H < 1 || E < 1 || R < 1) return MOE_EINVAL;
     if (E % N != 0 || R > E) return MOE_EINVAL;
-    if (sh->dtype != MOE_BF16 && sh->dtype != MOE_FP8_E4M3) return MOE_EINVAL;
+    if (sh->dtype != MOE_BF16 && sh->dtype != MOE_FP8_E4M3 && sh->dtype != MOE_BF16_TO_FP8)
+        return MOE_EINVAL;
     if (N > kMaxN || E > kMaxE || R > kMaxR) return MOE_EUNSUPPORTED;
-    const bool fp8 = sh->dtype == MOE_FP8_E4M3;
+    const bool fp8 = sh->dtype != MOE_BF16;  // e4m3 rows, given or made by the send pack
     if (!fp8 && H % 8 != 0) return MOE_EUNSUPPORTED;   // 16-byte rows
     if (fp8 && H % 512 != 0) return MOE_EUNSUPPORTED;  // 16-byte rows of codes and of scales
     const long long L = E / N;
@@ -60,6 +61,9 @@ int make_dims(const moe_shape* sh, Dims* D) {
     D->R = (int)R;
     D->L = (int)L;
     D->fp8 = fp8;
+    D->quant = sh->dtype == MOE_BF16_TO_FP8;
+    if (sh->tokens && reinterpret_cast<uintptr_t>(sh->tokens) % 4 != 0) return MOE_EINVAL;
+    D->tok = sh->tokens;
     D->TR = (int)TR;
     D->B = B;
     D->P = fp8 ? (int)(H + H / 32) : (int)(2 * H);
@@ -104,15 +108,15 @@ int moe_sizes(const moe_shape* shape, moe_sizes_t* out) {
     if (!out) return MOE_EINVAL;
     const int64_t N = D.N, T = D.T, H = D.H, E = D.E, R = D.R, L = D.L, B = D.B, P = D.P;
     const int64_t NT = N * T, M = N * T * R;
-    const int64_t xb = D.fp8 ? 1 : 2;
+    const int64_t xb = D.fp8 ? 1 : 2;  // bytes per value of expert_x
     out->capacity = B;
     out->row_bytes = P;
     out->logits = NT * E * 4;
     out->bias = E * 4;
     out->topk_idx = M * 4;
     out->topk_w = M * 4;
-    out->x = NT * H * xb;
-    out->x_scale = D.fp8 ? NT * (H / 128) * 4 : 0;
+    out->x = NT * H * (D.quant ? 2 : xb);
+    out->x_scale = D.fp8 && !D.quant ? NT * (H / 128) * 4 : 0;
     out->counts = N * E * 4;
     out->send_off = N * (N + 1) * 4;
     out->send_pos = M * 4;
@@ -154,7 +158,8 @@ int moe_dispatch_send(const moe_shape* shape, const void* x, const float* x_scal
     int rc = make_dims(shape, &D);
     if (rc) return rc;
     if (!aligned(x, 16) || !aligned(send_buf, 16) || !aligned(send_meta, 8)) return MOE_EINVAL;
-    if (D.fp8 && !aligned(x_scale, 16)) return MOE_EINVAL;
+    if (D.fp8 && !D.quant && !aligned(x_scale, 16)) return MOE_EINVAL;
+    if (D.quant && x_scale) return MOE_EINVAL;  // the scales are made here
     if (!aligned(topk_idx, 4) || !aligned(counts, 4) || !aligned(send_off, 4) || !aligned(send_pos, 4))
         return MOE_EINVAL;
     if (moe::send_workspace_bytes(D) > 0 && !aligned(workspace, 4)) return MOE_EINVAL;

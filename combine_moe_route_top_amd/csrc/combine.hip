@@ -203,6 +203,7 @@ __global__ __launch_bounds__(kBlock) void k_wsum(Dims D, const uint16_t* __restr
     const int lane = lane_id();
     const int R = D.R;
     const long s = tok / D.T;
+    if (tok - s * D.T >= rank_tokens(D, D.rb + s)) return;  // absent token: its row is not written
     const int my_pos = lane < R ? send_pos[tok * R + lane] : -1;
     const float my_w = lane < R ? topk_w[tok * R + lane] : 0.0f;
     const u32x4* rank_rows = reinterpret_cast<const u32x4*>(cr_buf + (size_t)s * D.TR * D.H);

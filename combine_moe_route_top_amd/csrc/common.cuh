@@ -16,7 +16,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // Everything a kernel needs to know about the problem, passed by value.
 struct Dims {
     int N, T, H, E, R, L;
-    int fp8;
+    int fp8;           // e4m3 payload rows (codes, then fp32 block scales)
+    int quant;         // the send pack makes those rows from bf16 tokens
+    const int32_t* tok;  // device int32[N]: tokens each rank dispatches, or NULL (T for all)
     int TR;            // T * R: rows each rank sends
     long long B;       // receive-side rows per rank
     int P;             // bytes of one dispatched row
@@ -61,6 +63,18 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 
 __device__ __forceinline__ void set_status(int32_t* status, int code) {
     if (status) atomicCAS(status, 0, code);
+}
+
+// Tokens rank s (a global rank) dispatches: T, or the caller's per-rank count; a count outside
+// [0, T] flags MOE_EINVAL and counts as 0.
+__device__ __forceinline__ int rank_tokens(const Dims& D, long s) {
+    if (!D.tok) return D.T;
+    const int v = D.tok[s];
+    if (v < 0 || v > D.T) {
+        set_status(D.status, MOE_EINVAL);
+        return 0;
+    }
+    return v;
 }
 
 // Exclusive scan of n ints (n <= a few thousand) done by one wave, in place from `in` to

@@ -72,7 +72,7 @@ __global__ __launch_bounds__(1024) void k_send_hist(Dims D, const int32_t* __res
     const long c0 = (long)c * blockDim.x;
     const long n = stage_chunk(idx_s, chunk, c0, D.TR);
     const long i = c0 + threadIdx.x;
-    if (i < D.TR) {
+    if (i < (long)rank_tokens(D, D.rb + s) * D.R) {  // slots of present tokens
         int e;
         if (slot_valid(idx_s, chunk, c0, n, i, D.R, D.E, e)) atomicAdd(&hist[e], 1);
     }
@@ -109,7 +109,7 @@ __global__ __launch_bounds__(1024) void k_send_rank(Dims D, const int32_t* __res
     const long i = c0 + threadIdx.x;
     int e = -1;
     bool valid = false;
-    if (i < TR) {
+    if (i < (long)rank_tokens(D, D.rb + s) * D.R) {  // slots of absent tokens stay invalid
         valid = slot_valid(idx_s, chunk, c0, n, i, D.R, E, e);
         if (!valid) set_status(D.status, MOE_EBADIDX);
     }
@@ -191,6 +191,7 @@ __global__ __launch_bounds__(kBlock) void k_send_pack(Dims D, int WPT, const uin
     if (tok >= (long)D.rc * D.T) return;
     const int lane = lane_id();
     const long s = tok / D.T;
+    if (tok - s * D.T >= rank_tokens(D, D.rb + s)) return;  // absent token
     const int R = D.R;
     const int mypos = lane < R ? send_pos[tok * R + lane] : -1;
     const long xrow = D.fp8 ? D.H : 2L * D.H;
@@ -215,6 +216,89 @@ __global__ __launch_bounds__(kBlock) void k_send_pack(Dims D, int WPT, const uin
                 const int c = c0 + u * stride + lane;
                 if (c < n16) dst[c] = v[u];
             }
+        }
+    }
+}
+
+// Nearest OCP e4m3 code (exponent bias 7, 3 mantissa bits, largest finite 448) to v, ties to
+// the even code, magnitudes above 448 clamped to 448.  Below 2^-6 the codes are multiples of
+// 2^-9 (v * 512 is exact; rint rounds half to even).  Above, the fp32 mantissa is rounded to
+// 3 bits in place (adding 0x7FFFF plus the kept last bit carries exactly when the dropped bits
+// exceed half, or equal half with an odd kept bit) and the exponent rebased from 127 to 7.
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float v) {
+    const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+    const float a = fminf(fabsf(v), 448.0f);
+    uint32_t code;
+    if (a < 0.015625f) {
+        code = (uint32_t)__builtin_rintf(a * 512.0f);
+    } else {
+        uint32_t b = __float_as_uint(a);
+        b += 0x7FFFFu + ((b >> 20) & 1u);
+        code = (b >> 20) - (120u << 3);
+    }
+    return sign | code;
+}
+
+// Send pack with on-the-fly block quantisation ([DSK] Implementation, Quantization: activation
+// scales are found per 128-value vector from its largest magnitude): bf16 tokens become e4m3
+// codes and one fp32 scale per 128 values, scale = amax / 448 (1 for an all-zero block),
+// code = e4m3(x / scale) with an IEEE fp32 division.  WPT waves per token; a wave takes 1024
+// values per pass, 16 per lane (8 lanes per 128-value block, whose amax is reduced over them),
+// writes 16 code bytes per lane and, from lanes 0 and 1, the pass's 8 scales (32 bytes) into
+// each of the token's send rows.
+__global__ __launch_bounds__(kBlock) void k_send_pack_q(Dims D, int WPT, const uint16_t* __restrict__ x,
+                                                        const int32_t* __restrict__ send_pos,
+                                                        uint8_t* __restrict__ send_buf) {
+    const long gw = (long)blockIdx.x * kWavesPerBlock + wave_id();
+    const long tok = gw / WPT;  // within the call's ranks
+    const int part = (int)(gw - tok * WPT);
+    if (tok >= (long)D.rc * D.T) return;
+    const long s = tok / D.T;
+    if (tok - s * D.T >= rank_tokens(D, D.rb + s)) return;  // absent token
+    const int lane = lane_id();
+    const int R = D.R, H = D.H;
+    const int mypos = lane < R ? send_pos[tok * R + lane] : -1;
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + tok * H);
+    uint8_t* rank_base = send_buf + (size_t)s * D.TR * D.P;
+    for (int v0 = part * 1024; v0 < H; v0 += WPT * 1024) {
+        const int v = v0 + lane * 16;  // this lane's first value
+        const bool in = v < H;
+        u32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
+        if (in) {
+            a = src[v / 8];
+            b = src[v / 8 + 1];
+        }
+        float f[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = bf16_to_f32(a[i] & 0xFFFFu);
+            f[2 * i + 1] = bf16_to_f32(a[i] >> 16);
+            f[8 + 2 * i] = bf16_to_f32(b[i] & 0xFFFFu);
+            f[8 + 2 * i + 1] = bf16_to_f32(b[i] >> 16);
+        }
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
+        amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+        amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+        amax = fmaxf(amax, __shfl_xor(amax, 4, kWave));
+        const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+        u32x4 q;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            q[i] = e4m3_rne_sat(f[4 * i] / sc) | (e4m3_rne_sat(f[4 * i + 1] / sc) << 8) |
+                   (e4m3_rne_sat(f[4 * i + 2] / sc) << 16) | (e4m3_rne_sat(f[4 * i + 3] / sc) << 24);
+        // lane 0 gathers the scales of blocks 0..3 of this pass, lane 1 those of blocks 4..7
+        u32x4 sv;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sv[j] = __float_as_uint(__shfl(sc, 8 * (4 * (lane & 1) + j), kWave));
+        const bool sc_lane = lane < 2 && v0 + 512 * lane < H;
+        for (int k = 0; k < R; ++k) {
+            const int pos = readlane(mypos, k);
+            if (pos < 0 || pos >= D.TR) continue;
+            uint8_t* row = rank_base + (size_t)pos * D.P;
+            if (in) *reinterpret_cast<u32x4*>(row + v) = q;
+            if (sc_lane) *reinterpret_cast<u32x4*>(row + H + 4 * (v0 / 128 + 4 * lane)) = sv;
         }
     }
 }
@@ -416,7 +500,7 @@ hipError_t launch_dispatch_send(const Dims& D, const void* x, const float* x_sca
     int32_t* chunk_cnt = static_cast<int32_t*>(workspace);
     // the call's ranks [rb, rb + rc): per-rank arrays start at rank rb
     const long rb = D.rb;
-    const long xrow = D.fp8 ? D.H : 2L * D.H;
+    const long xrow = D.fp8 && !D.quant ? D.H : 2L * D.H;  // bytes of one input token
     x = static_cast<const uint8_t*>(x) + rb * D.T * xrow;
     if (x_scale) x_scale += rb * D.T * D.nsc;
     topk_idx += rb * D.TR;
@@ -432,6 +516,15 @@ hipError_t launch_dispatch_send(const Dims& D, const void* x, const float* x_sca
     hipLaunchKernelGGL(k_send_rank, dim3(C, D.rc), dim3(CH), lds, st, D, topk_idx,
                        (const int32_t*)chunk_cnt, C, counts, send_off, send_pos, send_meta);
     const long ntok = (long)D.rc * D.T;
+    if (D.quant) {
+        // up to one wave per 1024 values when there are fewer than 4096 tokens
+        int wpt = 1;
+        while (wpt < 8 && ntok * wpt < 4096 && 1024L * wpt * 2 <= D.H) wpt *= 2;
+        const long waves = ntok * wpt;
+        hipLaunchKernelGGL(k_send_pack_q, dim3((waves + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock),
+                           0, st, D, wpt, (const uint16_t*)x, (const int32_t*)send_pos, (uint8_t*)send_buf);
+        return hipGetLastError();
+    }
     // up to 8 waves per token when there are fewer than 4096 tokens to keep the chip busy
     int wpt = 1;
     while (wpt < 8 && ntok * wpt < 4096 && (long)kWave * wpt * 2 <= D.P16) wpt *= 2;

@@ -61,14 +61,18 @@ template <int G, int VPL>
 __global__ __launch_bounds__(kBlock) void k_route(const float* __restrict__ logits,
                                                   const float* __restrict__ bias,
                                                   int32_t* __restrict__ topk_idx,
-                                                  float* __restrict__ topk_w, int ntok, int E,
-                                                  int R) {
+                                                  float* __restrict__ topk_w, Dims D) {
     constexpr int TPW = kWave / G;  // tokens per wave
+    const int E = D.E, R = D.R;
     const int lane = lane_id();
     const int grp = lane / G, gl = lane % G;
-    const long tok = ((long)blockIdx.x * kWavesPerBlock + wave_id()) * TPW + grp;
-    // no early exit: every lane takes part in the DPP rotations and lane swaps
-    const bool active = tok < ntok;
+    const long tok = ((long)blockIdx.x * kWavesPerBlock + wave_id()) * TPW + grp;  // call's ranks
+    const long s = tok / D.T;
+    // tokens past their rank's count take no part
+    const bool active = tok < (long)D.rc * D.T && tok - s * D.T < rank_tokens(D, D.rb + s);
+    // a wave with no token leaves; otherwise every lane takes part in the DPP rotations and
+    // lane swaps
+    if (ballot(active) == 0) return;
     const float* row = logits + (active ? tok : 0) * E;
 
     // ordered scores; 0 marks "taken" or "no expert" (every finite score maps above 0).  Within a
@@ -125,17 +129,17 @@ __global__ __launch_bounds__(kBlock) void k_route(const float* __restrict__ logi
 
 template <int G>
 static void launch_g(int vpl, dim3 grid, hipStream_t st, const float* logits, const float* bias,
-                     int32_t* topk_idx, float* topk_w, int ntok, int E, int R) {
+                     int32_t* topk_idx, float* topk_w, const Dims& D) {
     if (vpl <= 1)
-        hipLaunchKernelGGL((k_route<G, 1>), grid, dim3(kBlock), 0, st, logits, bias, topk_idx, topk_w, ntok, E, R);
+        hipLaunchKernelGGL((k_route<G, 1>), grid, dim3(kBlock), 0, st, logits, bias, topk_idx, topk_w, D);
     else if (vpl <= 2)
-        hipLaunchKernelGGL((k_route<G, 2>), grid, dim3(kBlock), 0, st, logits, bias, topk_idx, topk_w, ntok, E, R);
+        hipLaunchKernelGGL((k_route<G, 2>), grid, dim3(kBlock), 0, st, logits, bias, topk_idx, topk_w, D);
     else if (vpl <= 4)
-        hipLaunchKernelGGL((k_route<G, 4>), grid, dim3(kBlock), 0, st, logits, bias, topk_idx, topk_w, ntok, E, R);
+        hipLaunchKernelGGL((k_route<G, 4>), grid, dim3(kBlock), 0, st, logits, bias, topk_idx, topk_w, D);
     else if (vpl <= 8)
-        hipLaunchKernelGGL((k_route<G, 8>), grid, dim3(kBlock), 0, st, logits, bias, topk_idx, topk_w, ntok, E, R);
+        hipLaunchKernelGGL((k_route<G, 8>), grid, dim3(kBlock), 0, st, logits, bias, topk_idx, topk_w, D);
     else
-        hipLaunchKernelGGL((k_route<G, 16>), grid, dim3(kBlock), 0, st, logits, bias, topk_idx, topk_w, ntok, E, R);
+        hipLaunchKernelGGL((k_route<G, 16>), grid, dim3(kBlock), 0, st, logits, bias, topk_idx, topk_w, D);
 }
 
 hipError_t launch_route(const Dims& D, const float* logits, const float* bias, int32_t* topk_idx,
@@ -152,9 +156,9 @@ hipError_t launch_route(const Dims& D, const float* logits, const float* bias, i
     const int vpl = (D.E + G - 1) / G;
     const long waves = ((long)ntok * G + kWave - 1) / kWave;
     const dim3 grid((waves + kWavesPerBlock - 1) / kWavesPerBlock);
-    if (G == 16) launch_g<16>(vpl, grid, st, logits, bias, topk_idx, topk_w, ntok, D.E, D.R);
-    else if (G == 32) launch_g<32>(vpl, grid, st, logits, bias, topk_idx, topk_w, ntok, D.E, D.R);
-    else launch_g<64>(vpl, grid, st, logits, bias, topk_idx, topk_w, ntok, D.E, D.R);
+    if (G == 16) launch_g<16>(vpl, grid, st, logits, bias, topk_idx, topk_w, D);
+    else if (G == 32) launch_g<32>(vpl, grid, st, logits, bias, topk_idx, topk_w, D);
+    else launch_g<64>(vpl, grid, st, logits, bias, topk_idx, topk_w, D);
     return hipGetLastError();
 }
 

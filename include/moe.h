@@ -38,11 +38,12 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef enum {
     MOE_OK = 0,
-    MOE_EINVAL = -1,        /* bad shape, null or misaligned pointer */
+    MOE_EINVAL = -1,        /* bad shape, null or misaligned pointer; (device status word) a
+                               token count outside [0, T] */
     MOE_EUNSUPPORTED = -2,  /* valid but outside what these kernels implement */
     MOE_EHIP = -3,          /* a HIP launch failed */
     MOE_EBADIDX = -5        /* (device status word) bad expert id in topk_idx */
@@ -50,7 +51,13 @@ typedef enum {
 
 typedef enum {
     MOE_BF16 = 0,       /* dispatch payload: H bf16 values per row */
-    MOE_FP8_E4M3 = 1    /* OCP e4m3 codes, H per row, plus one fp32 scale per 128 of them */
+    MOE_FP8_E4M3 = 1,   /* OCP e4m3 codes, H per row, plus one fp32 scale per 128 of them */
+    MOE_BF16_TO_FP8 = 2 /* tokens arrive as bf16 and moe_dispatch_send quantises them into the
+                           e4m3 rows of MOE_FP8_E4M3 ([DSK] Implementation, Quantization: one
+                           scale per 128-value vector found from its largest magnitude):
+                           scale = amax / 448 (1.0 for an all-zero block), code = the e4m3 value
+                           nearest to x / scale (fp32 division), ties to even, clamped to
+                           +-448.  Everything after the send pack is the MOE_FP8_E4M3 path. */
 } moe_dtype;
 
 typedef struct {
@@ -69,6 +76,14 @@ typedef struct {
     int64_t capacity;   /* receive-side rows per rank; 0 = N*T*max(R, E/N), the [EFA] bound.
                            Must be at least N*T*min(R, E/N), the most any rank can receive. */
     int32_t* status;    /* device int32 sticky error word, or NULL */
+    const int32_t* tokens; /* device int32[N], or NULL: rank s dispatches only its first
+                              tokens[s] (0..T) tokens ([PORT] Portable kernels: T is the most any
+                              rank may dispatch; [DSK] Cuda Graph: ranks run different batch sizes
+                              without padding).  The others take no part: moe_route does not
+                              write their rows, their slots get send_pos = -1 and are not counted
+                              or sent, and moe_combine(_recv) does not write their output rows.
+                              The counts stay on the device; a count outside [0, T] sets
+                              MOE_EINVAL in the status word and counts as 0. */
 } moe_shape;
 
 /* Byte sizes of every buffer for a shape.  rows: capacity = B (receive-side rows per rank),
@@ -102,8 +117,8 @@ int moe_route(const moe_shape* shape, const float* logits, const float* bias,
 /* Dispatch, send half.  [EFA] dispatch timing paragraph: count tokens per expert, take the
  * cumulative sum of the counts as offsets into a send buffer contiguous per destination rank,
  * pack the tokens; [PORT] Dispatch: activations, block scales and index travel together.
- *   x         bf16[N][T][H] or e4m3 u8[N][T][H]   tokens
- *   x_scale   f32[N][T][H/128] (fp8) or NULL       block scales
+ *   x         bf16[N][T][H] (MOE_BF16, MOE_BF16_TO_FP8) or e4m3 u8[N][T][H]   tokens
+ *   x_scale   f32[N][T][H/128] (MOE_FP8_E4M3), else NULL                     block scales
  *   topk_idx  i32[N][T*R]                          experts per (token, slot)
  *   counts    i32[N][E] (out)       counts[s][e] = slots of rank s that chose expert e
  *   send_off  i32[N][N+1] (out)     exclusive scan over destinations of rows s sends to d

@@ -11,6 +11,8 @@ Workloads (shapes of the models the pages discuss; distributions are synthetic):
   deepseek_v3_decode_fp8   same, payload e4m3 + fp32 scale per 128 elements
   qwen3_235b_prefill       N=4  T=4096 H=4096 E=128 R=8  bf16, logits ~N(0,1)
   kimi_k2_worst            N=64 T=128  H=7168 E=384 R=8  e4m3 + scales, +16 bias on experts 0..5
+  deepseek_v3_decode_fp8q  DeepSeek-V3 decode, bf16 tokens quantised to e4m3 rows by the send pack
+  deepseek_v3_decode_ragged DeepSeek-V3 decode (bf16) with a token count per rank, T_s ~ U{1..T}
 
 Recipe (seed s, numpy PCG64 ``default_rng``): logits = rng(s).standard_normal((N*T, E), f32);
 then x = rng(s) (same stream, next draw) .standard_normal((N, T, H), f32) rounded to bf16
@@ -20,6 +22,8 @@ Zipf bias: bias[e] = -ln(1 + pi[e]) with pi a permutation of 0..E-1 drawn from
 ``default_rng(1)``, so expert popularity falls off as 1 / rank.
 Kimi worst case: bias = +16 on experts 0..5 (rank 0's experts), 0 elsewhere: every token picks
 all six, the other two slots go to the noise winners among experts 6..383.
+Ragged token counts: T_s = default_rng(seed + 2).integers(1, T + 1, N) (uniform on 1..T); the
+tokens past T_s of each rank still hold data but take no part.
 """
 from __future__ import annotations
 
@@ -43,10 +47,12 @@ class Config:
     H: int
     E: int
     R: int
-    fp8: bool = False
+    fp8: bool = False       # tokens arrive as e4m3 codes + scales
     bias: str = "none"      # "none" | "zipf" | "kimi"
     seed: int = 0
     desc: str = ""
+    quant: bool = False     # tokens arrive as bf16; the send pack makes the e4m3 rows
+    tokens: str = "full"    # "full" (T per rank) | "ragged" (T_s uniform on 1..T)
 
     @property
     def L(self) -> int:
@@ -63,8 +69,13 @@ class Config:
         return self.N * self.T * self.R
 
     @property
+    def rows_fp8(self) -> bool:
+        """Dispatched rows are e4m3 codes + scales."""
+        return self.fp8 or self.quant
+
+    @property
     def dtype(self) -> str:
-        return "fp8_e4m3" if self.fp8 else "bf16"
+        return "bf16->fp8_e4m3" if self.quant else ("fp8_e4m3" if self.fp8 else "bf16")
 
 
 CONFIGS = {
@@ -81,8 +92,27 @@ CONFIGS = {
         Config("kimi_k2_worst", 64, 128, 7168, 384, 8, fp8=True, bias="kimi",
                desc="Kimi-K2-shaped worst case, N64 T128 H7168 E384 R8 e4m3+scales, "
                     "all tokens on rank 0's six experts"),
+        Config("deepseek_v3_decode_fp8q", 32, 128, 7168, 256, 8, quant=True, bias="zipf",
+               desc="DeepSeek-V3-shaped decode, N32 T128 H7168 E256 R8, bf16 tokens quantised "
+                    "to e4m3+scales in the send pack, Zipf bias"),
+        Config("deepseek_v3_decode_ragged", 32, 128, 7168, 256, 8, bias="zipf", tokens="ragged",
+               desc="DeepSeek-V3-shaped decode, N32 T<=128 H7168 E256 R8 bf16, Zipf bias, "
+                    "tokens per rank uniform on 1..128"),
     ]
 }
+
+
+def make_tokens(kind: str, N: int, T: int, seed: int):
+    """Per-rank token counts (int32[N]) or None for T on every rank."""
+    if kind == "full":
+        return None
+    if kind == "ragged":
+        return np.random.default_rng(seed + 2).integers(1, T + 1, N).astype(np.int32)
+    raise ValueError(kind)
+
+
+def config_tokens(cfg: "Config"):
+    return make_tokens(cfg.tokens, cfg.N, cfg.T, cfg.seed)
 
 
 def make_bias(kind: str, E: int):

@@ -35,15 +35,19 @@ def upload_inputs(b, inp):
 
 
 def gpu_run(N, T, H, E, R, fp8, inp, expert_mode=0, capacity=0, y=None, topk_idx=None,
-            poison=True, split_combine=False):
-    """The whole path on the GPU.  Returns (buffers, host copies of every valid output)."""
+            poison=True, split_combine=False, quant=False, tokens=None):
+    """The whole path on the GPU.  Returns (buffers, host copies of every valid output).
+    quant: inp["x"] holds bf16 tokens that the send pack quantises to e4m3 rows; tokens: the
+    per-rank token counts (int array of N), or None."""
     import combine_moe_route_top_amd as moe
-    b = moe.alloc_buffers(N, T, H, E, R, fp8, capacity)
+    b = moe.alloc_buffers(N, T, H, E, R, fp8, capacity, quant=quant, tokens=tokens is not None)
     if poison:  # garbage in every output so that stale values cannot pass for results
         for k, t in b.t.items():
-            if t is not None and k not in ("status",):
+            if t is not None and k not in ("status", "tokens"):
                 t.view(torch.uint8).fill_(0xA5)
         b.status.zero_()
+    if tokens is not None:
+        b.tokens.copy_(torch.from_numpy(np.ascontiguousarray(tokens, np.int32)))
     upload_inputs(b, inp)
     if topk_idx is None:
         moe.moe_route(b.shape, b.logits, b.bias if inp["bias"] is not None else None,
@@ -75,7 +79,9 @@ def gpu_run(N, T, H, E, R, fp8, inp, expert_mode=0, capacity=0, y=None, topk_idx
     else:
         moe.run_combine(b)
     torch.cuda.synchronize()
-    return b, fetch(b, N, T, R)
+    g = fetch(b, N, T, R)
+    g["poisoned"] = poison
+    return b, g
 
 
 def fetch(b, N, T, R):
@@ -98,9 +104,16 @@ def fetch(b, N, T, R):
     return g
 
 
-def oracle_run(N, T, H, E, R, fp8, inp, expert_mode=0, y=None, topk_idx=None):
-    """The oracle on the same inputs, packed receive layout (rank d holds exactly its rows)."""
-    sh = oracle.shape(N, T, H, E, R, fp8)
+def oracle_run(N, T, H, E, R, fp8, inp, expert_mode=0, y=None, topk_idx=None, quant=False,
+               tokens=None):
+    """The oracle on the same inputs, packed receive layout (rank d holds exactly its rows).
+    quant: the oracle's block quantiser turns the bf16 tokens into e4m3 codes and scales, then
+    the e4m3 path runs on them."""
+    if quant:
+        q, sc = oracle.quantize_e4m3(inp["x"])
+        inp = dict(inp, x=q, x_scale=sc)
+        fp8 = True
+    sh = oracle.shape(N, T, H, E, R, fp8, tokens=tokens)
     if topk_idx is None:
         idx, w = oracle.route(inp["logits"], inp["bias"], R)
     else:
@@ -109,7 +122,7 @@ def oracle_run(N, T, H, E, R, fp8, inp, expert_mode=0, y=None, topk_idx=None):
     res = dict(topk_idx=idx, topk_w=w)
     res.update(oracle.dispatch_send(sh, inp["x"], inp["x_scale"], idx.reshape(N, T * R)))
     recv_rows = np.diff(res["send_off"], axis=1).sum(axis=0)
-    sh = oracle.packed_shape(N, T, H, E, R, fp8, recv_rows)
+    sh = oracle.packed_shape(N, T, H, E, R, fp8, recv_rows, tokens)
     res.update(oracle.net_dispatch(sh, res["send_off"], res["send_buf"], res["send_meta"]))
     res.update(oracle.dispatch_recv(sh, res["counts"], res["recv_off"], res["recv_buf"],
                                     res["recv_meta"]))
@@ -126,6 +139,7 @@ def oracle_run(N, T, H, E, R, fp8, inp, expert_mode=0, y=None, topk_idx=None):
         if mode == 0:
             res["cs_buf"], res["cr_buf"] = c["cs_buf"], c["cr_buf"]
     res["shape"] = sh
+    res["tokens"] = None if tokens is None else np.asarray(tokens)
     return res
 
 
@@ -143,8 +157,16 @@ def compare(g: dict, o: dict, N, T, H, E, R, fp8, check_stub=True, check_ulp=Tru
     TR = T * R
     stats = {}
     assert g["status"][0] == 0, f"device status word {g['status'][0]}"
-    assert np.array_equal(g["topk_idx"].reshape(N * T, R), o["topk_idx"]), "topk_idx"
-    gw, ow = g["topk_w"].reshape(N * T, R), o["topk_w"]
+    # tokens present on each rank (all T unless per-rank counts were given); rows of absent
+    # tokens must keep the poison the outputs were filled with
+    nt = np.full(N, T) if o.get("tokens") is None else np.asarray(o["tokens"])
+    present = (np.arange(T)[None, :] < nt[:, None]).reshape(N * T)
+    gi = g["topk_idx"].reshape(N * T, R)
+    if not present.all() and g.get("poisoned"):
+        assert np.all(gi[~present].view(np.uint32) == 0xA5A5A5A5), "route wrote absent tokens"
+        assert np.all(g["out"].reshape(N * T, H)[~present] == 0xA5A5), "combine wrote absent tokens"
+    assert np.array_equal(gi[present], o["topk_idx"][present]), "topk_idx"
+    gw, ow = g["topk_w"].reshape(N * T, R)[present], o["topk_w"][present]
     ulp = np.abs(gw.view(np.int32).astype(np.int64) - ow.view(np.int32).astype(np.int64))
     assert ulp.max() <= 1, f"topk_w differs by {ulp.max()} fp32 ulp"
     stats["w_exact"] = float((ulp == 0).mean())
@@ -173,13 +195,13 @@ def compare(g: dict, o: dict, N, T, H, E, R, fp8, check_stub=True, check_ulp=Tru
     for s in range(N):
         n = o["send_off"][s, N]
         assert np.array_equal(g["cr_buf"][s], o["cr_buf"][s, :n]), f"cr_buf rank {s}"
-    out = g["out"].reshape(N * T, H)
+    out = g["out"].reshape(N * T, H)[present]
     same_w = np.all(gw == ow, axis=1)
-    o1 = o["out1"].reshape(N * T, H)
+    o1 = o["out1"].reshape(N * T, H)[present]
     assert np.array_equal(out[same_w], o1[same_w]), "out vs the oracle's fp32 fma chain"
     stats["fma_chain_tokens"] = int(same_w.sum())
     if check_ulp:
-        d0 = _bf16_ulp_diff(out, o["out0"].reshape(N * T, H))
+        d0 = _bf16_ulp_diff(out, o["out0"].reshape(N * T, H)[present])
         assert d0.max() <= 1, f"out differs from the fp64 oracle by {d0.max()} bf16 ulp"
         stats["out_exact_vs_fp64"] = float((d0 == 0).mean())
     return stats

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strerror():
-    assert moe.moe_abi_version() == 2
+    assert moe.moe_abi_version() == 3
     for code in (0, -1, -2, -3, -5, 42):
         assert isinstance(moe.moe_strerror(code), str)
 
@@ -47,6 +47,13 @@ def test_sizes_of_the_workloads():
     assert sz["workspace"] >= 4 * 32 * 128 * 4       # 32 count chunks of 1024 slots per rank
     sz = moe.moe_sizes(moe.make_shape(8, 128, 4096, 8, 2, capacity=8 * 128 * 1))
     assert sz["capacity"] == 1024                    # the tight bound N*T*min(R, E/N)
+    # bf16 tokens quantised by the send pack: bf16 input, no input scales, e4m3 rows
+    q = moe.moe_sizes(moe.make_shape(32, 128, 7168, 256, 8, quant=True))
+    f = moe.moe_sizes(moe.make_shape(32, 128, 7168, 256, 8, fp8=True))
+    assert q["x"] == 32 * 128 * 7168 * 2 and q["x_scale"] == 0
+    assert q["row_bytes"] == 7392
+    for k in ("send_buf", "recv_buf", "expert_x", "expert_scale", "cr_buf", "out", "workspace"):
+        assert q[k] == f[k], k
 
 
 @pytest.mark.parametrize("args,code", [
@@ -81,6 +88,12 @@ def test_bad_fp8_hidden_and_capacity():
     with pytest.raises(moe.MoeError) as ex:
         moe.moe_sizes(moe.make_shape(2, 16, 256, 8, 2, fp8=True))   # fp8 needs H % 512 == 0
     assert ex.value.code == moe.MOE_EUNSUPPORTED
+    with pytest.raises(moe.MoeError) as ex:
+        moe.moe_sizes(moe.make_shape(2, 16, 256, 8, 2, quant=True))
+    assert ex.value.code == moe.MOE_EUNSUPPORTED
+    with pytest.raises(moe.MoeError) as ex:                          # unknown dtype
+        moe.moe_sizes(moe.moe_shape(2, 16, 512, 8, 2, 3, 0, 0, 0, None, None))
+    assert ex.value.code == moe.MOE_EINVAL
     with pytest.raises(moe.MoeError) as ex:                          # below the tight bound
         moe.moe_sizes(moe.make_shape(2, 16, 256, 8, 2, capacity=2 * 16 * 2 - 1))
     assert ex.value.code == moe.MOE_EINVAL
@@ -116,6 +129,17 @@ def test_null_and_misaligned_pointers_rejected_before_launch():
     assert ex.value.code == moe.MOE_EINVAL
     with pytest.raises(moe.MoeError) as ex:
         moe.moe_route(None if False else moe.make_shape(3, 1, 8, 8, 1), good, None, good, good, stream=0)
+    assert ex.value.code == moe.MOE_EINVAL
+    qsh = moe.make_shape(2, 16, 512, 8, 2, quant=True)
+    with pytest.raises(moe.MoeError) as ex:   # quantising send: the scales are outputs, not inputs
+        moe.moe_dispatch_send(qsh, good, good, good, good, good, good, good, good, good, stream=0)
+    assert ex.value.code == moe.MOE_EINVAL
+    tsh = moe.make_shape(2, 16, 256, 8, 2, tokens=good + 2)   # misaligned token counts
+    with pytest.raises(moe.MoeError) as ex:
+        moe.moe_route(tsh, good, None, good, good, stream=0)
+    assert ex.value.code == moe.MOE_EINVAL
+    with pytest.raises(moe.MoeError) as ex:
+        moe.moe_sizes(tsh)
     assert ex.value.code == moe.MOE_EINVAL
 
 

@@ -179,6 +179,92 @@ def test_rank_subrange_calls_compose(case):
                 assert np.array_equal(g[k][d], full[k][d]), (width, k, d)
 
 
+def _token_counts(N, T, seed):
+    """Per-rank token counts with an empty rank, a full rank and (N > 2) a one-token rank."""
+    t = np.random.default_rng(seed).integers(0, T + 1, N).astype(np.int32)
+    t[0], t[-1] = 0, T
+    if N > 2:
+        t[1] = 1
+    return t
+
+
+VARTOK = [SMALL[1], SMALL[2], SMALL[3], SMALL[7], SMALL[10]]
+
+
+@pytest.mark.parametrize("case", VARTOK, ids=lambda c: _case_id(c))
+@pytest.mark.parametrize("split", [False, True])
+def test_variable_tokens(case, split):
+    # rank s dispatches only its first tokens[s] tokens; rows of the others are not written
+    N, T, H, E, R, fp8, bias = case
+    tokens = _token_counts(N, T, 5)
+    print(f"\ncase tokens {_case_id(case)} split {split} tokens {tokens.tolist()}", flush=True)
+    inp = ms.make_inputs(N, T, H, E, R, fp8, bias, 2)
+    _, g = parity.gpu_run(N, T, H, E, R, fp8, inp, tokens=tokens, split_combine=split)
+    o = parity.oracle_run(N, T, H, E, R, fp8, inp, tokens=tokens)
+    parity.compare(g, o, N, T, H, E, R, fp8)
+    assert g["counts"].sum() == int(tokens.sum()) * R
+
+
+def test_bad_token_count_sets_status():
+    # a count above T flags MOE_EINVAL and the rank dispatches nothing; every kernel finishes
+    import combine_moe_route_top_amd as moe
+    N, T, H, E, R = 2, 8, 64, 8, 2
+    print("\ncase bad token count", flush=True)
+    inp = ms.make_inputs(N, T, H, E, R, False, "none", 0)
+    tokens = np.array([T + 1, 5], np.int32)
+    _, g = parity.gpu_run(N, T, H, E, R, False, inp, tokens=tokens)
+    assert g["status"][0] == moe.MOE_EINVAL
+    assert g["counts"][0].sum() == 0 and g["counts"][1].sum() == 5 * R
+    assert np.all(g["send_pos"][0] == -1)
+    assert np.all(g["out"][0] == 0xA5A5)
+
+
+def _quant_inputs(N, T, H, E, R, bias, seed):
+    """bf16 tokens with magnitudes spread over 2^-30 .. 2^30 per token, an all-zero block, a
+    block with one large value among small ones, and values in the e4m3 subnormal range."""
+    inp = ms.make_inputs(N, T, H, E, R, False, bias, seed)
+    xf = ms.bf16_bits_to_f32(inp["x"]).copy()
+    rng = np.random.default_rng(seed + 50)
+    xf *= np.exp2(rng.integers(-30, 31, (N, T, 1))).astype(np.float32)
+    xf[0, 0, :128] = 0.0
+    if T > 1:
+        xf[0, 1, 128:256] *= np.float32(1e-3)
+        xf[0, 1, 130] = 5.0
+    inp["x"] = ms.to_bf16_bits(xf.astype(np.float32))
+    return inp
+
+
+QUANT = [  # N, T, H, E, R, bias
+    (4, 300, 512, 16, 4, "none"),      # half a pass per token; two count chunks
+    (16, 32, 512, 96, 8, "kimi"),
+    (2, 5, 7168, 8, 4, "none"),        # seven passes of 1024 values
+    (3, 9, 1536, 12, 3, "zipf"),       # one and a half passes
+    (8, 129, 1024, 64, 8, "zipf"),
+]
+
+
+@pytest.mark.parametrize("case", QUANT, ids=lambda c: "N{}_T{}_H{}_E{}_R{}_{}".format(*c))
+def test_fused_quant(case):
+    # bf16 tokens quantised to e4m3 rows by the send pack: every byte of every stage matches the
+    # oracle's quantiser followed by the e4m3 path
+    N, T, H, E, R, bias = case
+    print(f"\ncase quant {case}", flush=True)
+    inp = _quant_inputs(N, T, H, E, R, bias, 6)
+    _, g = parity.gpu_run(N, T, H, E, R, True, inp, quant=True)
+    o = parity.oracle_run(N, T, H, E, R, False, inp, quant=True)
+    parity.compare(g, o, N, T, H, E, R, True)
+
+
+def test_fused_quant_with_token_counts():
+    N, T, H, E, R, bias = 8, 129, 1024, 64, 8, "zipf"
+    tokens = _token_counts(N, T, 8)
+    print(f"\ncase quant + tokens {tokens.tolist()}", flush=True)
+    inp = _quant_inputs(N, T, H, E, R, bias, 7)
+    _, g = parity.gpu_run(N, T, H, E, R, True, inp, quant=True, tokens=tokens, split_combine=True)
+    o = parity.oracle_run(N, T, H, E, R, False, inp, quant=True, tokens=tokens)
+    parity.compare(g, o, N, T, H, E, R, True)
+
+
 def test_tight_capacity():
     # receive buffers sized to the tight bound N*T*min(R, E/N) instead of N*T*max(R, E/N)
     N, T, H, E, R = 4, 40, 64, 32, 8
@@ -242,7 +328,8 @@ def test_bad_expert_ids_set_status():
 
 
 FULL = ["tiny", "mixtral_8x7b_decode", "deepseek_v3_decode", "deepseek_v3_decode_fp8",
-        "qwen3_235b_prefill", "kimi_k2_worst"]
+        "qwen3_235b_prefill", "kimi_k2_worst", "deepseek_v3_decode_fp8q",
+        "deepseek_v3_decode_ragged"]
 
 
 @pytest.mark.timeout(600)
@@ -251,11 +338,13 @@ def test_full_workload(name):
     c = ms.CONFIGS[name]
     print(f"\ncase full {name}", flush=True)
     inp = ms.config_inputs(c)
-    _, g = parity.gpu_run(c.N, c.T, c.H, c.E, c.R, c.fp8, inp, poison=False)
+    tokens = ms.config_tokens(c)
+    _, g = parity.gpu_run(c.N, c.T, c.H, c.E, c.R, c.rows_fp8, inp, poison=tokens is not None,
+                          quant=c.quant, tokens=tokens)
     print("  gpu done", flush=True)
-    o = parity.oracle_run(c.N, c.T, c.H, c.E, c.R, c.fp8, inp)
+    o = parity.oracle_run(c.N, c.T, c.H, c.E, c.R, c.fp8, inp, quant=c.quant, tokens=tokens)
     print("  oracle done", flush=True)
-    st = parity.compare(g, o, c.N, c.T, c.H, c.E, c.R, c.fp8)
+    st = parity.compare(g, o, c.N, c.T, c.H, c.E, c.R, c.rows_fp8)
     print(" ", st, flush=True)
     if name == "kimi_k2_worst":
         assert g["recv_off"][0, c.N] == 49152
