@@ -215,10 +215,13 @@ def traffic_record(kernel, workload):
                          r"source=(\S+) sha256=([0-9a-f]+)", line.strip())
             if not m or m.group(1) != kernel or m.group(2) != workload:
                 continue
-            src = os.path.join(ROOT, m.group(4))
-            if not os.path.exists(src):
-                return None
-            if hashlib.sha256(open(src, "rb").read()).hexdigest() != m.group(5):
+            h = hashlib.sha256()
+            for rel in m.group(4).split(","):     # every source file the kernel is built from
+                src = os.path.join(ROOT, rel)
+                if not os.path.exists(src):
+                    return None
+                h.update(open(src, "rb").read())
+            if h.hexdigest() != m.group(5):
                 return None
             return int(m.group(3))
     return None

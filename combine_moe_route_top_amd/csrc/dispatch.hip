@@ -15,6 +15,15 @@
 
 #include "common.cuh"
 
+// Waves the send packs aim for (the grid is one token per wave when there are at least this many
+// tokens); overridable at build time for launch-shape experiments.
+#ifndef MOE_PACK_MIN_WAVES
+#define MOE_PACK_MIN_WAVES 4096
+#endif
+#ifndef MOE_QPACK_MIN_WAVES
+#define MOE_QPACK_MIN_WAVES 32768
+#endif
+
 namespace moe {
 
 // ------------------------------------------------------------------ count and scan
@@ -517,17 +526,18 @@ hipError_t launch_dispatch_send(const Dims& D, const void* x, const float* x_sca
                        (const int32_t*)chunk_cnt, C, counts, send_off, send_pos, send_meta);
     const long ntok = (long)D.rc * D.T;
     if (D.quant) {
-        // up to one wave per 1024 values when there are fewer than 4096 tokens
-        int wpt = 1;
-        while (wpt < 8 && ntok * wpt < 4096 && 1024L * wpt * 2 <= D.H) wpt *= 2;
+        // waves per token: enough for MOE_QPACK_MIN_WAVES waves in all, at most one per pass
+        const long passes = (D.H + 1023) / 1024;
+        const long want = (MOE_QPACK_MIN_WAVES + ntok - 1) / ntok;
+        const int wpt = (int)std::max(1L, std::min(passes, want));
         const long waves = ntok * wpt;
         hipLaunchKernelGGL(k_send_pack_q, dim3((waves + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock),
                            0, st, D, wpt, (const uint16_t*)x, (const int32_t*)send_pos, (uint8_t*)send_buf);
         return hipGetLastError();
     }
-    // up to 8 waves per token when there are fewer than 4096 tokens to keep the chip busy
+    // up to 8 waves per token when there are fewer than MOE_PACK_MIN_WAVES tokens
     int wpt = 1;
-    while (wpt < 8 && ntok * wpt < 4096 && (long)kWave * wpt * 2 <= D.P16) wpt *= 2;
+    while (wpt < 8 && ntok * wpt < MOE_PACK_MIN_WAVES && (long)kWave * wpt * 2 <= D.P16) wpt *= 2;
     const long waves = ntok * wpt;
     hipLaunchKernelGGL(k_send_pack<8>, dim3((waves + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock), 0,
                        st, D, wpt, (const uint8_t*)x, x_scale, (const int32_t*)send_pos, (uint8_t*)send_buf);
