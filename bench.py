@@ -366,6 +366,8 @@ def overlap_leg(name, steps=10, warmup=2, inter=2048) -> dict:
         second()
         s1.wait_stream(s2)
 
+    # dispatch: the shared expert runs while the transfer (network + receive) is in flight;
+    # combine: while the combine send half (shuffle + network back) is, before the weighted sum
     variants = {
         "shared_alone": lambda: shared(s1),
         "dispatch_alone": lambda: (d_send(), d_transfer()),
@@ -373,7 +375,7 @@ def overlap_leg(name, steps=10, warmup=2, inter=2048) -> dict:
         "dispatch_overlap": lambda: fork_join(d_send, d_transfer),
         "combine_alone": lambda: (c_send(), c_recv()),
         "combine_then_shared": lambda: (c_send(), shared(s1), c_recv()),
-        "combine_overlap": lambda: (fork_join(c_send, lambda: None), c_recv()),
+        "combine_overlap": lambda: (fork_join(lambda: None, c_send), c_recv()),
     }
     us = {}
     for k, fn in variants.items():
@@ -395,6 +397,129 @@ def overlap_leg(name, steps=10, warmup=2, inter=2048) -> dict:
         res[f"{ph}_hidden_us"] = round(hidden, 2)
         res[f"{ph}_hidden_frac_of_shared"] = round(hidden / us["shared_alone"], 3)
     del b
+    torch.cuda.empty_cache()
+    return res
+
+
+def microbatch_leg(name, steps=10, warmup=2, inter=2048) -> dict:
+    """Two-micro-batch pipelining ([DSK] computation/communication overlap): the layer's tokens
+    are split into two micro-batches of T/2 tokens per rank, each with its own buffers.  A
+    stand-in compute stage (the shared-expert MLP of the overlap leg on the micro-batch's tokens)
+    runs on a second stream.  Serial: dispatch A, compute A, combine A, then the same for B.
+    Pipelined: dispatch A; compute A on stream 2 while dispatch B runs on stream 1; combine A
+    (after compute A) on stream 1 while compute B (after dispatch B) runs on stream 2; combine B.
+    Reports both times and the time hidden."""
+    import numpy as np
+    import torch
+    import torch.nn.functional as F
+
+    import combine_moe_route_top_amd as moe
+    import moe_synth as ms
+
+    c = ms.CONFIGS[name]
+    assert not c.rows_fp8 and c.T % 2 == 0, "the micro-batch leg runs on a bf16 workload, T even"
+    Th = c.T // 2
+    inp = ms.config_inputs(c)
+    s1 = torch.cuda.current_stream()
+    s2 = torch.cuda.Stream()   # default priority
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    wg = (torch.randn(c.H, inter, device="cuda", generator=gen) * c.H ** -0.5).to(torch.bfloat16)
+    wu = (torch.randn(c.H, inter, device="cuda", generator=gen) * c.H ** -0.5).to(torch.bfloat16)
+    wd = (torch.randn(inter, c.H, device="cuda", generator=gen) * inter ** -0.5).to(torch.bfloat16)
+    logits = inp["logits"].reshape(c.N, c.T, c.E)
+    x = inp["x"].view(np.int16)
+    use_bias = inp["bias"] is not None
+    mbs = []
+    for h in range(2):
+        b = moe.alloc_buffers(c.N, Th, c.H, c.E, c.R)
+        b.logits.copy_(torch.from_numpy(np.ascontiguousarray(logits[:, h * Th:(h + 1) * Th]).reshape(-1, c.E)))
+        if use_bias:
+            b.bias.copy_(torch.from_numpy(inp["bias"]))
+        b.x.copy_(torch.from_numpy(np.ascontiguousarray(x[:, h * Th:(h + 1) * Th])))
+        xs = b.x.view(torch.bfloat16).view(c.N * Th, c.H)
+        mbs.append((b, xs, torch.empty_like(xs)))
+
+    def dispatch(mb, st):
+        b = mb[0]
+        moe.moe_route(b.shape, b.logits, b.bias if use_bias else None, b.topk_idx, b.topk_w, st)
+        moe.moe_dispatch_send(b.shape, b.x, None, b.topk_idx, b.counts, b.send_off, b.send_pos,
+                              b.send_buf, b.send_meta, b.workspace, st)
+        moe.moe_net_dispatch(b.shape, b.send_off, b.send_buf, b.send_meta, b.recv_buf, b.recv_meta,
+                             b.recv_off, st)
+        moe.moe_dispatch_recv(b.shape, b.counts, b.recv_off, b.recv_buf, b.recv_meta, b.expert_x,
+                              None, b.expert_cnt, b.expert_off, b.expert_src, b.expert_rpos,
+                              b.workspace, st)
+
+    def compute(mb, st):
+        _, xs, ys = mb
+        with torch.cuda.stream(st):
+            torch.matmul(F.silu(xs @ wg) * (xs @ wu), wd, out=ys)
+
+    def combine(mb, st):
+        b = mb[0]
+        moe.moe_combine(b.shape, b.expert_x, b.expert_rpos, b.recv_off, b.send_off, b.send_pos,
+                        b.topk_w, b.cs_buf, b.cr_buf, b.out, st)
+
+    def after(st_wait, st_done):
+        ev = torch.cuda.Event()
+        ev.record(st_done)
+        st_wait.wait_event(ev)
+
+    A, Bm = mbs
+
+    def serial():
+        for mb in (A, Bm):
+            dispatch(mb, s1)
+            compute(mb, s1)
+            combine(mb, s1)
+
+    def pipelined():
+        dispatch(A, s1)
+        after(s2, s1)
+        compute(A, s2)         # compute A  ||  dispatch B
+        dispatch(Bm, s1)
+        after(s1, s2)          # combine A needs compute A
+        after(s2, s1)          # compute B needs dispatch B
+        combine(A, s1)
+        compute(Bm, s2)        # compute B  ||  combine A
+        after(s1, s2)
+        combine(Bm, s1)
+
+    us = {}
+    for k, fn in (("serial", serial), ("pipelined", pipelined)):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s1)
+        for _ in range(steps):
+            fn()
+        e1.record(s1)
+        torch.cuda.synchronize()
+        us[k] = round(e0.elapsed_time(e1) * 1e3 / steps, 2)
+    # the parts alone, for reference
+    parts = {}
+    for k, fn in (("dispatch", lambda: dispatch(A, s1)), ("compute", lambda: compute(A, s1)),
+                  ("combine", lambda: combine(A, s1))):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s1)
+        for _ in range(steps):
+            fn()
+        e1.record(s1)
+        torch.cuda.synchronize()
+        parts[k] = round(e0.elapsed_time(e1) * 1e3 / steps, 2)
+    for mb in mbs:
+        if int(mb[0].status.item()) != 0:
+            raise RuntimeError("device status word set in the micro-batch leg")
+    res = {"workload": name, "micro_batches": 2, "tokens_per_rank_each": Th,
+           "compute": f"bf16 MLP {c.H}->{inter}->{c.H} on each micro-batch's {c.N * Th} tokens "
+                      f"(torch GEMMs on a second stream)",
+           "us": us, "one_micro_batch_us": parts,
+           "hidden_us": round(us["serial"] - us["pipelined"], 2)}
+    del mbs, A, Bm
     torch.cuda.empty_cache()
     return res
 
@@ -485,6 +610,8 @@ def main():
                     help="skip the send/receive-split overlap leg")
     ap.add_argument("--no-rank-leg", action="store_true",
                     help="skip the one-rank-share timing leg")
+    ap.add_argument("--no-microbatch", action="store_true",
+                    help="skip the two-micro-batch pipelining leg")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the N expert-parallel ranks are simulated inside one "
@@ -535,6 +662,8 @@ def main():
     }
     if not args.no_overlap:
         line["overlap"] = overlap_leg(HEADLINE)
+    if not args.no_microbatch:
+        line["micro_batches"] = microbatch_leg(HEADLINE)
     if not args.no_rank_leg:
         line["one_rank_share"] = [rank_leg(w) for w in (HEADLINE, "kimi_k2_worst")]
     if calib is not None:

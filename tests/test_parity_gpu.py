@@ -130,6 +130,61 @@ def test_overlap_with_second_stream():
     parity.compare(g, o, N, T, H, E, R, False)
 
 
+def test_two_micro_batches_pipelined():
+    # two micro-batches on two streams in the pipelined order (dispatch B while A's compute runs
+    # on stream 2, combine A while B's compute runs): both match the oracle
+    import combine_moe_route_top_amd as moe
+    N, T, H, E, R = 8, 64, 1024, 64, 8
+    print("\ncase micro-batches", flush=True)
+    s1 = torch.cuda.current_stream()
+    s2 = torch.cuda.Stream()
+    inps, bufs = [], []
+    for h in range(2):
+        inp = ms.make_inputs(N, T, H, E, R, False, "zipf", 10 + h)
+        b = moe.alloc_buffers(N, T, H, E, R)
+        for k, t in b.t.items():
+            if t is not None and k != "status":
+                t.view(torch.uint8).fill_(0xA5)
+        b.status.zero_()
+        parity.upload_inputs(b, inp)
+        inps.append(inp)
+        bufs.append(b)
+    a = torch.randn(2048, 2048, device="cuda", dtype=torch.bfloat16)
+
+    def dispatch(b, st):
+        moe.run_dispatch(b, stream=st)
+        moe.moe_expert_stub(b.shape, 1, b.expert_x, None, b.expert_off, b.expert_y, st)
+
+    def compute(st):
+        nonlocal a
+        with torch.cuda.stream(st):
+            for _ in range(3):
+                a = (a @ a) * 0.01
+
+    def after(wait, done):
+        ev = torch.cuda.Event()
+        ev.record(done)
+        wait.wait_event(ev)
+
+    A, Bm = bufs
+    dispatch(A, s1)
+    after(s2, s1)
+    compute(s2)
+    dispatch(Bm, s1)
+    after(s1, s2)
+    after(s2, s1)
+    moe.run_combine(A, stream=s1)
+    compute(s2)
+    after(s1, s2)
+    moe.run_combine(Bm, stream=s1)
+    torch.cuda.synchronize()
+    for b, inp in zip(bufs, inps):
+        g = parity.fetch(b, N, T, R)
+        g["poisoned"] = True
+        o = parity.oracle_run(N, T, H, E, R, False, inp, expert_mode=1)
+        parity.compare(g, o, N, T, H, E, R, False)
+
+
 @pytest.mark.parametrize("case", [SMALL[3], SMALL[7], SMALL[8], SMALL[11]], ids=lambda c: _case_id(c))
 def test_rank_subrange_calls_compose(case):
     # every step called once per rank (as each GPU of a real deployment would), each step for all
