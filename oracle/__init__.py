@@ -233,6 +233,39 @@ def combine(sh: Shape, mode: int, expert_y, expert_rpos, recv_off, send_off, sen
     return dict(cs_buf=cs, cr_buf=cr, out=out)
 
 
+def prefill_dispatch(sh: Shape, x: np.ndarray, x_scale, topk_idx: np.ndarray):
+    """Replicated tokens: x uint16[T][H] (bf16 bits) or uint8[T][H] (e4m3), x_scale f32[T][H/128];
+    topk_idx i32[T][R].  sh.B is the per-rank row stride of the receive-side arrays."""
+    N, T, H, E, R = sh.N, sh.T, sh.H, sh.E, sh.R
+    L = E // N
+    x = np.ascontiguousarray(x)
+    xs = None if not sh.fp8 else np.ascontiguousarray(x_scale, dtype=np.float32)
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    slot_pos = np.full((T, R), -1, np.int32)
+    expert_x = np.zeros((N, sh.B, H), np.uint8 if sh.fp8 else np.uint16)
+    expert_scale = np.zeros((N, sh.B, H // 128), np.float32) if sh.fp8 else None
+    expert_cnt = np.empty((N, L), np.int32)
+    expert_off = np.empty((N, L + 1), np.int32)
+    expert_src = np.full((N, sh.B), -1, np.int32)
+    lib().oracle_prefill_dispatch(ctypes.byref(sh), _p(x), _p(xs), _p(idx), _p(slot_pos),
+                                  _p(expert_x), _p(expert_scale), _p(expert_cnt), _p(expert_off),
+                                  _p(expert_src))
+    return dict(slot_pos=slot_pos, expert_x=expert_x, expert_scale=expert_scale,
+                expert_cnt=expert_cnt, expert_off=expert_off, expert_src=expert_src)
+
+
+def prefill_combine(sh: Shape, mode: int, expert_y, slot_pos, topk_idx, topk_w):
+    N, T, H = sh.N, sh.T, sh.H
+    partial = np.zeros((N, T, H), np.float32)
+    out = np.zeros((T, H), np.uint16)
+    lib().oracle_prefill_combine(ctypes.byref(sh), ctypes.c_int(mode),
+                                 _p(np.ascontiguousarray(expert_y, np.uint16)),
+                                 _p(np.ascontiguousarray(slot_pos, np.int32)),
+                                 _p(np.ascontiguousarray(topk_idx, np.int32)),
+                                 _p(np.ascontiguousarray(topk_w, np.float32)), _p(partial), _p(out))
+    return dict(partial=partial, out=out)
+
+
 def run_all(sh: Shape, inp: dict, expert_mode: int = 0, combine_mode: int = 0,
             tight: bool = False) -> dict:
     """The whole path on one input set (see moe_synth.make_inputs).

@@ -9,7 +9,8 @@
  *
  * Pages cited: [EFA] "Enabling trillion-parameter models on AWS EFA";
  * [PORT] "Efficient and portable mixture-of-experts communication";
- * [DSK] "Lower latency and higher throughput with multi-node DeepSeek deployment".
+ * [DSK] "Lower latency and higher throughput with multi-node DeepSeek deployment";
+ * [QWEN] "Hosting Qwen on Blackwell".
  *
  * Readings of the pages taken here (the pages leave these steps open):
  *  - expert e lives on rank e / L, L = E / N (contiguous blocks; [DSK] Expert Parallelism only
@@ -409,6 +410,98 @@ void oracle_combine(const oracle_shape* sh, int mode, const uint16_t* expert_y,
                 }
                 out[((long)s * T + t) * H + h] =
                     oracle_bf16_from_double(mode == 0 ? acc : (double)accf);
+            }
+        }
+    }
+}
+
+/* ---------------------------------------------------------------- prefill (replicated inputs) */
+
+/* [QWEN] MoE dispatch-combine, Expert parallel: the prefill kernel's inputs are the same on every
+ * rank, so each rank's dispatch only picks the tokens routed to its own experts and stages them
+ * as grouped-GEMM inputs.  Rank d walks its local experts j in order and, for each, every
+ * (token, slot) in order: the rows of one expert are contiguous, in (t, k) order. */
+void oracle_prefill_dispatch(const oracle_shape* sh, const uint8_t* x, const float* x_scale,
+                             const int32_t* topk_idx, int32_t* slot_pos, uint8_t* expert_x,
+                             float* expert_scale, int32_t* expert_cnt, int32_t* expert_off,
+                             int32_t* expert_src) {
+    const int N = sh->N, T = sh->T, H = sh->H, E = sh->E, R = sh->R;
+    assert(N >= 1 && E % N == 0);
+    const int L = E / N;
+    const long xrow = sh->fp8 ? H : 2L * H;
+    const int nsc = H / 128;
+    for (int t = 0; t < T; ++t)
+        for (int k = 0; k < R; ++k) {
+            const int e = topk_idx[(long)t * R + k];
+            assert(e >= 0 && e < E);
+            for (int kk = 0; kk < k; ++kk) assert(topk_idx[(long)t * R + kk] != e); /* distinct */
+        }
+    for (int d = 0; d < N; ++d) {
+        int32_t* ecnt = expert_cnt + (long)d * L;
+        int32_t* eoff = expert_off + (long)d * (L + 1);
+        long q = 0;
+        eoff[0] = 0;
+        for (int j = 0; j < L; ++j) {
+            const int e = d * L + j;
+            for (int t = 0; t < T; ++t) {
+                for (int k = 0; k < R; ++k) {
+                    if (topk_idx[(long)t * R + k] != e) continue;
+                    assert(q < sh->B);
+                    const long row = (long)d * sh->B + q;
+                    memcpy(expert_x + row * xrow, x + (long)t * xrow, xrow);
+                    if (sh->fp8) memcpy(expert_scale + row * nsc, x_scale + (long)t * nsc, 4L * nsc);
+                    expert_src[row] = t * R + k;
+                    slot_pos[(long)t * R + k] = (int32_t)q;
+                    q += 1;
+                }
+            }
+            eoff[j + 1] = (int32_t)q;
+            ecnt[j] = eoff[j + 1] - eoff[j];
+        }
+    }
+}
+
+/* [QWEN] MoE dispatch-combine, Expert parallel: the combine kernel first accumulates, locally,
+ * the contributions of the tokens' slots routed to this rank's experts, then all-reduces across
+ * the ranks.  Every rank writes a partial for every token (zero where it owns none of the
+ * token's experts); the all-reduce sums them. */
+void oracle_prefill_combine(const oracle_shape* sh, int mode, const uint16_t* expert_y,
+                            const int32_t* slot_pos, const int32_t* topk_idx, const float* topk_w,
+                            float* partial, uint16_t* out) {
+    const int N = sh->N, T = sh->T, H = sh->H, R = sh->R;
+    const int L = sh->E / N;
+    for (int d = 0; d < N; ++d) {
+        for (int t = 0; t < T; ++t) {
+            for (int h = 0; h < H; ++h) {
+                double acc = 0.0;
+                float accf = 0.0f;
+                for (int k = 0; k < R; ++k) {
+                    const long i = (long)t * R + k;
+                    if (topk_idx[i] / L != d) continue;
+                    const double y =
+                        oracle_bf16_to_double(expert_y[((long)d * sh->B + slot_pos[i]) * H + h]);
+                    if (mode == 0) acc += (double)topk_w[i] * y;
+                    else accf = fmaf(topk_w[i], (float)y, accf);
+                }
+                partial[((long)d * T + t) * H + h] = mode == 0 ? (float)acc : accf;
+            }
+        }
+    }
+    for (int t = 0; t < T; ++t) {
+        for (int h = 0; h < H; ++h) {
+            if (mode == 0) {
+                double acc = 0.0;
+                for (int k = 0; k < R; ++k) {
+                    const long i = (long)t * R + k;
+                    const int d = topk_idx[i] / L;
+                    acc += (double)topk_w[i] *
+                           oracle_bf16_to_double(expert_y[((long)d * sh->B + slot_pos[i]) * H + h]);
+                }
+                out[(long)t * H + h] = oracle_bf16_from_double(acc);
+            } else {
+                float s = 0.0f;
+                for (int d = 0; d < N; ++d) s = s + partial[((long)d * T + t) * H + h];
+                out[(long)t * H + h] = oracle_bf16_from_double((double)s);
             }
         }
     }

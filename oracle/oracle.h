@@ -9,6 +9,7 @@
  *   [EFA]  "Enabling trillion-parameter models on AWS EFA"
  *   [PORT] "Efficient and portable mixture-of-experts communication"
  *   [DSK]  "Lower latency and higher throughput with multi-node DeepSeek deployment"
+ *   [QWEN] "Hosting Qwen on Blackwell"
  *
  * Problem statement ([EFA], send-buffer design paragraph): N ranks, each dispatching T tokens,
  * every token routed to R of E experts; expert e lives on rank e / L with L = E / N.
@@ -81,5 +82,28 @@ void oracle_combine(const oracle_shape* sh, int mode, const uint16_t* expert_y,
                     const int32_t* expert_rpos, const int32_t* recv_off, const int32_t* send_off,
                     const int32_t* send_pos, const float* topk_w, uint16_t* cs_buf, uint16_t* cr_buf,
                     uint16_t* out);
+
+/* Prefill expert parallelism with replicated inputs ([QWEN] "Hosting Qwen on Blackwell", MoE
+ * dispatch-combine, Expert parallel): every rank holds the same T tokens (sh->T), so dispatch
+ * only selects, on each rank, the slots routed to its own experts, and combine accumulates each
+ * rank's contributions locally and then all-reduces over the ranks.  sh->B is the per-rank row
+ * stride of the receive-side arrays; rank d has expert_off[d][L] rows.
+ *   x [T][H] (bf16 bits or e4m3 codes), x_scale [T][H/128] (fp8), topk_idx [T][R]
+ *   slot_pos [T][R] (out): row of slot (t, k) in its owner rank's expert-major arrays
+ *   expert_x [N][B][H], expert_scale [N][B][H/128], expert_cnt [N][L], expert_off [N][L+1],
+ *   expert_src [N][B] = t*R + k.  Rows are in (local expert, token, slot) order. */
+void oracle_prefill_dispatch(const oracle_shape* sh, const uint8_t* x, const float* x_scale,
+                             const int32_t* topk_idx, int32_t* slot_pos, uint8_t* expert_x,
+                             float* expert_scale, int32_t* expert_cnt, int32_t* expert_off,
+                             int32_t* expert_src);
+
+/* Prefill combine.  partial [N][T][H] fp32 (out), out [T][H] bf16 (out).
+ * mode 0: partial[d][t] = sum over d's slots of w * y in fp64 (stored rounded to fp32);
+ *         out = bf16 of the fp64 sum over every slot (the definition).
+ * mode 1: partial[d][t] = fp32 fused-multiply-add chain over d's slots in slot order;
+ *         out = bf16 of the fp32 sum of the partials in rank order 0..N-1. */
+void oracle_prefill_combine(const oracle_shape* sh, int mode, const uint16_t* expert_y,
+                            const int32_t* slot_pos, const int32_t* topk_idx, const float* topk_w,
+                            float* partial, uint16_t* out);
 
 #endif

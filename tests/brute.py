@@ -173,6 +173,22 @@ def dispatch(N, T, E, R, idx, tokens=None):
                 recv_order=recv_order, expert_order=expert_order, rank_e=rank_e)
 
 
+def prefill_layout(N, T, E, R, idx):
+    """Replicated tokens: rank d's expert-major order is every (t, k) whose expert d owns,
+    sorted by (local expert, t, k).  Returns the order per rank and each slot's position."""
+    L = E // N
+    idx = np.asarray(idx).reshape(T, R)
+    order, pos = [], {}
+    for d in range(N):
+        ent = [(int(idx[t, k]) - d * L, t, k) for t in range(T) for k in range(R)
+               if int(idx[t, k]) // L == d]
+        ent = sorted(ent)
+        order.append(ent)
+        for q, (_, t, k) in enumerate(ent):
+            pos[(t, k)] = q
+    return order, pos
+
+
 def combine_exact(N, T, R, E, y_of_entry, w):
     """out[s][t] = bf16(sum_k w[s,t,k] * y(s,t,k)) with the sum exact (Fractions).
 

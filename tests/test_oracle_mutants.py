@@ -55,6 +55,16 @@ MUTANTS = {
     "send_counts_absent_tokens": ("for (long i = 0; i < (long)Ts * R; ++i) {",
                                   "for (long i = 0; i < TR; ++i) {"),
     "send_packs_absent_tokens": ("for (int t = 0; t < Ts; ++t) {", "for (int t = 0; t < T; ++t) {"),
+    "prefill_src_transposed": ("expert_src[row] = t * R + k;", "expert_src[row] = k * T + t;"),
+    "prefill_owner_modulo": ("if (topk_idx[i] / L != d) continue;", "if (topk_idx[i] % N != d) continue;"),
+    "prefill_local_ignores_weight": ("else accf = fmaf(topk_w[i], (float)y, accf);",
+                                     "else accf = fmaf(1.0f, (float)y, accf);"),
+    "prefill_allreduce_reversed": ("for (int d = 0; d < N; ++d) s = s + partial",
+                                   "for (int d = N - 1; d >= 0; --d) s = s + partial"),
+    "prefill_allreduce_drops_rank": ("for (int d = 0; d < N; ++d) s = s + partial",
+                                     "for (int d = 1; d < N; ++d) s = s + partial"),
+    "prefill_sum_weight_of_slot0": ("                    acc += (double)topk_w[i] *\n",
+                                    "                    acc += (double)topk_w[(long)t * R] *\n"),
 }
 
 

@@ -340,6 +340,153 @@ def test_quantize_blocks(scale_exp):
     assert np.array_equal(sc, sc2) and np.array_equal(q, q2)
 
 
+# ------------------------------------------------------------------ prefill (replicated tokens)
+
+PREFILL = [  # N, T, H, E, R, fp8
+    (2, 9, 16, 8, 2, False), (4, 13, 8, 16, 4, False), (3, 7, 512, 12, 3, True),
+    (1, 10, 8, 6, 3, False), (8, 5, 8, 16, 8, False),
+]
+
+
+def run_prefill(N, T, H, E, R, fp8, seed=0, bias="none"):
+    inp = ms.make_inputs(1, T, H, E, R, fp8, bias, seed)      # one replicated token set
+    idx, w = oracle.route(inp["logits"], inp["bias"], R)
+    B = T * min(R, E // N)
+    sh = oracle.shape(N, T, H, E, R, fp8, B=B)
+    x = inp["x"].reshape(T, H)
+    xs = None if not fp8 else inp["x_scale"].reshape(T, H // 128)
+    res = oracle.prefill_dispatch(sh, x, xs, idx)
+    res.update(idx=idx, w=w, x=x, xs=xs, sh=sh)
+    return res
+
+
+@pytest.mark.parametrize("case", PREFILL)
+def test_prefill_dispatch_brute(case):
+    N, T, H, E, R, fp8 = case
+    res = run_prefill(*case, seed=3)
+    order, pos = brute.prefill_layout(N, T, E, R, res["idx"])
+    L = E // N
+    for (t, k), q in pos.items():
+        assert res["slot_pos"][t, k] == q
+    assert sum(len(o) for o in order) == T * R
+    for d in range(N):
+        assert res["expert_off"][d, 0] == 0 and res["expert_off"][d, L] == len(order[d])
+        for j in range(L):
+            assert res["expert_cnt"][d, j] == sum(1 for z in order[d] if z[0] == j)
+            assert res["expert_off"][d, j + 1] - res["expert_off"][d, j] == res["expert_cnt"][d, j]
+        for q, (j, t, k) in enumerate(order[d]):
+            assert res["expert_src"][d, q] == t * R + k
+            assert res["expert_x"][d, q].tobytes() == res["x"][t].tobytes()
+            if fp8:
+                assert res["expert_scale"][d, q].tobytes() == res["xs"][t].tobytes()
+        assert len(order[d]) <= T * min(R, L)
+
+
+def test_prefill_single_rank_equals_decode_layout():
+    # with one rank, replicated-input dispatch and the decode path's receive side agree
+    N, T, H, E, R = 1, 12, 16, 9, 3
+    res = run_prefill(N, T, H, E, R, False, seed=5)
+    dec = run_small(N, T, H, E, R, False, seed=5)
+    n = int(dec["expert_off"][0, -1])
+    assert np.array_equal(res["expert_off"], dec["expert_off"])
+    assert np.array_equal(res["expert_src"][0, :n], dec["expert_src"][0, :n])
+    assert np.array_equal(res["expert_x"][0, :n], dec["expert_x"][0, :n])
+
+
+@pytest.mark.parametrize("case", PREFILL)
+def test_prefill_combine_identity_closed_form(case):
+    # identity experts: out = bf16(x * sum_k w_k) whichever rank each slot lives on
+    N, T, H, E, R, fp8 = case
+    res = run_prefill(*case, seed=4)
+    sh = res["sh"]
+    y = oracle.expert(sh, 0, res["expert_x"], res["expert_scale"], res["expert_off"])
+    c = oracle.prefill_combine(sh, 0, y, res["slot_pos"], res["idx"], res["w"])
+    inp = {"x": res["x"][None], "x_scale": None if not fp8 else res["xs"][None]}
+    for t in range(T):
+        yv = _dequant_bf16(inp, 0, t, fp8)
+        sw = sum(Fraction(float(res["w"][t, k])) for k in range(R))
+        want = [brute.bf16_round_exact(brute.bf16_bits_to_fraction(int(v) & 0x7FFF) * sw *
+                                       (-1 if int(v) & 0x8000 else 1)) for v in yv]
+        assert list(c["out"][t]) == want
+
+
+@pytest.mark.parametrize("case", PREFILL[:2] + PREFILL[4:])
+def test_prefill_combine_fp32_steps_brute(case):
+    # mode 1 (fp32 partials per rank in slot order, then an fp32 sum over ranks in order) against
+    # exact-rational emulation of each fp32 operation, on random mixed-sign expert outputs
+    N, T, H, E, R, fp8 = case
+    res = run_prefill(*case, seed=6)
+    sh = res["sh"]
+    L = E // N
+    y = ms.random_y(N, sh.B, H, seed=8)
+    c = oracle.prefill_combine(sh, 1, y, res["slot_pos"], res["idx"], res["w"])
+    for t in range(T):
+        for h in range(H):
+            parts = []
+            for d in range(N):
+                acc = np.float32(0.0)
+                for k in range(R):
+                    e = int(res["idx"][t, k])
+                    if e // L != d:
+                        continue
+                    yv = brute.bf16_bits_to_fraction(int(y[d, res["slot_pos"][t, k], h]))
+                    acc = brute.fma_f32_exact(res["w"][t, k], yv, acc)
+                assert c["partial"][d, t, h] == acc
+                parts.append(acc)
+            s_ = np.float32(0.0)
+            for p_ in parts:
+                s_ = brute.f32_round_exact(Fraction(float(s_)) + Fraction(float(p_)))
+            assert c["out"][t, h] == brute.bf16_round_exact(Fraction(float(s_)))
+
+
+def test_prefill_allreduce_rank_order():
+    # partials 2^28, -2^28 and 0.25 on ranks 0, 1, 2: summed in rank order the big ones cancel
+    # first and 0.25 survives (the exact result); any other order absorbs 0.25 into 2^28 in fp32
+    N, T, H, E, R = 3, 1, 8, 3, 3
+    sh = oracle.shape(N, T, H, E, R, False, B=1)
+    idx = np.array([[0, 1, 2]], np.int32)
+    w = np.full((1, 3), 0.25, np.float32)
+    x = np.zeros((T, H), np.uint16)
+    res = oracle.prefill_dispatch(sh, x, None, idx)
+    assert res["slot_pos"].tolist() == [[0, 0, 0]]
+    y = np.zeros((N, 1, H), np.uint16)
+    y[0, 0, :] = oracle.bf16_from_double(2.0 ** 30)
+    y[1, 0, :] = oracle.bf16_from_double(-2.0 ** 30)
+    y[2, 0, :] = oracle.bf16_from_double(1.0)
+    quarter = oracle.bf16_from_double(0.25)
+    for mode in (0, 1):
+        c = oracle.prefill_combine(sh, mode, y, res["slot_pos"], idx, w)
+        assert np.all(c["out"] == quarter), mode
+    c = oracle.prefill_combine(sh, 1, y, res["slot_pos"], idx, w)
+    assert c["partial"][:, 0, 0].tolist() == [2.0 ** 28, -2.0 ** 28, 0.25]
+
+
+@pytest.mark.parametrize("case", [PREFILL[1], PREFILL[2]])
+def test_prefill_combine_tagged_closed_form(case):
+    # tagged experts: out = bf16(sum_k w_k * bf16(x * c_{e_k})): each slot's weight meets the row
+    # of that slot's expert on that slot's rank
+    N, T, H, E, R, fp8 = case
+    res = run_prefill(*case, seed=7)
+    sh = res["sh"]
+    y = oracle.expert(sh, 1, res["expert_x"], res["expert_scale"], res["expert_off"])
+    c = oracle.prefill_combine(sh, 0, y, res["slot_pos"], res["idx"], res["w"])
+    tab = brute.e4m3_table()
+    for t in range(T):
+        for h in range(0, H, max(1, H // 16)):
+            if fp8:
+                xv = tab[int(res["x"][t, h])] * Fraction(float(res["xs"][t, h // 128]))
+            else:
+                b_ = int(res["x"][t, h])
+                xv = brute.bf16_bits_to_fraction(b_ & 0x7FFF) * (-1 if b_ & 0x8000 else 1)
+            acc = Fraction(0)
+            for k in range(R):
+                e = int(res["idx"][t, k])
+                yk = brute.bf16_round_exact(xv * Fraction(64 + e % 64, 64))
+                acc += Fraction(float(res["w"][t, k])) * brute.bf16_bits_to_fraction(yk & 0x7FFF) * \
+                    (-1 if yk & 0x8000 else 1)
+            assert c["out"][t, h] == brute.bf16_round_exact(acc), (t, h)
+
+
 def test_dispatch_invariants_at_scale():
     # DeepSeek-V3-shaped routing with a tiny payload: invariants the method fixes at any size
     N, T, H, E, R = 32, 128, 8, 256, 8
