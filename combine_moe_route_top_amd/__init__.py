@@ -32,6 +32,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP, MOE_EBADIDX = 0, -1, -2, -3, -5
 MOE_BF16, MOE_FP8_E4M3, MOE_BF16_TO_FP8 = 0, 1, 2
+MOE_LAYOUT_DECODE, MOE_LAYOUT_PREFILL = 0, 1
 
 
 class moe_shape(ctypes.Structure):
@@ -39,13 +40,14 @@ class moe_shape(ctypes.Structure):
                 ("E", ctypes.c_int32), ("R", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("rank_begin", ctypes.c_int32), ("rank_count", ctypes.c_int32),
                 ("capacity", ctypes.c_int64), ("status", ctypes.c_void_p),
-                ("tokens", ctypes.c_void_p)]
+                ("tokens", ctypes.c_void_p), ("layout", ctypes.c_int32)]
 
 
 _SIZE_FIELDS = ["capacity", "row_bytes", "logits", "bias", "topk_idx", "topk_w", "x", "x_scale",
                 "counts", "send_off", "send_pos", "send_buf", "send_meta", "recv_buf",
                 "recv_meta", "recv_off", "expert_x", "expert_scale", "expert_cnt", "expert_off",
-                "expert_src", "expert_rpos", "expert_y", "cs_buf", "cr_buf", "out", "workspace"]
+                "expert_src", "expert_rpos", "expert_y", "cs_buf", "cr_buf", "out", "workspace",
+                "slot_pos", "partial"]
 
 
 class moe_sizes_t(ctypes.Structure):
@@ -63,6 +65,10 @@ _SIGS = {
     "moe_combine_send": [ctypes.POINTER(moe_shape)] + [_vp] * 7,
     "moe_combine_recv": [ctypes.POINTER(moe_shape)] + [_vp] * 5,
     "moe_expert_stub": [ctypes.POINTER(moe_shape), ctypes.c_int32] + [_vp] * 5,
+    "moe_prefill_dispatch": [ctypes.POINTER(moe_shape)] + [_vp] * 11,
+    "moe_prefill_combine_local": [ctypes.POINTER(moe_shape)] + [_vp] * 6,
+    "moe_prefill_allreduce": [ctypes.POINTER(moe_shape)] + [_vp] * 3,
+    "moe_prefill_combine": [ctypes.POINTER(moe_shape)] + [_vp] * 7,
     "moe_strerror": [ctypes.c_int],
     "moe_abi_version": [],
 }
@@ -112,18 +118,19 @@ def _check(name, rc):
 
 
 def make_shape(N, T, H, E, R, fp8=False, capacity=0, status=None, rank_begin=0,
-               rank_count=0, quant=False, tokens=None) -> moe_shape:
+               rank_count=0, quant=False, tokens=None, prefill=False) -> moe_shape:
     """quant: bf16 tokens quantised to e4m3 rows by the send pack (MOE_BF16_TO_FP8);
-    tokens: a device int32[N] tensor of per-rank token counts, or None."""
+    tokens: a device int32[N] tensor of per-rank token counts, or None;
+    prefill: the replicated-token layout (MOE_LAYOUT_PREFILL)."""
     dtype = MOE_BF16_TO_FP8 if quant else (MOE_FP8_E4M3 if fp8 else MOE_BF16)
     return moe_shape(N, T, H, E, R, dtype, rank_begin, rank_count, capacity, _ptr(status),
-                     _ptr(tokens))
+                     _ptr(tokens), MOE_LAYOUT_PREFILL if prefill else MOE_LAYOUT_DECODE)
 
 
 def for_ranks(shape: moe_shape, rank_begin: int, rank_count: int) -> moe_shape:
     """The same shape restricted to ranks [rank_begin, rank_begin + rank_count)."""
     return moe_shape(shape.N, shape.T, shape.H, shape.E, shape.R, shape.dtype, rank_begin,
-                     rank_count, shape.capacity, shape.status, shape.tokens)
+                     rank_count, shape.capacity, shape.status, shape.tokens, shape.layout)
 
 
 def moe_sizes(shape: moe_shape) -> dict:
@@ -184,6 +191,31 @@ def moe_expert_stub(shape, mode, expert_x, expert_scale, expert_off, expert_y, s
     _check("moe_expert_stub", _lib.moe_expert_stub(
         ctypes.byref(shape), int(mode), _ptr(expert_x), _ptr(expert_scale), _ptr(expert_off),
         _ptr(expert_y), _stream(stream)))
+
+
+def moe_prefill_dispatch(shape, x, x_scale, topk_idx, slot_pos, expert_x, expert_scale,
+                         expert_cnt, expert_off, expert_src, workspace, stream=None):
+    _check("moe_prefill_dispatch", _lib.moe_prefill_dispatch(
+        ctypes.byref(shape), _ptr(x), _ptr(x_scale), _ptr(topk_idx), _ptr(slot_pos),
+        _ptr(expert_x), _ptr(expert_scale), _ptr(expert_cnt), _ptr(expert_off), _ptr(expert_src),
+        _ptr(workspace), _stream(stream)))
+
+
+def moe_prefill_combine_local(shape, expert_y, topk_idx, slot_pos, topk_w, partial, stream=None):
+    _check("moe_prefill_combine_local", _lib.moe_prefill_combine_local(
+        ctypes.byref(shape), _ptr(expert_y), _ptr(topk_idx), _ptr(slot_pos), _ptr(topk_w),
+        _ptr(partial), _stream(stream)))
+
+
+def moe_prefill_allreduce(shape, partial, out, stream=None):
+    _check("moe_prefill_allreduce", _lib.moe_prefill_allreduce(
+        ctypes.byref(shape), _ptr(partial), _ptr(out), _stream(stream)))
+
+
+def moe_prefill_combine(shape, expert_y, topk_idx, slot_pos, topk_w, partial, out, stream=None):
+    _check("moe_prefill_combine", _lib.moe_prefill_combine(
+        ctypes.byref(shape), _ptr(expert_y), _ptr(topk_idx), _ptr(slot_pos), _ptr(topk_w),
+        _ptr(partial), _ptr(out), _stream(stream)))
 
 
 # ------------------------------------------------------------------ buffers (plumbing)
@@ -252,6 +284,48 @@ def alloc_buffers(N, T, H, E, R, fp8=False, capacity=0, device="cuda", with_stat
     if tokens:
         shape.tokens = t["tokens"].data_ptr()
     return Buffers(shape, sz, t)
+
+
+def alloc_prefill_buffers(N, T, H, E, R, fp8=False, capacity=0, device="cuda",
+                          with_status=True) -> Buffers:
+    """Every buffer of the replicated-token (prefill) path for one shape (contents undefined)."""
+    shape = make_shape(N, T, H, E, R, fp8, capacity, prefill=True)
+    sz = moe_sizes(shape)
+    B = sz["capacity"]
+    L = E // N
+    dev = torch.device(device)
+    i32, f32, u8, i16 = torch.int32, torch.float32, torch.uint8, torch.int16
+    xdt = u8 if fp8 else i16
+    t = dict(
+        logits=torch.empty((T, E), dtype=f32, device=dev),
+        bias=torch.zeros((E,), dtype=f32, device=dev),
+        topk_idx=torch.empty((T, R), dtype=i32, device=dev),
+        topk_w=torch.empty((T, R), dtype=f32, device=dev),
+        x=torch.empty((T, H), dtype=xdt, device=dev),
+        x_scale=torch.empty((T, H // 128), dtype=f32, device=dev) if fp8 else None,
+        slot_pos=torch.empty((T, R), dtype=i32, device=dev),
+        expert_x=torch.empty((N, B, H), dtype=xdt, device=dev),
+        expert_scale=torch.empty((N, B, H // 128), dtype=f32, device=dev) if fp8 else None,
+        expert_cnt=torch.empty((N, L), dtype=i32, device=dev),
+        expert_off=torch.empty((N, L + 1), dtype=i32, device=dev),
+        expert_src=torch.empty((N, B), dtype=i32, device=dev),
+        expert_y=torch.empty((N, B, H), dtype=i16, device=dev),
+        partial=torch.empty((N, T, H), dtype=f32, device=dev),
+        out=torch.empty((T, H), dtype=i16, device=dev),
+        workspace=torch.empty((max(sz["workspace"], 16),), dtype=u8, device=dev),
+        status=torch.zeros((1,), dtype=i32, device=dev) if with_status else None,
+    )
+    if with_status:
+        shape.status = t["status"].data_ptr()
+    return Buffers(shape, sz, t)
+
+
+def run_prefill_dispatch(b: Buffers, bias=True, stream=None):
+    """route -> prefill dispatch on the buffers' replicated inputs."""
+    moe_route(b.shape, b.logits, b.bias if bias else None, b.topk_idx, b.topk_w, stream)
+    moe_prefill_dispatch(b.shape, b.x, b.x_scale, b.topk_idx, b.slot_pos, b.expert_x,
+                         b.expert_scale, b.expert_cnt, b.expert_off, b.expert_src, b.workspace,
+                         stream)
 
 
 def run_dispatch(b: Buffers, bias=True, stream=None):

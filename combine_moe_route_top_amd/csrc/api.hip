@@ -23,6 +23,12 @@ hipError_t launch_combine_send(const Dims&, const uint16_t*, const int32_t*, con
                                const int32_t*, uint16_t*, uint16_t*, hipStream_t);
 hipError_t launch_combine_recv(const Dims&, const uint16_t*, const int32_t*, const float*, uint16_t*,
                                hipStream_t);
+size_t prefill_workspace_bytes(const Dims&);
+hipError_t launch_prefill_dispatch(const Dims&, const void*, const float*, const int32_t*, int32_t*, void*,
+                                   float*, int32_t*, int32_t*, int32_t*, void*, hipStream_t);
+hipError_t launch_prefill_local(const Dims&, const uint16_t*, const int32_t*, const int32_t*, const float*,
+                                float*, hipStream_t);
+hipError_t launch_prefill_allreduce(const Dims&, const float*, uint16_t*, hipStream_t);
 }  // namespace moe
 
 using moe::Dims;
@@ -41,6 +47,10 @@ int make_dims(const moe_shape* sh, Dims* D) {
     if (E % N != 0 || R > E) return MOE_EINVAL;
     if (sh->dtype != MOE_BF16 && sh->dtype != MOE_FP8_E4M3 && sh->dtype != MOE_BF16_TO_FP8)
         return MOE_EINVAL;
+    if (sh->layout != MOE_LAYOUT_DECODE && sh->layout != MOE_LAYOUT_PREFILL) return MOE_EINVAL;
+    const bool prefill = sh->layout == MOE_LAYOUT_PREFILL;
+    if (prefill && sh->tokens) return MOE_EINVAL;                        // one replicated token set
+    if (prefill && sh->dtype == MOE_BF16_TO_FP8) return MOE_EUNSUPPORTED;
     if (N > kMaxN || E > kMaxE || R > kMaxR) return MOE_EUNSUPPORTED;
     const bool fp8 = sh->dtype != MOE_BF16;  // e4m3 rows, given or made by the send pack
     if (!fp8 && H % 8 != 0) return MOE_EUNSUPPORTED;   // 16-byte rows
@@ -48,8 +58,9 @@ int make_dims(const moe_shape* sh, Dims* D) {
     const long long L = E / N;
     const long long TR = T * R;
     if (N * TR > INT_MAX || E * TR > INT_MAX) return MOE_EUNSUPPORTED;  // int32 indices, meta
-    const long long tight = N * T * (R < L ? R : L);
-    const long long bound = N * T * (R > L ? R : L);
+    const long long S = prefill ? 1 : N;  // token sets: one per rank, or one replicated set
+    const long long tight = S * T * (R < L ? R : L);
+    const long long bound = S * T * (R > L ? R : L);
     const long long B = sh->capacity == 0 ? bound : sh->capacity;
     if (B < tight) return MOE_EINVAL;
     if (B > INT_MAX) return MOE_EUNSUPPORTED;
@@ -62,6 +73,7 @@ int make_dims(const moe_shape* sh, Dims* D) {
     D->L = (int)L;
     D->fp8 = fp8;
     D->quant = sh->dtype == MOE_BF16_TO_FP8;
+    D->prefill = prefill;
     if (sh->tokens && reinterpret_cast<uintptr_t>(sh->tokens) % 4 != 0) return MOE_EINVAL;
     D->tok = sh->tokens;
     D->TR = (int)TR;
@@ -107,7 +119,8 @@ int moe_sizes(const moe_shape* shape, moe_sizes_t* out) {
     if (rc) return rc;
     if (!out) return MOE_EINVAL;
     const int64_t N = D.N, T = D.T, H = D.H, E = D.E, R = D.R, L = D.L, B = D.B, P = D.P;
-    const int64_t NT = N * T, M = N * T * R;
+    const int64_t S = D.prefill ? 1 : N;  // token sets
+    const int64_t NT = S * T, M = S * T * R;
     const int64_t xb = D.fp8 ? 1 : 2;  // bytes per value of expert_x
     out->capacity = B;
     out->row_bytes = P;
@@ -117,27 +130,34 @@ int moe_sizes(const moe_shape* shape, moe_sizes_t* out) {
     out->topk_w = M * 4;
     out->x = NT * H * (D.quant ? 2 : xb);
     out->x_scale = D.fp8 && !D.quant ? NT * (H / 128) * 4 : 0;
-    out->counts = N * E * 4;
-    out->send_off = N * (N + 1) * 4;
-    out->send_pos = M * 4;
-    out->send_buf = M * P;
-    out->send_meta = M * 8;
-    out->recv_buf = N * B * P;
-    out->recv_meta = N * B * 8;
-    out->recv_off = N * (N + 1) * 4;
+    const bool dec = !D.prefill;  // the decode path's send/receive staging
+    out->counts = dec ? N * E * 4 : 0;
+    out->send_off = dec ? N * (N + 1) * 4 : 0;
+    out->send_pos = dec ? M * 4 : 0;
+    out->send_buf = dec ? M * P : 0;
+    out->send_meta = dec ? M * 8 : 0;
+    out->recv_buf = dec ? N * B * P : 0;
+    out->recv_meta = dec ? N * B * 8 : 0;
+    out->recv_off = dec ? N * (N + 1) * 4 : 0;
     out->expert_x = N * B * H * xb;
     out->expert_scale = D.fp8 ? N * B * (H / 128) * 4 : 0;
     out->expert_cnt = N * L * 4;
     out->expert_off = N * (L + 1) * 4;
     out->expert_src = N * B * 4;
-    out->expert_rpos = N * B * 4;
+    out->expert_rpos = dec ? N * B * 4 : 0;
     out->expert_y = N * B * H * 2;
-    out->cs_buf = N * B * H * 2;
-    out->cr_buf = M * H * 2;
+    out->cs_buf = dec ? N * B * H * 2 : 0;
+    out->cr_buf = dec ? M * H * 2 : 0;
     out->out = NT * H * 2;
-    size_t ws = moe::send_workspace_bytes(D);
-    size_t wr = moe::recv_workspace_bytes(D);
-    out->workspace = (int64_t)(ws > wr ? ws : wr);
+    out->slot_pos = D.prefill ? M * 4 : 0;
+    out->partial = D.prefill ? N * T * H * 4 : 0;
+    if (D.prefill) {
+        out->workspace = (int64_t)moe::prefill_workspace_bytes(D);
+    } else {
+        size_t ws = moe::send_workspace_bytes(D);
+        size_t wr = moe::recv_workspace_bytes(D);
+        out->workspace = (int64_t)(ws > wr ? ws : wr);
+    }
     return MOE_OK;
 }
 
@@ -157,6 +177,7 @@ int moe_dispatch_send(const moe_shape* shape, const void* x, const float* x_scal
     Dims D;
     int rc = make_dims(shape, &D);
     if (rc) return rc;
+    if (D.prefill) return MOE_EINVAL;  // the decode layout only
     if (!aligned(x, 16) || !aligned(send_buf, 16) || !aligned(send_meta, 8)) return MOE_EINVAL;
     if (D.fp8 && !D.quant && !aligned(x_scale, 16)) return MOE_EINVAL;
     if (D.quant && x_scale) return MOE_EINVAL;  // the scales are made here
@@ -173,6 +194,7 @@ int moe_net_dispatch(const moe_shape* shape, const int32_t* send_off, const void
     Dims D;
     int rc = make_dims(shape, &D);
     if (rc) return rc;
+    if (D.prefill) return MOE_EINVAL;  // the decode layout only
     if (!aligned(send_off, 4) || !aligned(send_buf, 16) || !aligned(send_meta, 8) ||
         !aligned(recv_buf, 16) || !aligned(recv_meta, 8) || !aligned(recv_off, 4))
         return MOE_EINVAL;
@@ -187,6 +209,7 @@ int moe_dispatch_recv(const moe_shape* shape, const int32_t* counts, const int32
     Dims D;
     int rc = make_dims(shape, &D);
     if (rc) return rc;
+    if (D.prefill) return MOE_EINVAL;  // the decode layout only
     if (!aligned(counts, 4) || !aligned(recv_off, 4) || !aligned(recv_buf, 16) ||
         !aligned(recv_meta, 8) || !aligned(expert_x, 16) || !aligned(expert_cnt, 4) ||
         !aligned(expert_off, 4) || !aligned(expert_src, 4) || !aligned(expert_rpos, 4))
@@ -204,6 +227,7 @@ int moe_combine_send(const moe_shape* shape, const uint16_t* expert_y, const int
     Dims D;
     int rc = make_dims(shape, &D);
     if (rc) return rc;
+    if (D.prefill) return MOE_EINVAL;  // the decode layout only
     if (!aligned(expert_y, 16) || !aligned(expert_rpos, 4) || !aligned(recv_off, 4) ||
         !aligned(send_off, 4) || !aligned(cs_buf, 16) || !aligned(cr_buf, 16))
         return MOE_EINVAL;
@@ -216,6 +240,7 @@ int moe_combine_recv(const moe_shape* shape, const uint16_t* cr_buf, const int32
     Dims D;
     int rc = make_dims(shape, &D);
     if (rc) return rc;
+    if (D.prefill) return MOE_EINVAL;  // the decode layout only
     if (!aligned(cr_buf, 16) || !aligned(send_pos, 4) || !aligned(topk_w, 4) || !aligned(out, 16))
         return MOE_EINVAL;
     return hip_status(moe::launch_combine_recv(D, cr_buf, send_pos, topk_w, out, (hipStream_t)stream));
@@ -227,6 +252,7 @@ int moe_combine(const moe_shape* shape, const uint16_t* expert_y, const int32_t*
     Dims D;
     int rc = make_dims(shape, &D);
     if (rc) return rc;
+    if (D.prefill) return MOE_EINVAL;  // the decode layout only
     // validate both halves before launching either
     if (!aligned(expert_y, 16) || !aligned(expert_rpos, 4) || !aligned(recv_off, 4) ||
         !aligned(send_off, 4) || !aligned(send_pos, 4) || !aligned(topk_w, 4) ||
@@ -249,6 +275,68 @@ int moe_expert_stub(const moe_shape* shape, int32_t mode, const void* expert_x,
     if (D.fp8 && !aligned(expert_scale, 4)) return MOE_EINVAL;
     return hip_status(moe::launch_expert_stub(D, mode, expert_x, expert_scale, expert_off, expert_y,
                                               (hipStream_t)stream));
+}
+
+}  // extern "C"
+
+extern "C" {
+
+int moe_prefill_dispatch(const moe_shape* shape, const void* x, const float* x_scale,
+                         const int32_t* topk_idx, int32_t* slot_pos, void* expert_x,
+                         float* expert_scale, int32_t* expert_cnt, int32_t* expert_off,
+                         int32_t* expert_src, void* workspace, void* stream) {
+    Dims D;
+    int rc = make_dims(shape, &D);
+    if (rc) return rc;
+    if (!D.prefill) return MOE_EINVAL;
+    if (!aligned(x, 16) || !aligned(topk_idx, 4) || !aligned(slot_pos, 4) || !aligned(expert_x, 16) ||
+        !aligned(expert_cnt, 4) || !aligned(expert_off, 4) || !aligned(expert_src, 4))
+        return MOE_EINVAL;
+    if (D.fp8 && (!aligned(x_scale, 16) || !aligned(expert_scale, 16))) return MOE_EINVAL;
+    if (moe::prefill_workspace_bytes(D) > 0 && !aligned(workspace, 4)) return MOE_EINVAL;
+    return hip_status(moe::launch_prefill_dispatch(D, x, x_scale, topk_idx, slot_pos, expert_x,
+                                                   expert_scale, expert_cnt, expert_off, expert_src,
+                                                   workspace, (hipStream_t)stream));
+}
+
+int moe_prefill_combine_local(const moe_shape* shape, const uint16_t* expert_y,
+                              const int32_t* topk_idx, const int32_t* slot_pos, const float* topk_w,
+                              float* partial, void* stream) {
+    Dims D;
+    int rc = make_dims(shape, &D);
+    if (rc) return rc;
+    if (!D.prefill) return MOE_EINVAL;
+    if (!aligned(expert_y, 16) || !aligned(topk_idx, 4) || !aligned(slot_pos, 4) ||
+        !aligned(topk_w, 4) || !aligned(partial, 16))
+        return MOE_EINVAL;
+    return hip_status(moe::launch_prefill_local(D, expert_y, topk_idx, slot_pos, topk_w, partial,
+                                                (hipStream_t)stream));
+}
+
+int moe_prefill_allreduce(const moe_shape* shape, const float* partial, uint16_t* out, void* stream) {
+    Dims D;
+    int rc = make_dims(shape, &D);
+    if (rc) return rc;
+    if (!D.prefill) return MOE_EINVAL;
+    if (!aligned(partial, 16) || !aligned(out, 16)) return MOE_EINVAL;
+    return hip_status(moe::launch_prefill_allreduce(D, partial, out, (hipStream_t)stream));
+}
+
+int moe_prefill_combine(const moe_shape* shape, const uint16_t* expert_y, const int32_t* topk_idx,
+                        const int32_t* slot_pos, const float* topk_w, float* partial, uint16_t* out,
+                        void* stream) {
+    Dims D;
+    int rc = make_dims(shape, &D);
+    if (rc) return rc;
+    if (!D.prefill) return MOE_EINVAL;
+    // validate both steps before launching either
+    if (!aligned(expert_y, 16) || !aligned(topk_idx, 4) || !aligned(slot_pos, 4) ||
+        !aligned(topk_w, 4) || !aligned(partial, 16) || !aligned(out, 16))
+        return MOE_EINVAL;
+    rc = hip_status(moe::launch_prefill_local(D, expert_y, topk_idx, slot_pos, topk_w, partial,
+                                              (hipStream_t)stream));
+    if (rc) return rc;
+    return hip_status(moe::launch_prefill_allreduce(D, partial, out, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -19,6 +19,7 @@ struct Dims {
     int fp8;           // e4m3 payload rows (codes, then fp32 block scales)
     int quant;         // the send pack makes those rows from bf16 tokens
     const int32_t* tok;  // device int32[N]: tokens each rank dispatches, or NULL (T for all)
+    int prefill;       // replicated tokens: the same T tokens on every rank
     int TR;            // T * R: rows each rank sends
     long long B;       // receive-side rows per rank
     int P;             // bytes of one dispatched row
@@ -112,11 +113,13 @@ __device__ __forceinline__ int wave_sum(int v) {
 }
 
 // At most how many rows the call's ranks receive in total: every rank receives at most
-// N*T*min(R, L) rows (one per routed slot, distinct experts per token), and all ranks together
-// exactly the N*T*R routed rows.
+// S*T*min(R, L) rows (one per routed slot, distinct experts per token) from the S token sets
+// (N sources; one replicated set for prefill), and all ranks together exactly the S*T*R routed
+// rows.
 inline long recv_rows_bound(const Dims& D) {
-    const long per_rank = (long)D.N * D.T * (D.R < D.L ? D.R : D.L);
-    const long all = (long)D.N * D.TR;
+    const long S = D.prefill ? 1 : D.N;
+    const long per_rank = S * D.T * (D.R < D.L ? D.R : D.L);
+    const long all = S * D.TR;
     const long b = (long)D.rc * per_rank;
     return b < all ? b : all;
 }

@@ -14,6 +14,7 @@
 #include <algorithm>
 
 #include "common.cuh"
+#include "slots.cuh"
 
 // Waves the send packs aim for (the grid is one token per wave when there are at least this many
 // tokens); overridable at build time for launch-shape experiments.
@@ -27,46 +28,6 @@
 namespace moe {
 
 // ------------------------------------------------------------------ count and scan
-
-// Slot (t, k) of rank s is valid if its expert id is in range and differs from the ids of the
-// token's earlier slots.  Invalid slots are dropped and flagged in the status word.  `chunk`
-// holds the ids of slots c0 .. c0 + n - 1 in LDS; earlier slots come from global memory.
-__device__ __forceinline__ bool slot_valid(const int32_t* __restrict__ idx_s, const int* chunk,
-                                           long c0, long n, long i, int R, int E, int& e) {
-    e = chunk[i - c0];
-    if (e < 0 || e >= E) return false;
-    const long t0 = (i / R) * R;
-    for (long j = t0; j < i; ++j) {
-        const int o = (j >= c0 && j < c0 + n) ? chunk[j - c0] : idx_s[j];
-        if (o == e) return false;
-    }
-    return true;
-}
-
-// Stage the ids of slots c0 .. c0 + blockDim - 1 (those below TR) into LDS; returns how many.
-__device__ __forceinline__ long stage_chunk(const int32_t* __restrict__ idx_s, int* chunk, long c0, long TR) {
-    const long n = min((long)blockDim.x, TR - c0);
-    if ((long)threadIdx.x < n) chunk[threadIdx.x] = idx_s[c0 + threadIdx.x];
-    __syncthreads();
-    return n;
-}
-
-// Stable rank of this lane's key among the active lanes of the wave with the same key (lower
-// lanes first); the leader of each key group also stores the group's size in cnt_row[key].
-__device__ __forceinline__ int wave_match_rank(bool active, int key, int* cnt_row) {
-    uint64_t pending = ballot(active);
-    int rank = 0;
-    while (pending) {
-        const int leader = __ffsll((unsigned long long)pending) - 1;
-        const int lkey = readlane(key, leader);
-        const bool mine = active && key == lkey;
-        const uint64_t m = ballot(mine);
-        if (mine) rank = __popcll(m & lanemask_lt());
-        if (lane_id() == leader) cnt_row[lkey] = __popcll(m);
-        pending &= ~m;
-    }
-    return rank;
-}
 
 // Per-chunk expert histogram (only when a rank's T*R slots span several chunks): the counts of
 // earlier chunks give each chunk's starting ranks.  Grid (C, N), one slot per thread.
@@ -492,6 +453,12 @@ static int send_chunk(const Dims& D) {
     // 16 waves per chunk when the per-wave key table fits in 64 KB of LDS, else 4 (E, N <= 1024
     // keeps the 4-wave table under 64 KB)
     return send_rank_lds(D, 1024) <= 64 * 1024 ? 1024 : 256;
+}
+
+hipError_t launch_slot_hist(const Dims& D, const int32_t* topk_idx, int32_t* chunk_cnt, int C, int CH,
+                            int ranks, hipStream_t st) {
+    hipLaunchKernelGGL(k_send_hist, dim3(C, ranks), dim3(CH), (D.E + CH) * 4, st, D, topk_idx, chunk_cnt, C);
+    return hipGetLastError();
 }
 
 size_t send_workspace_bytes(const Dims& D) {

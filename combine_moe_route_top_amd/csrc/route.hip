@@ -142,8 +142,14 @@ static void launch_g(int vpl, dim3 grid, hipStream_t st, const float* logits, co
         hipLaunchKernelGGL((k_route<G, 16>), grid, dim3(kBlock), 0, st, logits, bias, topk_idx, topk_w, D);
 }
 
-hipError_t launch_route(const Dims& D, const float* logits, const float* bias, int32_t* topk_idx,
+hipError_t launch_route(const Dims& D0, const float* logits, const float* bias, int32_t* topk_idx,
                         float* topk_w, hipStream_t st) {
+    // replicated tokens (prefill): one token set of T, routed once whatever the rank range
+    Dims D = D0;
+    if (D.prefill) {
+        D.rb = 0;
+        D.rc = 1;
+    }
     // the tokens of ranks [rb, rb + rc)
     const long t0 = (long)D.rb * D.T;
     const int ntok = D.rc * D.T;

@@ -5,6 +5,7 @@
  *   [EFA]  "Enabling trillion-parameter models on AWS EFA"
  *   [PORT] "Efficient and portable mixture-of-experts communication"
  *   [DSK]  "Lower latency and higher throughput with multi-node DeepSeek deployment"
+ *   [QWEN] "Hosting Qwen on Blackwell"
  *
  * The problem ([EFA], send-buffer design paragraph): N ranks each dispatch T tokens of hidden
  * size H; every token goes to R of E experts; expert e lives on rank e / L, L = E / N.  Here all
@@ -38,7 +39,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 typedef enum {
     MOE_OK = 0,
@@ -60,6 +61,13 @@ typedef enum {
                            +-448.  Everything after the send pack is the MOE_FP8_E4M3 path. */
 } moe_dtype;
 
+typedef enum {
+    MOE_LAYOUT_DECODE = 0,  /* every rank dispatches its own T tokens (the send/network/receive path) */
+    MOE_LAYOUT_PREFILL = 1  /* every rank holds the same T tokens ([QWEN] MoE dispatch-combine, Expert
+                               parallel): moe_prefill_dispatch / moe_prefill_combine(_local) /
+                               moe_prefill_allreduce; x, topk_idx, topk_w and out are [T][...] */
+} moe_layout;
+
 typedef struct {
     int32_t N;          /* ranks (expert-parallel size), 1..1024 */
     int32_t T;          /* tokens dispatched per rank */
@@ -73,8 +81,9 @@ typedef struct {
                              its receive side (dispatch receive, combine shuffle, stand-in expert).
                              Running every rank's calls, each step for all ranks before the next,
                              gives exactly the all-ranks result.  Arrays stay full-size [N][...]. */
-    int64_t capacity;   /* receive-side rows per rank; 0 = N*T*max(R, E/N), the [EFA] bound.
-                           Must be at least N*T*min(R, E/N), the most any rank can receive. */
+    int64_t capacity;   /* receive-side rows per rank; 0 = S*T*max(R, E/N), the [EFA] bound, with
+                           S = N token sets (decode) or 1 (prefill).  Must be at least
+                           S*T*min(R, E/N), the most any rank can receive. */
     int32_t* status;    /* device int32 sticky error word, or NULL */
     const int32_t* tokens; /* device int32[N], or NULL: rank s dispatches only its first
                               tokens[s] (0..T) tokens ([PORT] Portable kernels: T is the most any
@@ -83,7 +92,9 @@ typedef struct {
                               write their rows, their slots get send_pos = -1 and are not counted
                               or sent, and moe_combine(_recv) does not write their output rows.
                               The counts stay on the device; a count outside [0, T] sets
-                              MOE_EINVAL in the status word and counts as 0. */
+                              MOE_EINVAL in the status word and counts as 0.  Decode layout
+                              only (NULL for prefill). */
+    int32_t layout;     /* moe_layout; the calls of the other layout return MOE_EINVAL */
 } moe_shape;
 
 /* Byte sizes of every buffer for a shape.  rows: capacity = B (receive-side rows per rank),
@@ -97,6 +108,7 @@ typedef struct {
     int64_t expert_x, expert_scale, expert_cnt, expert_off, expert_src, expert_rpos;
     int64_t expert_y, cs_buf, cr_buf, out;
     int64_t workspace;
+    int64_t slot_pos, partial;  /* prefill only (0 for decode); decode-only buffers are 0 for prefill */
 } moe_sizes_t;
 
 /* Host only; no GPU needed.  Fills *out for a valid shape, else returns MOE_EINVAL or
@@ -106,7 +118,8 @@ int moe_sizes(const moe_shape* shape, moe_sizes_t* out);
 /* Router.  [DSK] Expert Parallelism and MoE Router: each token takes R experts from a sort of
  * the router scores that tracks indices, and the expert outputs are summed with weights;
  * [PORT] introduction: the weights come from the router's probability distribution.
- *   logits   f32[N*T][E]        router scores
+ *   logits   f32[N*T][E]        router scores ([T][E] for MOE_LAYOUT_PREFILL: the replicated
+ *                                tokens are routed once, whatever the rank range)
  *   bias     f32[E] or NULL     added to every token's scores before selection (one fp32 add)
  *   topk_idx i32[N*T][R] (out)  experts by descending (score + bias), ties to the lower id
  *   topk_w   f32[N*T][R] (out)  softmax over the R selected values, computed in fp64 and
@@ -199,10 +212,51 @@ int moe_combine_recv(const moe_shape* shape, const uint16_t* cr_buf, const int32
  *   mode 0 (identity): y = the dispatched value (bf16 as is; e4m3 decoded times its block
  *          scale, rounded once to bf16)
  *   mode 1 (tagged):   y = bf16(that value * (64 + e % 64) / 64) for the row's expert e
- *   expert_x, expert_scale, expert_off  from moe_dispatch_recv;  expert_y bf16[N][B][H] (out) */
+ *   expert_x, expert_scale, expert_off  from moe_dispatch_recv or moe_prefill_dispatch;
+ *   expert_y bf16[N][B][H] (out).  Both layouts. */
 int moe_expert_stub(const moe_shape* shape, int32_t mode, const void* expert_x,
                     const float* expert_scale, const int32_t* expert_off, uint16_t* expert_y,
                     void* stream);
+
+/* Prefill dispatch (MOE_LAYOUT_PREFILL).  [QWEN] MoE dispatch-combine, Expert parallel: the
+ * inputs are replicated on every rank, so each rank's dispatch only selects the tokens routed to
+ * its own experts and stages them for the grouped GEMM.  No network step: nothing moves between
+ * ranks until the combine's all-reduce.
+ *   x            bf16[T][H] or e4m3 u8[T][H]       the replicated tokens
+ *   x_scale      f32[T][H/128] (e4m3) or NULL
+ *   topk_idx     i32[T][R]                          from moe_route on the same shape (routes T tokens)
+ *   slot_pos     i32[T][R] (out)    row of slot (t, k) in its owner rank's expert-major arrays; -1
+ *                                    for a dropped slot (bad id, flagged as MOE_EBADIDX)
+ *   expert_x     [N][B][H] (out), expert_scale f32[N][B][H/128] (out, e4m3), expert_cnt i32[N][L]
+ *   (out), expert_off i32[N][L+1] (out), expert_src i32[N][B] (out) = t*R + k: rank d's rows in
+ *   (local expert, token, slot) order, as moe_dispatch_recv lays them out for one source
+ *   workspace    device scratch of moe_sizes().workspace bytes (NULL if 0)
+ * With a rank range, only the range's rows and tables are written; slot_pos covers every slot. */
+int moe_prefill_dispatch(const moe_shape* shape, const void* x, const float* x_scale,
+                         const int32_t* topk_idx, int32_t* slot_pos, void* expert_x,
+                         float* expert_scale, int32_t* expert_cnt, int32_t* expert_off,
+                         int32_t* expert_src, void* workspace, void* stream);
+
+/* Prefill combine, local step: [QWEN] MoE dispatch-combine, Expert parallel: each rank first
+ * accumulates the contributions of its own experts.
+ *   expert_y   bf16[N][B][H]       expert outputs in the dispatch's expert-major order
+ *   topk_idx, slot_pos, topk_w    [T][R] from moe_route and moe_prefill_dispatch
+ *   partial    f32[N][T][H] (out)  for each of the call's ranks d and every token t: the fp32
+ *                                   fused-multiply-add chain over t's slots owned by d in slot
+ *                                   order 0..R-1 (0 where d owns none) */
+int moe_prefill_combine_local(const moe_shape* shape, const uint16_t* expert_y,
+                              const int32_t* topk_idx, const int32_t* slot_pos, const float* topk_w,
+                              float* partial, void* stream);
+
+/* Prefill combine, all-reduce (the collective's stand-in): out[t] = bf16 of the fp32 sum of
+ * partial[0][t] .. partial[N-1][t] in rank order, rounded once (nearest even).  Reads every
+ * rank's partial whatever the rank range (each must have been written); out is bf16[T][H]. */
+int moe_prefill_allreduce(const moe_shape* shape, const float* partial, uint16_t* out, void* stream);
+
+/* = moe_prefill_combine_local then moe_prefill_allreduce (all arguments validated first). */
+int moe_prefill_combine(const moe_shape* shape, const uint16_t* expert_y, const int32_t* topk_idx,
+                        const int32_t* slot_pos, const float* topk_w, float* partial, uint16_t* out,
+                        void* stream);
 
 /* Static string for a status code. */
 const char* moe_strerror(int status);

@@ -13,6 +13,8 @@ Workloads (shapes of the models the pages discuss; distributions are synthetic):
   kimi_k2_worst            N=64 T=128  H=7168 E=384 R=8  e4m3 + scales, +16 bias on experts 0..5
   deepseek_v3_decode_fp8q  DeepSeek-V3 decode, bf16 tokens quantised to e4m3 rows by the send pack
   deepseek_v3_decode_ragged DeepSeek-V3 decode (bf16) with a token count per rank, T_s ~ U{1..T}
+  qwen3_235b_prefill_ep    N=4  T=4096 H=4096 E=128 R=8  bf16, the same T tokens on every rank
+                           (prefill expert parallelism with replicated inputs), logits ~N(0,1)
 
 Recipe (seed s, numpy PCG64 ``default_rng``): logits = rng(s).standard_normal((N*T, E), f32);
 then x = rng(s) (same stream, next draw) .standard_normal((N, T, H), f32) rounded to bf16
@@ -53,6 +55,7 @@ class Config:
     desc: str = ""
     quant: bool = False     # tokens arrive as bf16; the send pack makes the e4m3 rows
     tokens: str = "full"    # "full" (T per rank) | "ragged" (T_s uniform on 1..T)
+    layout: str = "decode"  # "decode" (T tokens per rank) | "prefill" (T tokens on every rank)
 
     @property
     def L(self) -> int:
@@ -98,6 +101,9 @@ CONFIGS = {
         Config("deepseek_v3_decode_ragged", 32, 128, 7168, 256, 8, bias="zipf", tokens="ragged",
                desc="DeepSeek-V3-shaped decode, N32 T<=128 H7168 E256 R8 bf16, Zipf bias, "
                     "tokens per rank uniform on 1..128"),
+        Config("qwen3_235b_prefill_ep", 4, 4096, 4096, 128, 8, layout="prefill",
+               desc="Qwen3-235B-shaped prefill with replicated inputs (EP=4), T4096 H4096 E128 R8 "
+                    "bf16"),
     ]
 }
 

@@ -205,3 +205,108 @@ def compare(g: dict, o: dict, N, T, H, E, R, fp8, check_stub=True, check_ulp=Tru
         assert d0.max() <= 1, f"out differs from the fp64 oracle by {d0.max()} bf16 ulp"
         stats["out_exact_vs_fp64"] = float((d0 == 0).mean())
     return stats
+
+
+# ------------------------------------------------------------------ prefill (replicated tokens)
+
+
+def prefill_inputs(T, H, E, R, fp8, bias, seed):
+    """One replicated token set: moe_synth's inputs for a single rank, reshaped to [T][...]."""
+    inp = ms.make_inputs(1, T, H, E, R, fp8, bias, seed)
+    out = dict(logits=inp["logits"], bias=inp["bias"], x=inp["x"].reshape(T, H),
+               x_scale=None if inp["x_scale"] is None else inp["x_scale"].reshape(T, H // 128))
+    return out
+
+
+def gpu_run_prefill(N, T, H, E, R, fp8, inp, expert_mode=0, capacity=0, y=None, split=False,
+                    width=None):
+    """The replicated-token path on the GPU; width: run every call once per range of `width`
+    ranks (each step for all ranges before the next) instead of once for all ranks."""
+    import combine_moe_route_top_amd as moe
+    b = moe.alloc_prefill_buffers(N, T, H, E, R, fp8, capacity)
+    for k, t in b.t.items():
+        if t is not None and k != "status":
+            t.view(torch.uint8).fill_(0xA5)
+    b.status.zero_()
+    upload_inputs(b, inp)
+    shapes = [b.shape] if width is None else \
+        [moe.for_ranks(b.shape, r0, min(width, N - r0)) for r0 in range(0, N, width)]
+    use_bias = inp["bias"] is not None
+    moe.moe_route(b.shape, b.logits, b.bias if use_bias else None, b.topk_idx, b.topk_w)
+    for sh in shapes:
+        moe.moe_prefill_dispatch(sh, b.x, b.x_scale, b.topk_idx, b.slot_pos, b.expert_x,
+                                 b.expert_scale, b.expert_cnt, b.expert_off, b.expert_src,
+                                 b.workspace)
+    if y is None:
+        for sh in shapes:
+            moe.moe_expert_stub(sh, expert_mode, b.expert_x, b.expert_scale, b.expert_off,
+                                b.expert_y)
+    else:
+        b.expert_y.copy_(torch.from_numpy(y.view(np.int16)))
+    if split or width is not None:
+        for sh in shapes:
+            moe.moe_prefill_combine_local(sh, b.expert_y, b.topk_idx, b.slot_pos, b.topk_w,
+                                          b.partial)
+        moe.moe_prefill_allreduce(b.shape, b.partial, b.out)
+    else:
+        moe.moe_prefill_combine(b.shape, b.expert_y, b.topk_idx, b.slot_pos, b.topk_w, b.partial,
+                                b.out)
+    torch.cuda.synchronize()
+    g = {k: _np(getattr(b, k)) for k in ("topk_idx", "topk_w", "slot_pos", "expert_cnt",
+                                          "expert_off", "partial", "out", "status")}
+    eo = g["expert_off"]
+    for k in ("expert_x", "expert_src", "expert_y"):
+        g[k] = [_np(getattr(b, k)[d, :eo[d, -1]]) for d in range(N)]
+    if fp8:
+        g["expert_scale"] = [_np(b.expert_scale[d, :eo[d, -1]]) for d in range(N)]
+    return b, g
+
+
+def oracle_run_prefill(N, T, H, E, R, fp8, inp, expert_mode=0, y=None):
+    idx, w = oracle.route(inp["logits"], inp["bias"], R)
+    B = T * min(R, E // N)          # the most any rank receives; keeps host arrays small
+    sh = oracle.shape(N, T, H, E, R, fp8, B=B)
+    res = dict(topk_idx=idx, topk_w=w, shape=sh)
+    res.update(oracle.prefill_dispatch(sh, inp["x"], inp["x_scale"], idx))
+    if y is None:
+        res["expert_y"] = oracle.expert(sh, expert_mode, res["expert_x"], res["expert_scale"],
+                                        res["expert_off"])
+    else:
+        res["expert_y"] = np.ascontiguousarray(y[:, :B], np.uint16)
+    for mode in (0, 1):
+        c = oracle.prefill_combine(sh, mode, res["expert_y"], res["slot_pos"], idx, w)
+        res[f"out{mode}"] = c["out"]
+        if mode == 1:
+            res["partial"] = c["partial"]
+    return res
+
+
+def compare_prefill(g, o, N, T, H, E, R, fp8, check_stub=True, check_ulp=True):
+    """Bit-exact layout and payload; partials and out bit-exact against the oracle's fp32 steps
+    wherever the router weights agree bit for bit, and out within 1 bf16 ulp of the fp64 sum."""
+    stats = {}
+    assert g["status"][0] == 0, f"device status word {g['status'][0]}"
+    assert np.array_equal(g["topk_idx"], o["topk_idx"]), "topk_idx"
+    ulp = np.abs(g["topk_w"].view(np.int32).astype(np.int64) - o["topk_w"].view(np.int32).astype(np.int64))
+    assert ulp.max() <= 1, f"topk_w differs by {ulp.max()} fp32 ulp"
+    assert np.array_equal(g["slot_pos"], o["slot_pos"]), "slot_pos"
+    assert np.array_equal(g["expert_cnt"], o["expert_cnt"]), "expert_cnt"
+    assert np.array_equal(g["expert_off"], o["expert_off"]), "expert_off"
+    for d in range(N):
+        n = int(o["expert_off"][d, -1])
+        assert np.array_equal(g["expert_x"][d], o["expert_x"][d, :n]), f"expert_x rank {d}"
+        if fp8:
+            assert np.array_equal(g["expert_scale"][d], o["expert_scale"][d, :n]), f"expert_scale {d}"
+        assert np.array_equal(g["expert_src"][d], o["expert_src"][d, :n]), f"expert_src rank {d}"
+        if check_stub:
+            assert np.array_equal(g["expert_y"][d], o["expert_y"][d, :n]), f"expert_y rank {d}"
+    same_w = np.all(g["topk_w"] == o["topk_w"], axis=1)
+    assert np.array_equal(g["partial"][:, same_w].view(np.uint32),
+                          o["partial"][:, same_w].view(np.uint32)), "partial vs fp32 steps"
+    assert np.array_equal(g["out"][same_w], o["out1"][same_w]), "out vs the oracle's fp32 steps"
+    stats["fp32_step_tokens"] = int(same_w.sum())
+    if check_ulp:
+        d0 = _bf16_ulp_diff(g["out"], o["out0"])
+        assert d0.max() <= 1, f"out differs from the fp64 oracle by {d0.max()} bf16 ulp"
+        stats["out_exact_vs_fp64"] = float((d0 == 0).mean())
+    return stats

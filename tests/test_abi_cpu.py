@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strerror():
-    assert moe.moe_abi_version() == 3
+    assert moe.moe_abi_version() == 4
     for code in (0, -1, -2, -3, -5, 42):
         assert isinstance(moe.moe_strerror(code), str)
 
@@ -79,6 +79,56 @@ def test_bad_rank_ranges(rb, rc):
     assert ex.value.code == moe.MOE_EINVAL
 
 
+def test_prefill_layout_sizes_and_guards():
+    sh = moe.make_shape(4, 4096, 4096, 128, 8, prefill=True)
+    sz = moe.moe_sizes(sh)
+    assert sz["capacity"] == 4096 * 32                 # T*max(R, E/N): one token set
+    assert sz["x"] == 4096 * 4096 * 2 and sz["logits"] == 4096 * 128 * 4
+    assert sz["slot_pos"] == 4096 * 8 * 4 and sz["partial"] == 4 * 4096 * 4096 * 4
+    assert sz["out"] == 4096 * 4096 * 2 and sz["send_buf"] == 0 and sz["recv_buf"] == 0
+    assert sz["workspace"] >= 32 * 128 * 4             # 32 count chunks of 1024 slots
+    dec = moe.moe_sizes(moe.make_shape(4, 4096, 4096, 128, 8))
+    assert dec["slot_pos"] == 0 and dec["partial"] == 0
+    # the tight bound T*min(R, E/N) is the least capacity
+    moe.moe_sizes(moe.make_shape(4, 64, 256, 32, 8, capacity=64 * 8, prefill=True))
+    with pytest.raises(moe.MoeError) as ex:
+        moe.moe_sizes(moe.make_shape(4, 64, 256, 32, 8, capacity=64 * 8 - 1, prefill=True))
+    assert ex.value.code == moe.MOE_EINVAL
+    with pytest.raises(moe.MoeError) as ex:           # one replicated token set: no counts
+        moe.moe_sizes(moe.make_shape(2, 16, 256, 8, 2, prefill=True, tokens=1 << 20))
+    assert ex.value.code == moe.MOE_EINVAL
+    with pytest.raises(moe.MoeError) as ex:
+        moe.moe_sizes(moe.make_shape(2, 16, 512, 8, 2, quant=True, prefill=True))
+    assert ex.value.code == moe.MOE_EUNSUPPORTED
+    with pytest.raises(moe.MoeError) as ex:           # unknown layout
+        moe.moe_sizes(moe.moe_shape(2, 16, 256, 8, 2, 0, 0, 0, 0, None, None, 2))
+    assert ex.value.code == moe.MOE_EINVAL
+    good = 1 << 20
+    psh = moe.make_shape(2, 16, 256, 8, 2, prefill=True)
+    dsh = moe.make_shape(2, 16, 256, 8, 2)
+    wrong_layout = [
+        lambda: moe.moe_dispatch_send(psh, good, None, good, good, good, good, good, good, good, stream=0),
+        lambda: moe.moe_net_dispatch(psh, good, good, good, good, good, good, stream=0),
+        lambda: moe.moe_dispatch_recv(psh, good, good, good, good, good, None, good, good, good,
+                                      good, None, stream=0),
+        lambda: moe.moe_combine(psh, good, good, good, good, good, good, good, good, good, stream=0),
+        lambda: moe.moe_combine_send(psh, good, good, good, good, good, good, stream=0),
+        lambda: moe.moe_combine_recv(psh, good, good, good, good, stream=0),
+        lambda: moe.moe_prefill_dispatch(dsh, good, None, good, good, good, None, good, good,
+                                         good, good, stream=0),
+        lambda: moe.moe_prefill_combine_local(dsh, good, good, good, good, good, stream=0),
+        lambda: moe.moe_prefill_allreduce(dsh, good, good, stream=0),
+        lambda: moe.moe_prefill_combine(dsh, good, good, good, good, good, good, stream=0),
+        lambda: moe.moe_prefill_combine(psh, good, good, good, good, good, good + 4, stream=0),
+        lambda: moe.moe_prefill_dispatch(psh, good + 4, None, good, good, good, None, good, good,
+                                         good, good, stream=0),
+    ]
+    for fn in wrong_layout:
+        with pytest.raises(moe.MoeError) as ex:
+            fn()
+        assert ex.value.code == moe.MOE_EINVAL
+
+
 def test_good_rank_ranges():
     for rb, rc in [(0, 0), (0, 4), (3, 1), (1, 2)]:
         moe.moe_sizes(moe.make_shape(4, 16, 256, 8, 2, rank_begin=rb, rank_count=rc))
@@ -92,7 +142,7 @@ def test_bad_fp8_hidden_and_capacity():
         moe.moe_sizes(moe.make_shape(2, 16, 256, 8, 2, quant=True))
     assert ex.value.code == moe.MOE_EUNSUPPORTED
     with pytest.raises(moe.MoeError) as ex:                          # unknown dtype
-        moe.moe_sizes(moe.moe_shape(2, 16, 512, 8, 2, 3, 0, 0, 0, None, None))
+        moe.moe_sizes(moe.moe_shape(2, 16, 512, 8, 2, 3, 0, 0, 0, None, None, 0))
     assert ex.value.code == moe.MOE_EINVAL
     with pytest.raises(moe.MoeError) as ex:                          # below the tight bound
         moe.moe_sizes(moe.make_shape(2, 16, 256, 8, 2, capacity=2 * 16 * 2 - 1))
