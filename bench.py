@@ -23,7 +23,7 @@ METRIC = "dispatch+combine µs/layer and effective HBM GB/s (fraction of MI355X 
 PEAK_HBM_GBS = 8000.0
 HEADLINE = "deepseek_v3_decode"
 EXTRA = ["deepseek_v3_decode_fp8", "kimi_k2_worst", "deepseek_v3_decode_fp8q",
-         "deepseek_v3_decode_ragged"]
+         "deepseek_v3_decode_ragged", "qwen3_235b_prefill_ep"]
 
 
 def alg_bytes(c) -> dict:
@@ -50,6 +50,105 @@ def alg_bytes(c) -> dict:
     b["dispatch"] = b["route"] + b["dispatch_send"] + b["net_dispatch"] + b["dispatch_recv"]
     b["total"] = b["dispatch"] + b["combine"]
     return b
+
+
+def prefill_alg_bytes(c) -> dict:
+    """Compulsory bytes of the replicated-token (prefill) calls: the T tokens are read once,
+    every slot's row written once to its owner rank and read once by the local combine, every
+    rank writes a partial of every token and the all-reduce reads them all."""
+    N, T, H, E, R, L = c.N, c.T, c.H, c.E, c.R, c.L
+    M = T * R
+    P = (H + 4 * (H // 128)) if c.fp8 else 2 * H
+    Pc = 2 * H
+    bias = E * 4 if c.bias != "none" else 0
+    b = {"route": T * E * 4 + bias + M * 8,
+         "prefill_dispatch": M * 16 + T * P + M * P + M * 4 + N * (2 * L + 1) * 4,
+         "combine_local": M * Pc + N * M * 12 + N * T * H * 4,
+         "allreduce": N * T * H * 4 + T * Pc}
+    b["dispatch"] = b["route"] + b["prefill_dispatch"]
+    b["combine"] = b["combine_local"] + b["allreduce"]
+    b["total"] = b["dispatch"] + b["combine"]
+    return b
+
+
+def run_prefill_workload(name, steps, warmup, check=True):
+    """The replicated-token path: route -> prefill dispatch | (stand-in expert, untimed) |
+    local combine -> all-reduce, per call timed with HIP events on the kernels' stream."""
+    import numpy as np
+    import torch
+
+    import combine_moe_route_top_amd as moe
+    import moe_synth as ms
+
+    c = ms.CONFIGS[name]
+    inp = ms.make_inputs(1, c.T, c.H, c.E, c.R, c.fp8, c.bias, c.seed)
+    b = moe.alloc_prefill_buffers(c.N, c.T, c.H, c.E, c.R, c.fp8)
+    b.logits.copy_(torch.from_numpy(inp["logits"]))
+    use_bias = inp["bias"] is not None
+    if use_bias:
+        b.bias.copy_(torch.from_numpy(inp["bias"]))
+    x = inp["x"].reshape(c.T, c.H)
+    b.x.copy_(torch.from_numpy(x.view(np.int16) if x.dtype == np.uint16 else x))
+    if c.fp8:
+        b.x_scale.copy_(torch.from_numpy(inp["x_scale"].reshape(c.T, -1)))
+    st = torch.cuda.current_stream()
+    sh = b.shape
+    names = ["route", "prefill_dispatch", "stub", "combine_local", "allreduce"]
+    calls = [
+        lambda: moe.moe_route(sh, b.logits, b.bias if use_bias else None, b.topk_idx, b.topk_w, st),
+        lambda: moe.moe_prefill_dispatch(sh, b.x, b.x_scale, b.topk_idx, b.slot_pos, b.expert_x,
+                                         b.expert_scale, b.expert_cnt, b.expert_off, b.expert_src,
+                                         b.workspace, st),
+        lambda: moe.moe_expert_stub(sh, 0, b.expert_x, b.expert_scale, b.expert_off, b.expert_y, st),
+        lambda: moe.moe_prefill_combine_local(sh, b.expert_y, b.topk_idx, b.slot_pos, b.topk_w,
+                                              b.partial, st),
+        lambda: moe.moe_prefill_allreduce(sh, b.partial, b.out, st),
+    ]
+    for _ in range(warmup):
+        for f in calls:
+            f()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
+    for k in range(steps):
+        for i, f in enumerate(calls):
+            evs[k][i].record(st)
+            f()
+        evs[k][len(calls)].record(st)
+    torch.cuda.synchronize()
+    per = {n: round(sum(evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(steps)) * 1e3 / steps, 2)
+           for i, n in enumerate(names)}
+    ab = prefill_alg_bytes(c)
+    dispatch_us = per["route"] + per["prefill_dispatch"]
+    combine_us = per["combine_local"] + per["allreduce"]
+    layer_us = dispatch_us + combine_us
+    res = dict(workload=name, dtype=c.dtype, layer_us=round(layer_us, 2),
+               dispatch_us=round(dispatch_us, 2), combine_us=round(combine_us, 2), per_call_us=per,
+               gbs=round(ab["total"] / (layer_us * 1e-6) / 1e9, 1),
+               per_call_gbs={n: round(ab[n] / (per[n] * 1e-6) / 1e9, 1)
+                             for n in ["route", "prefill_dispatch", "combine_local", "allreduce"]},
+               alg_bytes=ab["total"])
+    if check:
+        # identity experts: out == bf16(x * sum_k w_k) up to the torch reference's own double
+        # rounding; every slot lands on exactly one rank
+        sw = b.topk_w.double().sum(1, keepdim=True)
+        if c.fp8:
+            xv = (b.x.view(torch.float8_e4m3fn).double() *
+                  b.x_scale.double().repeat_interleave(128, dim=1)).to(torch.bfloat16).double()
+        else:
+            xv = b.x.view(torch.bfloat16).double()
+        want = (xv * sw).to(torch.float32).to(torch.bfloat16).view(torch.int16).int()
+        got = b.out.int()
+        key = lambda u: torch.where(u < 0, -(u & 0x7FFF), u & 0x7FFF)  # noqa: E731
+        ulp = (key(want) - key(got)).abs().max().item()
+        cnt_ok = int(b.expert_cnt.sum().item()) == c.T * c.R
+        if ulp > 2 or not cnt_ok:
+            raise RuntimeError(f"prefill closed-form check failed: {ulp} ulp, counts ok {cnt_ok}")
+        res["check"] = f"ok (max {ulp} bf16 ulp vs identity closed form; every slot on one rank)"
+    if int(b.status.item()) != 0:
+        raise RuntimeError(f"device status word {int(b.status.item())}")
+    del b
+    torch.cuda.empty_cache()
+    return res
 
 
 def run_workload(name, steps, warmup, check=True):
@@ -618,15 +717,26 @@ def main():
               "GPU's HBM (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
     import torch
+
+    import moe_synth as ms
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+    if ms.CONFIGS[args.workload].layout != "decode":
+        print("the headline workload must use the decode layout (prefill workloads run as extras)",
+              file=sys.stderr)
+        sys.exit(2)
 
     calib = None if args.no_copy_calibration else copy_calibration()
     head = run_workload(args.workload, args.steps, args.warmup, check=not args.no_check)
     extras = {}
     for name in [e for e in args.extra.split(",") if e and e != args.workload]:
+        if ms.CONFIGS[name].layout == "prefill":
+            r = run_prefill_workload(name, args.steps, args.warmup, check=not args.no_check)
+            r["frac_of_peak"] = round(r["gbs"] / PEAK_HBM_GBS, 4)
+            extras[name] = r
+            continue
         r = run_workload(name, args.steps, args.warmup, check=not args.no_check)
         extras[name] = {k: (round(v, 2) if isinstance(v, float) else v) for k, v in r.items()
                         if k in ("layer_us", "dispatch_us", "combine_us", "gbs", "per_call_us",

@@ -18,6 +18,15 @@
 #include "common.cuh"
 #include "slots.cuh"
 
+// Launch-shape constants, overridable at build time for experiments: waves per (rank, token) in
+// the local accumulation, and the waves the pack aims for.
+#ifndef MOE_PF_LOCAL_WAVES
+#define MOE_PF_LOCAL_WAVES 4
+#endif
+#ifndef MOE_PF_PACK_MIN_WAVES
+#define MOE_PF_PACK_MIN_WAVES 4096
+#endif
+
 namespace moe {
 
 hipError_t launch_slot_hist(const Dims& D, const int32_t* topk_idx, int32_t* chunk_cnt, int C, int CH,
@@ -152,7 +161,7 @@ __global__ __launch_bounds__(kBlock) void k_pf_pack(Dims D, int WPT, const uint8
 
 // ------------------------------------------------------------------ combine
 
-constexpr int kLocalWaves = 4;  // waves per (rank, token) in the local accumulation
+constexpr int kLocalWaves = MOE_PF_LOCAL_WAVES;  // waves per (rank, token) in the local accumulation
 
 // partial[d][t] = the fp32 fused-multiply-add chain, in slot order, of w[t][k] * y[d][pos(t, k)]
 // over the token's slots k owned by rank d (zero when there are none).  kLocalWaves waves per
@@ -267,7 +276,7 @@ hipError_t launch_prefill_dispatch(const Dims& D, const void* x, const float* x_
                        (const int32_t*)chunk_cnt, C, slot_pos, expert_cnt, expert_off);
     const long ntok = D.T;
     int wpt = 1;
-    while (wpt < 8 && ntok * wpt < 4096 && (long)kWave * wpt * 2 <= D.P16) wpt *= 2;
+    while (wpt < 8 && ntok * wpt < MOE_PF_PACK_MIN_WAVES && (long)kWave * wpt * 2 <= D.P16) wpt *= 2;
     const long waves = ntok * wpt;
     hipLaunchKernelGGL(k_pf_pack<8>, dim3((waves + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock), 0,
                        st, D, wpt, (const uint8_t*)x, x_scale, topk_idx, (const int32_t*)slot_pos,
