@@ -91,11 +91,12 @@ __global__ __launch_bounds__(1024) void k_send_rank(Dims D, const int32_t* __res
     // experts: rank base from earlier chunks, per-wave starting ranks, rank totals
     for (int key = threadIdx.x; key < E; key += blockDim.x) {
         int before = 0, after = 0;
-        for (int cc = 0; cc < C; ++cc) {
-            if (cc == c) continue;
+        const int nc = C > 1 ? C : 0;  // one chunk: no histograms (the workspace may be absent)
+#pragma unroll 8
+        for (int cc = 0; cc < nc; ++cc) {  // independent loads, several in flight
             const int v = chunk_cnt[((long)s * C + cc) * E + key];
-            if (cc < c) before += v;
-            else after += v;
+            before += cc < c ? v : 0;
+            after += cc > c ? v : 0;
         }
         int run = before;
         for (int ww = 0; ww < W; ++ww) {

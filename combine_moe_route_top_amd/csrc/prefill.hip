@@ -18,10 +18,10 @@
 #include "common.cuh"
 #include "slots.cuh"
 
-// Launch-shape constants, overridable at build time for experiments: waves per (rank, token) in
-// the local accumulation, and the waves the pack aims for.
+// Launch-shape constants, overridable at build time for experiments: the most waves per (rank,
+// token) in the local accumulation, and the waves the pack aims for.
 #ifndef MOE_PF_LOCAL_WAVES
-#define MOE_PF_LOCAL_WAVES 4
+#define MOE_PF_LOCAL_WAVES 16
 #endif
 #ifndef MOE_PF_PACK_MIN_WAVES
 #define MOE_PF_PACK_MIN_WAVES 4096
@@ -68,11 +68,12 @@ __global__ __launch_bounds__(1024) void k_pf_rank(Dims D, const int32_t* __restr
     __syncthreads();
     for (int key = threadIdx.x; key < E; key += blockDim.x) {
         int before = 0, after = 0;
-        for (int cc = 0; cc < C; ++cc) {
-            if (cc == c) continue;
+        const int nc = C > 1 ? C : 0;  // one chunk: no histograms (the workspace may be absent)
+#pragma unroll 8
+        for (int cc = 0; cc < nc; ++cc) {  // independent loads, several in flight
             const int v = chunk_cnt[(long)cc * E + key];
-            if (cc < c) before += v;
-            else after += v;
+            before += cc < c ? v : 0;
+            after += cc > c ? v : 0;
         }
         int run = before;
         for (int ww = 0; ww < W; ++ww) {
@@ -161,20 +162,19 @@ __global__ __launch_bounds__(kBlock) void k_pf_pack(Dims D, int WPT, const uint8
 
 // ------------------------------------------------------------------ combine
 
-constexpr int kLocalWaves = MOE_PF_LOCAL_WAVES;  // waves per (rank, token) in the local accumulation
-
 // partial[d][t] = the fp32 fused-multiply-add chain, in slot order, of w[t][k] * y[d][pos(t, k)]
-// over the token's slots k owned by rank d (zero when there are none).  kLocalWaves waves per
-// (rank, token), each owning every kLocalWaves-th group of 64 chunks of 8 hidden values; a lane
-// keeps one chunk (8 fp32 sums) and loads every owned slot's chunk before the multiply-adds.
-__global__ __launch_bounds__(kBlock) void k_pf_local(Dims D, const uint16_t* __restrict__ expert_y,
+// over the token's slots k owned by rank d (zero when there are none).  LW waves per (rank,
+// token), each owning every LW-th group of 64 chunks of 8 hidden values (the launcher picks LW
+// so that a lane has one chunk where it can); a lane keeps one chunk (8 fp32 sums) and loads
+// every owned slot's chunk before the multiply-adds.
+__global__ __launch_bounds__(kBlock) void k_pf_local(Dims D, int LW, const uint16_t* __restrict__ expert_y,
                                                      const int32_t* __restrict__ topk_idx,
                                                      const int32_t* __restrict__ slot_pos,
                                                      const float* __restrict__ topk_w,
                                                      float* __restrict__ partial) {
     const long gw = (long)blockIdx.x * kWavesPerBlock + wave_id();
-    const long item = gw / kLocalWaves;  // (rank in the call, token)
-    const int part = (int)(gw - item * kLocalWaves);
+    const long item = gw / LW;  // (rank in the call, token)
+    const int part = (int)(gw - item * LW);
     if (item >= (long)D.rc * D.T) return;
     const int lane = lane_id();
     const int R = D.R;
@@ -187,7 +187,7 @@ __global__ __launch_bounds__(kBlock) void k_pf_local(Dims D, const uint16_t* __r
     const u32x4* yrows = reinterpret_cast<const u32x4*>(expert_y + (size_t)d * D.B * D.H);
     u32x4* prow = reinterpret_cast<u32x4*>(partial + ((size_t)d * D.T + t) * D.H);
     const int n16 = D.Y16;
-    for (int c = part * kWave + lane; c < n16; c += kWave * kLocalWaves) {
+    for (int c = part * kWave + lane; c < n16; c += kWave * LW) {
         float acc[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) acc[u] = 0.0f;
@@ -287,9 +287,10 @@ hipError_t launch_prefill_dispatch(const Dims& D, const void* x, const float* x_
 hipError_t launch_prefill_local(const Dims& D, const uint16_t* expert_y, const int32_t* topk_idx,
                                 const int32_t* slot_pos, const float* topk_w, float* partial,
                                 hipStream_t st) {
-    const long waves = (long)D.rc * D.T * kLocalWaves;
+    const int LW = (int)std::min<long>(MOE_PF_LOCAL_WAVES, std::max<long>(1, (D.Y16 + kWave - 1) / kWave));
+    const long waves = (long)D.rc * D.T * LW;
     hipLaunchKernelGGL(k_pf_local, dim3((waves + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock), 0,
-                       st, D, expert_y, topk_idx, slot_pos, topk_w, partial);
+                       st, D, LW, expert_y, topk_idx, slot_pos, topk_w, partial);
     return hipGetLastError();
 }
 
