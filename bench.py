@@ -302,6 +302,42 @@ def closed_form_check(b, c) -> str:
     return f"ok (max {ulp} bf16 ulp vs identity closed form; counts sum to T_s*R)"
 
 
+def kernel_text(src: str, name: str):
+    """The definition of kernel (or device function) `name` in a source text: from its
+    template/__global__/__device__ line to the brace that closes its body, or None."""
+    import re
+    m = re.search(r"^(template <[^\n]*>\n)?(__global__|__device__)[^\n]*\b" + re.escape(name) + r"\(",
+                  src, re.M)
+    if not m:
+        return None
+    i = src.index("{", m.end())
+    depth = 0
+    for j in range(i, len(src)):
+        depth += {"{": 1, "}": -1}.get(src[j], 0)
+        if depth == 0:
+            return src[m.start():j + 1]
+    return None
+
+
+def source_digest(spec: str):
+    """sha256 over the sources a kernel is built from: comma-separated files, where
+    `file#kernel` stands for that kernel's own definition in the file."""
+    import hashlib
+    h = hashlib.sha256()
+    for item in spec.split(","):
+        rel, _, kern = item.partition("#")
+        path = os.path.join(ROOT, rel)
+        if not os.path.exists(path):
+            return None
+        text = open(path).read()
+        if kern:
+            text = kernel_text(text, kern)
+            if text is None:
+                return None
+        h.update(text.encode())
+    return h.hexdigest()
+
+
 def traffic_record(kernel, workload):
     """Scaled FETCH_SIZE + WRITE_SIZE bytes per launch from the committed counter summary, or
     None if there is none or the kernel's source changed since the counters were taken."""
@@ -314,13 +350,8 @@ def traffic_record(kernel, workload):
                          r"source=(\S+) sha256=([0-9a-f]+)", line.strip())
             if not m or m.group(1) != kernel or m.group(2) != workload:
                 continue
-            h = hashlib.sha256()
-            for rel in m.group(4).split(","):     # every source file the kernel is built from
-                src = os.path.join(ROOT, rel)
-                if not os.path.exists(src):
-                    return None
-                h.update(open(src, "rb").read())
-            if h.hexdigest() != m.group(5):
+            digest = source_digest(m.group(4))
+            if digest is None or digest != m.group(5):
                 return None
             return int(m.group(3))
     return None
