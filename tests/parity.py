@@ -168,8 +168,8 @@ def compare(g: dict, o: dict, N, T, H, E, R, fp8, check_stub=True, check_ulp=Tru
     assert np.array_equal(gi[present], o["topk_idx"][present]), "topk_idx"
     gw, ow = g["topk_w"].reshape(N * T, R)[present], o["topk_w"][present]
     ulp = np.abs(gw.view(np.int32).astype(np.int64) - ow.view(np.int32).astype(np.int64))
-    assert ulp.max() <= 1, f"topk_w differs by {ulp.max()} fp32 ulp"
-    stats["w_exact"] = float((ulp == 0).mean())
+    assert ulp.max(initial=0) <= 1, f"topk_w differs by {ulp.max()} fp32 ulp"
+    stats["w_exact"] = float((ulp == 0).mean()) if ulp.size else 1.0
     assert np.array_equal(g["counts"], o["counts"]), "counts"
     assert np.array_equal(g["send_off"], o["send_off"]), "send_off"
     assert np.array_equal(g["send_pos"], o["send_pos"]), "send_pos"
@@ -202,8 +202,8 @@ def compare(g: dict, o: dict, N, T, H, E, R, fp8, check_stub=True, check_ulp=Tru
     stats["fma_chain_tokens"] = int(same_w.sum())
     if check_ulp:
         d0 = _bf16_ulp_diff(out, o["out0"].reshape(N * T, H)[present])
-        assert d0.max() <= 1, f"out differs from the fp64 oracle by {d0.max()} bf16 ulp"
-        stats["out_exact_vs_fp64"] = float((d0 == 0).mean())
+        assert d0.max(initial=0) <= 1, f"out differs from the fp64 oracle by {d0.max()} bf16 ulp"
+        stats["out_exact_vs_fp64"] = float((d0 == 0).mean()) if d0.size else 1.0
     return stats
 
 

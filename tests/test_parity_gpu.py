@@ -330,6 +330,38 @@ def test_tight_capacity():
     parity.compare(g, o, N, T, H, E, R, False)
 
 
+# the ABI's largest N, E and R with small T and H: tables over 1024 ranks, 1024 experts,
+# 64 slots per token (the router's 64-lane groups with 16 experts per lane)
+LIMITS = [
+    (1024, 2, 8, 1024, 4, False, "none"),     # N = E = 1024: one expert per rank
+    (4, 16, 64, 1024, 64, False, "zipf"),     # R = 64 of E = 1024
+    (16, 9, 512, 1024, 64, True, "none"),     # R = 64, e4m3, 64 experts per rank
+]
+
+
+@pytest.mark.parametrize("case", LIMITS, ids=_case_id)
+def test_largest_supported_shapes(case):
+    N, T, H, E, R, fp8, bias = case
+    print(f"\ncase limits {_case_id(case)}", flush=True)
+    inp = ms.make_inputs(N, T, H, E, R, fp8, bias, 0)
+    _, g = parity.gpu_run(N, T, H, E, R, fp8, inp, split_combine=True)
+    o = parity.oracle_run(N, T, H, E, R, fp8, inp)
+    parity.compare(g, o, N, T, H, E, R, fp8)
+
+
+def test_no_tokens_anywhere():
+    # every rank dispatches zero tokens: empty counts, segments and receive sides everywhere; no
+    # output row is written and every kernel still finishes
+    N, T, H, E, R = 8, 33, 64, 32, 4
+    print("\ncase zero tokens", flush=True)
+    inp = ms.make_inputs(N, T, H, E, R, False, "none", 1)
+    tokens = np.zeros(N, np.int32)
+    _, g = parity.gpu_run(N, T, H, E, R, False, inp, tokens=tokens)
+    o = parity.oracle_run(N, T, H, E, R, False, inp, tokens=tokens)
+    parity.compare(g, o, N, T, H, E, R, False)
+    assert g["counts"].sum() == 0 and g["recv_off"].sum() == 0 and g["expert_off"].sum() == 0
+
+
 def test_everything_to_one_rank():
     # bias +16 on rank 0's experts with R <= L: every slot goes to rank 0, the other ranks
     # receive nothing (empty segments and empty ranks everywhere)
