@@ -689,19 +689,23 @@ def rank_leg(name, steps=20, warmup=3) -> dict:
     out = {"workload": name, "rows_received": {}}
     for label, r in picks.items():
         sh = moe.for_ranks(b.shape, r, 1)
-        fns = [
-            lambda: moe.moe_route(sh, b.logits, b.bias if use_bias else None, b.topk_idx, b.topk_w, st),
-            lambda: moe.moe_dispatch_send(sh, b.x, b.x_scale, b.topk_idx, b.counts, b.send_off,
-                                          b.send_pos, b.send_buf, b.send_meta, b.workspace, st),
-            lambda: moe.moe_net_dispatch(sh, b.send_off, b.send_buf, b.send_meta, b.recv_buf,
-                                         b.recv_meta, b.recv_off, st),
-            lambda: moe.moe_dispatch_recv(sh, b.counts, b.recv_off, b.recv_buf, b.recv_meta,
-                                          b.expert_x, b.expert_scale, b.expert_cnt, b.expert_off,
-                                          b.expert_src, b.expert_rpos, b.workspace, st),
-            lambda: moe.moe_combine_send(sh, y, b.expert_rpos, b.recv_off, b.send_off, b.cs_buf,
-                                         b.cr_buf, st),
-            lambda: moe.moe_combine_recv(sh, b.cr_buf, b.send_pos, b.topk_w, b.out, st),
-        ]
+
+        def calls_on(s_):
+            return [
+                lambda: moe.moe_route(sh, b.logits, b.bias if use_bias else None, b.topk_idx,
+                                      b.topk_w, s_),
+                lambda: moe.moe_dispatch_send(sh, b.x, b.x_scale, b.topk_idx, b.counts, b.send_off,
+                                              b.send_pos, b.send_buf, b.send_meta, b.workspace, s_),
+                lambda: moe.moe_net_dispatch(sh, b.send_off, b.send_buf, b.send_meta, b.recv_buf,
+                                             b.recv_meta, b.recv_off, s_),
+                lambda: moe.moe_dispatch_recv(sh, b.counts, b.recv_off, b.recv_buf, b.recv_meta,
+                                              b.expert_x, b.expert_scale, b.expert_cnt, b.expert_off,
+                                              b.expert_src, b.expert_rpos, b.workspace, s_),
+                lambda: moe.moe_combine_send(sh, y, b.expert_rpos, b.recv_off, b.send_off, b.cs_buf,
+                                             b.cr_buf, s_),
+                lambda: moe.moe_combine_recv(sh, b.cr_buf, b.send_pos, b.topk_w, b.out, s_),
+            ]
+        fns = calls_on(st)
         for _ in range(warmup):
             for f in fns:
                 f()
@@ -715,8 +719,30 @@ def rank_leg(name, steps=20, warmup=3) -> dict:
         torch.cuda.synchronize()
         per = {n: round(sum(evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(steps)) * 1e3 / steps, 2)
                for i, n in enumerate(calls)}
+        # the rank's layer captured once in a HIP graph and replayed: no host launch per call
+        side = torch.cuda.Stream()
+        side.wait_stream(st)
+        for f in calls_on(side):
+            f()
+        st.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for f in calls_on(torch.cuda.current_stream()):
+                f()
+        torch.cuda.synchronize()
+        for _ in range(warmup):
+            graph.replay()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(st)
+        for _ in range(steps):
+            graph.replay()
+        g1.record(st)
+        torch.cuda.synchronize()
         out[label] = {"rank": r, "rows_received": int(recv[r]), "us_per_layer": round(sum(per.values()), 2),
+                      "graph_replay_us_per_layer": round(g0.elapsed_time(g1) * 1e3 / steps, 2),
                       "per_call_us": per}
+        del graph
     status = int(b.status.item())
     if status != 0:
         raise RuntimeError(f"device status word {status}")
