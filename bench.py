@@ -151,7 +151,12 @@ def run_prefill_workload(name, steps, warmup, check=True):
     return res
 
 
-def run_workload(name, steps, warmup, check=True):
+def run_workload(name, steps, warmup, check=True, flush_mall=False):
+    """One decode-layout workload: per-call HIP-event times (mean and median over the steps),
+    graph replay time, and the closed-form check.  flush_mall: read a 1 GiB scratch buffer
+    between steps (outside every timed call) so the 256 MB memory-side cache holds none of the
+    previous step's data.  A read, not a write: written lines would stay dirty and be written
+    back during the next step's first calls."""
     import numpy as np
     import torch
 
@@ -208,16 +213,20 @@ def run_workload(name, steps, warmup, check=True):
         step()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
+    scratch = torch.zeros(1 << 28, dtype=torch.int32, device="cuda") if flush_mall else None
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(steps):
+        if scratch is not None:
+            scratch.sum()
         step(evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = {n: 0.0 for n in names}
-    for k in range(steps):
-        for i, n in enumerate(names):
-            per[n] += evs[k][i].elapsed_time(evs[k][i + 1]) * 1e3 / steps   # us
+    samples = {n: [evs[k][i].elapsed_time(evs[k][i + 1]) * 1e3 for k in range(steps)]   # us
+               for i, n in enumerate(names)}
+    per = {n: float(np.mean(v)) for n, v in samples.items()}
+    med = {n: round(float(np.median(v)), 2) for n, v in samples.items()}
+    del scratch
     dispatch_us = per["route"] + per["dispatch_send"] + per["net_dispatch"] + per["dispatch_recv"]
     combine_us = per["combine"]
     layer_us = dispatch_us + combine_us
@@ -226,6 +235,8 @@ def run_workload(name, steps, warmup, check=True):
                layer_us=layer_us, dispatch_us=dispatch_us, combine_us=combine_us,
                wall_ms_per_step=wall * 1e3 / steps,
                per_call_us={n: round(v, 2) for n, v in per.items()},
+               per_call_median_us=med,
+               layer_median_us=round(sum(v for n, v in med.items() if n != "stub"), 2),
                alg_bytes=ab, gbs=ab["total"] / (layer_us * 1e-6) / 1e9)
     res["per_call_gbs"] = {n: round(ab[n] / (per[n] * 1e-6) / 1e9, 1)
                            for n in ["route", "dispatch_send", "net_dispatch", "dispatch_recv", "combine"]}
@@ -768,6 +779,9 @@ def main():
                     help="skip the one-rank-share timing leg")
     ap.add_argument("--no-microbatch", action="store_true",
                     help="skip the two-micro-batch pipelining leg")
+    ap.add_argument("--flush-mall", action="store_true",
+                    help="read a 1 GiB scratch buffer between timed steps (untimed by the "
+                         "per-call events; included in ms_per_step)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the N expert-parallel ranks are simulated inside one "
@@ -786,7 +800,8 @@ def main():
         sys.exit(2)
 
     calib = None if args.no_copy_calibration else copy_calibration()
-    head = run_workload(args.workload, args.steps, args.warmup, check=not args.no_check)
+    head = run_workload(args.workload, args.steps, args.warmup, check=not args.no_check,
+                        flush_mall=args.flush_mall)
     extras = {}
     for name in [e for e in args.extra.split(",") if e and e != args.workload]:
         if ms.CONFIGS[name].layout == "prefill":
@@ -794,10 +809,11 @@ def main():
             r["frac_of_peak"] = round(r["gbs"] / PEAK_HBM_GBS, 4)
             extras[name] = r
             continue
-        r = run_workload(name, args.steps, args.warmup, check=not args.no_check)
+        r = run_workload(name, args.steps, args.warmup, check=not args.no_check,
+                         flush_mall=args.flush_mall)
         extras[name] = {k: (round(v, 2) if isinstance(v, float) else v) for k, v in r.items()
-                        if k in ("layer_us", "dispatch_us", "combine_us", "gbs", "per_call_us",
-                                 "per_call_gbs", "check", "dtype")}
+                        if k in ("layer_us", "layer_median_us", "dispatch_us", "combine_us", "gbs",
+                                 "per_call_us", "per_call_median_us", "per_call_gbs", "check", "dtype")}
         extras[name]["frac_of_peak"] = round(r["gbs"] / PEAK_HBM_GBS, 4)
     line = {
         "metric": METRIC,
@@ -821,6 +837,9 @@ def main():
         "frac_of_peak": round(head["gbs"] / PEAK_HBM_GBS, 4),
         "alg_bytes_per_layer": head["alg_bytes"]["total"],
         "per_call_us": head["per_call_us"],
+        "us_per_layer_median": head["layer_median_us"],
+        "per_call_median_us": head["per_call_median_us"],
+        "mall_flushed_between_steps": bool(args.flush_mall),
         "per_call_gbs": head["per_call_gbs"],
         "graph_replay_us_per_step": head["graph_replay_us_per_step"],
         "check": head.get("check"),
