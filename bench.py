@@ -414,7 +414,16 @@ def cpu_baseline(name, budget_s=25.0) -> dict:
         if time.perf_counter() - t_start > budget_s * 0.5 or len(times) >= 3:
             break
     t = float(np.median(times))
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": round(ab["total"] / t / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "host_cpus": os.cpu_count(), "cpu_model": model,
             "us_per_layer": round(t * 1e6, 1),
             "sample": f"one full {name} layer (all {c.N} ranks) through the single-threaded C oracle "
                       f"(route, dispatch, network, unpack, combine; stand-in expert excluded), "
