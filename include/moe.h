@@ -70,7 +70,8 @@ typedef enum {
 
 typedef struct {
     int32_t N;          /* ranks (expert-parallel size), 1..1024 */
-    int32_t T;          /* tokens dispatched per rank */
+    int32_t T;          /* tokens per rank (decode: each rank's own; prefill: the one set every
+                           rank holds) */
     int32_t H;          /* hidden size; multiple of 8 (bf16) or 512 (fp8) */
     int32_t E;          /* experts, multiple of N, at most 1024 */
     int32_t R;          /* experts per token, 1..min(E, 64) */
