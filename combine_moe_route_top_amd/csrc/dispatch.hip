@@ -1,10 +1,12 @@
 // dispatch.hip -- MoE dispatch: per-expert counts and exclusive-scan offsets, the pack into
-// send buffers contiguous per destination rank, the network stand-in, and the unpack into
-// expert-major order.
+// send buffers contiguous per destination rank (optionally quantising bf16 tokens to e4m3 rows
+// on the way), the network stand-in, and the unpack into expert-major order.  Ranks may
+// dispatch fewer than T tokens (per-rank counts on the device); absent tokens take no part.
 //
 // Pages: [EFA] = "Enabling trillion-parameter models on AWS EFA" (send-buffer design paragraph;
 // dispatch timing paragraph), [PORT] = "Efficient and portable mixture-of-experts
-// communication" (sections Portable kernels and Dispatch).
+// communication" (sections Portable kernels and Dispatch), [DSK] = "Lower latency and higher
+// throughput with multi-node DeepSeek deployment" (Implementation: Quantization, Cuda Graph).
 //
 // Orders (all stable, so every output has exactly one correct value):
 //  - send buffer of rank s: rows grouped by destination rank d = e / L, (token, slot) order
