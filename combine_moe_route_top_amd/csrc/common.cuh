@@ -222,14 +222,6 @@ inline StreamShape stream_shape(int n16, int min_chunks) {
 // The (RPB, U) instances a launcher may pick.
 #define MOE_STREAM_SHAPES(X) \
     X(1, 1) X(1, 2) X(1, 4) X(1, 8) X(2, 1) X(2, 2) X(2, 4) X(2, 8) X(4, 1) X(4, 2) X(4, 4) X(4, 8)
-inline StreamShape stream_shape(int n16) {
-    int rpb = 1;
-    while (rpb < kWavesPerBlock && (rpb * 2) * n16 <= kBlock) rpb *= 2;
-    const int per_thread = (rpb * n16 + kBlock - 1) / kBlock;
-    int u = 1;
-    while (u < per_thread && u < 8) u *= 2;
-    return {rpb, u};
-}
 
 // Global row bases over ranks, gb[d] = sum over d' < d of table[d' * stride + col], gb[N] = the
 // total; computed by wave 0 into LDS (the caller synchronises).
