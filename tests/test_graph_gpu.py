@@ -66,3 +66,41 @@ def test_graph_replay_matches_eager(case):
     # and the last replay against the oracle
     o = parity.oracle_run(N, T, H, E, R, fp8, inputs[-1], expert_mode=1)
     parity.compare(gg, o, N, T, H, E, R, fp8)
+
+
+def test_graph_replay_with_changing_token_counts():
+    # one captured layer serves every batch mix: the per-rank token counts live on the device and
+    # are rewritten between replays; every replay matches the oracle for that mix, and rows of
+    # absent tokens keep what was there before
+    import combine_moe_route_top_amd as moe
+    N, T, H, E, R = 8, 64, 512, 64, 8
+    print("\ncase graph with token counts", flush=True)
+    b = moe.alloc_buffers(N, T, H, E, R, tokens=True)
+    inp = ms.make_inputs(N, T, H, E, R, False, "zipf", 3)
+    parity.upload_inputs(b, inp)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        _layer(moe, b, True, False)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        _layer(moe, b, True, False)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(9)
+    mixes = [np.full(N, T, np.int32), rng.integers(0, T + 1, N).astype(np.int32),
+             np.zeros(N, np.int32), rng.integers(1, T + 1, N).astype(np.int32)]
+    for i, tokens in enumerate(mixes):
+        print(f"  replay {i} tokens {tokens.tolist()}", flush=True)
+        b.out.fill_(0x5A5A)
+        b.topk_idx.fill_(-5)
+        b.tokens.copy_(torch.from_numpy(tokens))
+        graph.replay()
+        torch.cuda.synchronize()
+        g = parity.fetch(b, N, T, R)
+        present = (np.arange(T)[None, :] < tokens[:, None])
+        assert np.all(g["out"][~present] == 0x5A5A), i
+        assert np.all(g["topk_idx"].reshape(N, T, R)[~present] == -5), i
+        o = parity.oracle_run(N, T, H, E, R, False, inp, expert_mode=1, tokens=tokens)
+        parity.compare(g, o, N, T, H, E, R, False)
