@@ -381,7 +381,7 @@ def dominant_kernel(res) -> dict:
             "bytes_per_launch": ab["net_dispatch"], "us_per_launch": round(us, 2)}
 
 
-def cpu_baseline(name, budget_s=25.0) -> dict:
+def cpu_baseline(name, budget_s=20.0) -> dict:
     """The oracle, as it stands, on one full layer of the workload on the host cores."""
     import numpy as np
 
@@ -411,7 +411,8 @@ def cpu_baseline(name, budget_s=25.0) -> dict:
         oracle.combine(sh, 0, y, r["expert_rpos"], r["recv_off"], r["send_off"], r["send_pos"], w)
         t3 = time.perf_counter()
         times.append((t1 - t0) + (t3 - t2))
-        if time.perf_counter() - t_start > budget_s * 0.5 or len(times) >= 3:
+        # about budget_s/2 .. budget_s of host work: at least 3 layers, at most 20
+        if len(times) >= 20 or (len(times) >= 3 and time.perf_counter() - t_start > budget_s * 0.5):
             break
     t = float(np.median(times))
     model = ""
