@@ -7,6 +7,8 @@
 // accumulated from the receive buffer into the output); [PORT] = "Efficient and portable
 // mixture-of-experts communication" (section Combine: 16-bit activations, the receiver forms
 // the weighted average of all expert contributions into an externally allocated tensor).
+#include <algorithm>
+
 #include "common.cuh"
 
 namespace moe {
@@ -187,18 +189,25 @@ __global__ __launch_bounds__(kBlock) void k_combine_net(Dims D, const uint16_t* 
 }
 
 // Weighted sum: out[s][t] = bf16(sum_k w[k] * cr[s][send_pos[k]]), fp32 fused multiply-adds in
-// slot order k = 0..R-1; dropped slots (send_pos < 0) add nothing.  kWsumWaves waves per token,
-// each owning every kWsumWaves-th group of 64 chunks; a lane keeps 2 chunks (16 hidden values)
-// and up to 8 slots' loads in flight.
-constexpr int kWsumWaves = 4;
+// slot order k = 0..R-1; dropped slots (send_pos < 0) add nothing.  WW waves per token, each
+// owning every WW-th group of 64 chunks; a lane keeps MOE_WSUM_CHUNKS chunks (8 hidden values
+// each) and up to 8 slots' loads in flight.  The launcher picks the fewest waves that cover the
+// row in one pass, at most MOE_WSUM_MAX_WAVES, so that short rows leave no wave idle.
+#ifndef MOE_WSUM_MAX_WAVES
+#define MOE_WSUM_MAX_WAVES 16
+#endif
+#ifndef MOE_WSUM_CHUNKS
+#define MOE_WSUM_CHUNKS 1
+#endif
 
-__global__ __launch_bounds__(kBlock) void k_wsum(Dims D, const uint16_t* __restrict__ cr_buf,
+__global__ __launch_bounds__(kBlock) void k_wsum(Dims D, int WW, const uint16_t* __restrict__ cr_buf,
                                                  const int32_t* __restrict__ send_pos,
                                                  const float* __restrict__ topk_w,
                                                  uint16_t* __restrict__ out) {
-    constexpr int CU = 2;
-    const long tok = ((long)blockIdx.x * kWavesPerBlock + wave_id()) / kWsumWaves;  // call's ranks
-    const int part = wave_id() % kWsumWaves;
+    constexpr int CU = MOE_WSUM_CHUNKS;
+    const long gw = (long)blockIdx.x * kWavesPerBlock + wave_id();
+    const long tok = gw / WW;  // within the call's ranks
+    const int part = (int)(gw - tok * WW);
     if (tok >= (long)D.rc * D.T) return;
     const int lane = lane_id();
     const int R = D.R;
@@ -209,7 +218,7 @@ __global__ __launch_bounds__(kBlock) void k_wsum(Dims D, const uint16_t* __restr
     const u32x4* rank_rows = reinterpret_cast<const u32x4*>(cr_buf + (size_t)s * D.TR * D.H);
     u32x4* orow = reinterpret_cast<u32x4*>(out + (size_t)tok * D.H);
     const int n16 = D.Y16;
-    for (int c0 = part * kWave + lane; c0 < n16; c0 += kWave * kWsumWaves * CU) {
+    for (int c0 = part * kWave + lane; c0 < n16; c0 += kWave * WW * CU) {
         float acc[CU][8];
 #pragma unroll
         for (int cu = 0; cu < CU; ++cu)
@@ -227,7 +236,7 @@ __global__ __launch_bounds__(kBlock) void k_wsum(Dims D, const uint16_t* __restr
                 wk[kk] = k < R ? readlane_f(my_w, k) : 0.0f;
 #pragma unroll
                 for (int cu = 0; cu < CU; ++cu) {
-                    const int c = c0 + cu * kWave * kWsumWaves;
+                    const int c = c0 + cu * kWave * WW;
                     if (ok[kk] && c < n16) v[cu][kk] = ld_nt(rank_rows + (size_t)pos * n16 + c);
                 }
             }
@@ -245,7 +254,7 @@ __global__ __launch_bounds__(kBlock) void k_wsum(Dims D, const uint16_t* __restr
         }
 #pragma unroll
         for (int cu = 0; cu < CU; ++cu) {
-            const int c = c0 + cu * kWave * kWsumWaves;
+            const int c = c0 + cu * kWave * WW;
             if (c < n16) {
                 u32x4 o;
 #pragma unroll
@@ -308,9 +317,11 @@ hipError_t launch_combine_recv(const Dims& D, const uint16_t* cr_buf, const int3
     send_pos += rb * D.TR;
     topk_w += rb * D.T * D.R;
     out += rb * D.T * D.H;
-    const long waves = (long)D.rc * D.T * kWsumWaves;
+    const int WW = (int)std::min<long>(MOE_WSUM_MAX_WAVES, std::max<long>(1, (D.Y16 + MOE_WSUM_CHUNKS * kWave - 1) /
+                                                                      (MOE_WSUM_CHUNKS * kWave)));
+    const long waves = (long)D.rc * D.T * WW;
     hipLaunchKernelGGL(k_wsum, dim3((waves + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock), 0, st, D,
-                       cr_buf, send_pos, topk_w, out);
+                       WW, cr_buf, send_pos, topk_w, out);
     return hipGetLastError();
 }
 

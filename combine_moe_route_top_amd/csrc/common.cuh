@@ -127,7 +127,10 @@ inline long recv_rows_bound(const Dims& D) {
 // Blocks for a row kernel whose rows are only known on the device: one block per RPB rows of
 // the bound when the call covers all ranks (every row exists), at most kSubrangeBlocks when it
 // covers a subset (most of the bound is usually empty; blocks then stride over the rows).
-constexpr long kSubrangeBlocks = 4096;
+#ifndef MOE_SUBRANGE_BLOCKS
+#define MOE_SUBRANGE_BLOCKS 4096
+#endif
+constexpr long kSubrangeBlocks = MOE_SUBRANGE_BLOCKS;
 inline long row_blocks(const Dims& D, long rows_bound, int rpb) {
     long b = (rows_bound + rpb - 1) / rpb;
     if (D.rc < D.N && b > kSubrangeBlocks) b = kSubrangeBlocks;

@@ -86,8 +86,8 @@ __global__ __launch_bounds__(1024) void k_send_rank(Dims D, const int32_t* __res
         if (!valid) set_status(D.status, MOE_EBADIDX);
     }
     const int d = valid ? e / L : 0;
-    const int re = wave_match_rank(valid, e, wcnt + w * K);
-    const int rd = wave_match_rank(valid, E + d, wcnt + w * K);
+    const int re = wave_key_rank(valid, e, key_bits(E), wcnt + w * K);
+    const int rd = wave_key_rank(valid, d, key_bits(N), wcnt + w * K + E);
     __syncthreads();
 
     // experts: rank base from earlier chunks, per-wave starting ranks, rank totals
@@ -100,14 +100,8 @@ __global__ __launch_bounds__(1024) void k_send_rank(Dims D, const int32_t* __res
             before += cc < c ? v : 0;
             after += cc > c ? v : 0;
         }
-        int run = before;
-        for (int ww = 0; ww < W; ++ww) {
-            const int x = wcnt[ww * K + key];
-            wcnt[ww * K + key] = run;
-            run += x;
-        }
         base[key] = before;
-        tot[key] = run + after;
+        tot[key] = column_excl_scan(wcnt + key, K, W, before) + after;
     }
     __syncthreads();
     // destinations: the same from the experts they own
@@ -117,12 +111,7 @@ __global__ __launch_bounds__(1024) void k_send_rank(Dims D, const int32_t* __res
             b += base[ee];
             n += tot[ee];
         }
-        int run = b;
-        for (int ww = 0; ww < W; ++ww) {
-            const int x = wcnt[ww * K + E + dd];
-            wcnt[ww * K + E + dd] = run;
-            run += x;
-        }
+        column_excl_scan(wcnt + E + dd, K, W, b);
         tot[E + dd] = n;
     }
     __syncthreads();

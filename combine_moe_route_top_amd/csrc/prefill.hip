@@ -64,7 +64,7 @@ __global__ __launch_bounds__(1024) void k_pf_rank(Dims D, const int32_t* __restr
         valid = slot_valid(topk_idx, chunk, c0, n, i, D.R, E, e);
         if (!valid) set_status(D.status, MOE_EBADIDX);
     }
-    const int re = wave_match_rank(valid, e, wcnt + w * E);
+    const int re = wave_key_rank(valid, e, key_bits(E), wcnt + w * E);
     __syncthreads();
     for (int key = threadIdx.x; key < E; key += blockDim.x) {
         int before = 0, after = 0;
@@ -75,13 +75,7 @@ __global__ __launch_bounds__(1024) void k_pf_rank(Dims D, const int32_t* __restr
             before += cc < c ? v : 0;
             after += cc > c ? v : 0;
         }
-        int run = before;
-        for (int ww = 0; ww < W; ++ww) {
-            const int x = wcnt[ww * E + key];
-            wcnt[ww * E + key] = run;
-            run += x;
-        }
-        tot[key] = run + after;
+        tot[key] = column_excl_scan(wcnt + key, E, W, before) + after;
     }
     __syncthreads();
     // rows of each rank's earlier experts: a scan over its L experts

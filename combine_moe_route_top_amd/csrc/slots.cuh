@@ -29,21 +29,40 @@ __device__ __forceinline__ long stage_chunk(const int32_t* __restrict__ idx_s, i
     return n;
 }
 
+// Bits needed to hold the keys 0 .. n-1.
+__device__ __forceinline__ int key_bits(int n) { return n > 1 ? 32 - __clz(n - 1) : 0; }
+
 // Stable rank of this lane's key among the active lanes of the wave with the same key (lower
-// lanes first); the leader of each key group also stores the group's size in cnt_row[key].
-__device__ __forceinline__ int wave_match_rank(bool active, int key, int* cnt_row) {
-    uint64_t pending = ballot(active);
-    int rank = 0;
-    while (pending) {
-        const int leader = __ffsll((unsigned long long)pending) - 1;
-        const int lkey = readlane(key, leader);
-        const bool mine = active && key == lkey;
-        const uint64_t m = ballot(mine);
-        if (mine) rank = __popcll(m & lanemask_lt());
-        if (lane_id() == leader) cnt_row[lkey] = __popcll(m);
-        pending &= ~m;
+// lanes first); the lowest lane of each key group also stores the group's size in cnt_row[key].
+// Keys lie in [0, 2^nbits).  The lanes sharing a key are found in constant time, one ballot per
+// key bit (the ballot form of a multisplit): a lane keeps the lanes that agree with it on every
+// bit.
+__device__ __forceinline__ int wave_key_rank(bool active, int key, int nbits, int* cnt_row) {
+    uint64_t same = ballot(active);
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = (key >> b) & 1;
+        const uint64_t ones = ballot(bit);
+        same &= bit ? ones : ~ones;
     }
-    return rank;
+    const uint64_t lower = same & lanemask_lt();
+    if (active && lower == 0) cnt_row[key] = __popcll(same);
+    return __popcll(lower);
+}
+
+// Exclusive running sums down a column of W <= 16 LDS entries col[0], col[stride], ...,
+// starting at `start`, written in place; returns start plus the column's total.  Every load is
+// issued before the first store.
+__device__ __forceinline__ int column_excl_scan(int* col, int stride, int W, int start) {
+    int x[16];
+#pragma unroll
+    for (int ww = 0; ww < 16; ++ww) x[ww] = ww < W ? col[ww * stride] : 0;
+    int run = start;
+#pragma unroll
+    for (int ww = 0; ww < 16; ++ww) {
+        if (ww < W) col[ww * stride] = run;
+        run += x[ww];
+    }
+    return run;
 }
 
 }  // namespace moe
