@@ -15,6 +15,12 @@
 // once to fp32.
 #include "common.cuh"
 
+// Waves below which the launcher gives each token a wider lane group; overridable at build time
+// for launch-shape experiments.
+#ifndef MOE_ROUTE_MIN_WAVES
+#define MOE_ROUTE_MIN_WAVES 1024
+#endif
+
 namespace moe {
 
 // Order-preserving map of a float to uint32 (after -0 is folded into +0).
@@ -114,13 +120,13 @@ __global__ __launch_bounds__(kBlock) void k_route(const float* __restrict__ logi
         }
     }
 
-    // softmax over the group's R selected values, shifted by the largest (slot 0), in fp64,
-    // summed in slot order by every lane of the group
+    // softmax over the group's R selected values, shifted by the largest (slot 0), in fp64: lane
+    // k of the group forms slot k's term, and every lane sums the terms in slot order
     const int base = grp * G;
     const double v0 = (double)__shfl(my_v, base, kWave);
-    double sum = 0.0;
-    for (int j = 0; j < R; ++j) sum += exp((double)__shfl(my_v, base + j, kWave) - v0);
     const double z = exp((double)my_v - v0);
+    double sum = 0.0;
+    for (int j = 0; j < R; ++j) sum += __shfl(z, base + j, kWave);
     if (active && gl < R) {
         topk_idx[tok * R + gl] = my_e;
         topk_w[tok * R + gl] = (float)(z / sum);
@@ -156,9 +162,11 @@ hipError_t launch_route(const Dims& D0, const float* logits, const float* bias, 
     logits += t0 * D.E;
     topk_idx += t0 * D.R;
     topk_w += t0 * D.R;
-    // the smallest group with at most 16 experts per lane and at least R lanes
+    // the smallest group with at most 16 experts per lane and at least R lanes, widened while
+    // the call has fewer than MOE_ROUTE_MIN_WAVES waves (fewer experts per lane, shorter rounds)
     int G = 16;
     while (G < 64 && (D.E > 16 * G || D.R > G)) G *= 2;
+    while (G < 64 && (long)ntok * G < (long)MOE_ROUTE_MIN_WAVES * kWave) G *= 2;
     const int vpl = (D.E + G - 1) / G;
     const long waves = ((long)ntok * G + kWave - 1) / kWave;
     const dim3 grid((waves + kWavesPerBlock - 1) / kWavesPerBlock);
