@@ -330,6 +330,45 @@ def test_tight_capacity():
     parity.compare(g, o, N, T, H, E, R, False)
 
 
+def _sweep_case(seed):
+    """A seeded random configuration: ranks, experts per rank, slots, tokens, hidden size, payload
+    type, bias, per-rank token counts, receive capacity and combine form all drawn together."""
+    rng = np.random.default_rng(1000 + seed)
+    N = int(rng.choice([1, 2, 3, 4, 5, 7, 8, 12, 16, 33]))
+    L = int(rng.integers(1, 7))
+    E = N * L
+    R = int(rng.integers(1, min(E, 9) + 1))
+    T = int(rng.integers(1, 161))
+    kind = rng.choice(["bf16", "bf16", "fp8", "quant"])
+    H = int(rng.choice([512, 1024])) if kind != "bf16" else 8 * int(rng.integers(1, 97))
+    bias = str(rng.choice(["none", "zipf"]))
+    tokens = rng.integers(0, T + 1, N).astype(np.int32) if rng.random() < 0.4 else None
+    tight = bool(rng.random() < 0.25)
+    split = bool(rng.random() < 0.5)
+    return N, T, H, E, R, str(kind), bias, tokens, tight, split
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_shape_sweep(seed):
+    # random configurations, each compared with the oracle stage by stage
+    N, T, H, E, R, kind, bias, tokens, tight, split = _sweep_case(seed)
+    print(f"\ncase sweep {seed}: N{N} T{T} H{H} E{E} R{R} {kind} {bias} tokens "
+          f"{None if tokens is None else tokens.tolist()} tight {tight} split {split}", flush=True)
+    cap = N * T * min(R, E // N) if tight else 0
+    if kind == "quant":
+        inp = _quant_inputs(N, T, H, E, R, bias, seed)
+        _, g = parity.gpu_run(N, T, H, E, R, True, inp, capacity=cap, quant=True, tokens=tokens,
+                              split_combine=split)
+        o = parity.oracle_run(N, T, H, E, R, False, inp, quant=True, tokens=tokens)
+    else:
+        fp8 = kind == "fp8"
+        inp = ms.make_inputs(N, T, H, E, R, fp8, bias, seed)
+        _, g = parity.gpu_run(N, T, H, E, R, fp8, inp, capacity=cap, tokens=tokens,
+                              split_combine=split)
+        o = parity.oracle_run(N, T, H, E, R, fp8, inp, tokens=tokens)
+    parity.compare(g, o, N, T, H, E, R, kind != "bf16")
+
+
 # the ABI's largest N, E and R with small T and H: tables over 1024 ranks, 1024 experts,
 # 64 slots per token (the router's 64-lane groups with 16 experts per lane)
 LIMITS = [
