@@ -233,6 +233,27 @@ def combine(sh: Shape, mode: int, expert_y, expert_rpos, recv_off, send_off, sen
     return dict(cs_buf=cs, cr_buf=cr, out=out)
 
 
+def combine_acc(sh: Shape, mode: int, expert_y, expert_src, expert_rpos, recv_off, send_off,
+                topk_idx, send_pos, topk_w):
+    """Combine with the sum taken on the sending side (one bf16 partial row per token and owner
+    rank).  cs_buf/cr_buf start filled with bf16 3.0 (0x4040), which rows that hold no partial
+    keep: a sum that reads such a row shows."""
+    N, H, T, R = sh.N, sh.H, sh.T, sh.R
+    cs = np.full(sh.lead() + (H,), 0x4040, np.uint16)
+    cr = np.full((N, T * R, H), 0x4040, np.uint16)
+    out = np.zeros((N, T, H), np.uint16)
+    lib().oracle_combine_acc(ctypes.byref(sh), ctypes.c_int(mode),
+                             _p(np.ascontiguousarray(expert_y, np.uint16)),
+                             _p(np.ascontiguousarray(expert_src, np.int32)),
+                             _p(np.ascontiguousarray(expert_rpos, np.int32)),
+                             _p(np.ascontiguousarray(recv_off, np.int32)),
+                             _p(np.ascontiguousarray(send_off, np.int32)),
+                             _p(np.ascontiguousarray(topk_idx, np.int32)),
+                             _p(np.ascontiguousarray(send_pos, np.int32)),
+                             _p(np.ascontiguousarray(topk_w, np.float32)), _p(cs), _p(cr), _p(out))
+    return dict(cs_buf=cs, cr_buf=cr, out=out)
+
+
 def prefill_dispatch(sh: Shape, x: np.ndarray, x_scale, topk_idx: np.ndarray):
     """Replicated tokens: x uint16[T][H] (bf16 bits) or uint8[T][H] (e4m3), x_scale f32[T][H/128];
     topk_idx i32[T][R].  sh.B is the per-rank row stride of the receive-side arrays."""

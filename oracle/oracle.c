@@ -415,6 +415,98 @@ void oracle_combine(const oracle_shape* sh, int mode, const uint16_t* expert_y,
     }
 }
 
+/* Combine with the sum taken on the sending side ([EFA] results for the EP64 prefill latency
+ * figure: another library sums a token's expert contributions on the expert side before sending,
+ * which cuts the bytes moved at some cost in accuracy; the decode kernels of the page sum on the
+ * receiving side only).  Rank d turns the rows it received for one token (s, t) -- consecutive in
+ * its receive order, in slot order -- into one partial row
+ *     p[d][s][t] = bf16( sum over those rows of w[s][t][k] * y ),
+ * stored at the receive position of the token's first row (cs_buf) and sent back to the send
+ * position of the token's first slot owned by d (cr_buf); the other rows are not sent.  Rank s
+ * then adds the partials of each token in the order of their first slots:
+ *     out[s][t] = bf16( sum over owners of p ).
+ * The bf16 rounding of each partial is the transmitted precision (the accuracy cost).
+ * mode 0: both sums in fp64, each rounded once to bf16.
+ * mode 1: the partial as an fp32 fused-multiply-add chain in slot order, the final sum as fp32
+ *         additions in first-slot order, each rounded once to bf16. */
+void oracle_combine_acc(const oracle_shape* sh, int mode, const uint16_t* expert_y,
+                        const int32_t* expert_src, const int32_t* expert_rpos,
+                        const int32_t* recv_off, const int32_t* send_off, const int32_t* topk_idx,
+                        const int32_t* send_pos, const float* topk_w, uint16_t* cs_buf,
+                        uint16_t* cr_buf, uint16_t* out) {
+    const int N = sh->N, T = sh->T, H = sh->H, R = sh->R, L = sh->E / sh->N;
+    const long TR = (long)T * R;
+    /* first[d][r]: receive row r of rank d is its token's first row there */
+    char** first = calloc(N, sizeof(char*));
+    assert(first);
+    /* expert side */
+    for (int d = 0; d < N; ++d) {
+        const long total = recv_off[(long)d * (N + 1) + N];
+        long* qof = malloc(sizeof(long) * (total > 0 ? total : 1));  /* receive row -> expert-major row */
+        first[d] = calloc(total > 0 ? total : 1, 1);
+        assert(qof && first[d]);
+        for (long q = 0; q < total; ++q) qof[expert_rpos[rrow0(sh, d) + q]] = q;
+        long r = 0;
+        while (r < total) {
+            const long tok = expert_src[rrow0(sh, d) + qof[r]] / R;  /* s * T + t */
+            long c = 1;  /* the token's rows at rank d: r .. r + c - 1 */
+            while (r + c < total && expert_src[rrow0(sh, d) + qof[r + c]] / R == tok) ++c;
+            first[d][r] = 1;
+            for (int h = 0; h < H; ++h) {
+                double acc = 0.0;
+                float accf = 0.0f;
+                for (long i = 0; i < c; ++i) {
+                    const long q = qof[r + i];
+                    const long si = expert_src[rrow0(sh, d) + q];  /* s * T * R + t * R + k */
+                    const double y = oracle_bf16_to_double(expert_y[(rrow0(sh, d) + q) * H + h]);
+                    if (mode == 0) acc += (double)topk_w[si] * y;
+                    else accf = fmaf(topk_w[si], (float)y, accf);
+                }
+                cs_buf[(rrow0(sh, d) + r) * H + h] = oracle_bf16_from_double(mode == 0 ? acc : (double)accf);
+            }
+            r += c;
+        }
+        free(qof);
+    }
+    /* network back: the partial rows only; segment (d -> s) row i lands where s's dispatch
+     * segment for d held row i, i.e. at the send position of the token's first slot owned by d */
+    for (int s = 0; s < N; ++s) {
+        const int32_t* soff = send_off + (long)s * (N + 1);
+        for (int d = 0; d < N; ++d) {
+            const long r0 = recv_off[(long)d * (N + 1) + s];
+            for (long i = 0; i < soff[d + 1] - soff[d]; ++i) {
+                if (!first[d][r0 + i]) continue;
+                memcpy(cr_buf + ((long)s * TR + soff[d] + i) * H, cs_buf + (rrow0(sh, d) + r0 + i) * H,
+                       2L * H);
+            }
+        }
+    }
+    for (int d = 0; d < N; ++d) free(first[d]);
+    free(first);
+    /* the source's sum over the token's owners, in the order of their first slots */
+    for (int s = 0; s < N; ++s) {
+        for (int t = 0; t < ntok(sh, s); ++t) {
+            const long base = (long)s * TR + (long)t * R;
+            for (int h = 0; h < H; ++h) {
+                double acc = 0.0;
+                float accf = 0.0f;
+                for (int k = 0; k < R; ++k) {
+                    if (send_pos[base + k] < 0) continue;  /* dropped slot */
+                    const int d = topk_idx[base + k] / L;
+                    int is_first = 1;
+                    for (int kk = 0; kk < k; ++kk)
+                        if (send_pos[base + kk] >= 0 && topk_idx[base + kk] / L == d) is_first = 0;
+                    if (!is_first) continue;
+                    const double p = oracle_bf16_to_double(cr_buf[((long)s * TR + send_pos[base + k]) * H + h]);
+                    if (mode == 0) acc += p;
+                    else accf = accf + (float)p;
+                }
+                out[((long)s * T + t) * H + h] = oracle_bf16_from_double(mode == 0 ? acc : (double)accf);
+            }
+        }
+    }
+}
+
 /* ---------------------------------------------------------------- prefill (replicated inputs) */
 
 /* [QWEN] MoE dispatch-combine, Expert parallel: the prefill kernel's inputs are the same on every

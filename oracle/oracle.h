@@ -83,6 +83,21 @@ void oracle_combine(const oracle_shape* sh, int mode, const uint16_t* expert_y,
                     const int32_t* send_pos, const float* topk_w, uint16_t* cs_buf, uint16_t* cr_buf,
                     uint16_t* out);
 
+/* Combine with the sum taken on the sending side: rank d sends one bf16 partial row per token
+ * it holds rows for (the weighted sum of those rows), and the source adds the partials.
+ * expert_src/expert_rpos as dispatch receive wrote them; topk_idx [N][T][R] (the owner of each
+ * slot).  cs_buf holds a partial at the receive position of each token's first row at rank d,
+ * cr_buf at the send position of each token's first slot per owner rank; no other rows are
+ * written.
+ * mode 0: partial and final sums in fp64, each rounded once to bf16.
+ * mode 1: the partial as an fp32 fused-multiply-add chain in slot order, the final sum as fp32
+ *         additions in first-slot order, each rounded once to bf16. */
+void oracle_combine_acc(const oracle_shape* sh, int mode, const uint16_t* expert_y,
+                        const int32_t* expert_src, const int32_t* expert_rpos,
+                        const int32_t* recv_off, const int32_t* send_off, const int32_t* topk_idx,
+                        const int32_t* send_pos, const float* topk_w, uint16_t* cs_buf,
+                        uint16_t* cr_buf, uint16_t* out);
+
 /* Prefill expert parallelism with replicated inputs ([QWEN] "Hosting Qwen on Blackwell", MoE
  * dispatch-combine, Expert parallel): every rank holds the same T tokens (sh->T), so dispatch
  * only selects, on each rank, the slots routed to its own experts, and combine accumulates each

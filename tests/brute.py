@@ -208,3 +208,52 @@ def combine_exact(N, T, R, E, y_of_entry, w):
             rows.append(row)
         out.append(rows)
     return np.array(out, np.uint16)
+
+
+def combine_acc_exact(N, T, R, L, idx, y_of_entry, w, mode):
+    """Combine with the sum on the sending side, from its definition: the token's slots grouped by
+    owner rank e // L in the order of each owner's first slot; each group's partial is
+    bf16(sum of w * y) (mode 0: exact sum; mode 1: fp32 fused multiply-adds in slot order, each
+    exactly rounded); out = bf16(sum of the partials) (mode 0: exact; mode 1: fp32 additions in
+    group order).  idx int32[N][T*R] (-1 never occurs here); returns (out, partials) with
+    partials[(s, t, owner)] = bf16 bits per hidden position."""
+    out = []
+    partials = {}
+    for s in range(N):
+        rows = []
+        for t in range(T):
+            owners = []
+            for k in range(R):
+                d = int(idx[s, t * R + k]) // L
+                if d not in owners:
+                    owners.append(d)
+            ys = {k: y_of_entry(s, t, k) for k in range(R)}
+            H = len(ys[0])
+            for d in owners:
+                ks = [k for k in range(R) if int(idx[s, t * R + k]) // L == d]
+                prow = []
+                for h in range(H):
+                    if mode == 0:
+                        acc = Fraction(0)
+                        for k in ks:
+                            acc += Fraction(float(w[s * T + t, k])) * bf16_bits_to_fraction(ys[k][h])
+                        prow.append(bf16_round_exact(acc))
+                    else:
+                        acc = np.float32(0)
+                        for k in ks:
+                            acc = fma_f32_exact(w[s * T + t, k], float(bf16_bits_to_fraction(ys[k][h])), acc)
+                        prow.append(bf16_round_exact(Fraction(float(acc))))
+                partials[(s, t, d)] = prow
+            row = []
+            for h in range(H):
+                if mode == 0:
+                    acc = sum((bf16_bits_to_fraction(partials[(s, t, d)][h]) for d in owners), Fraction(0))
+                    row.append(bf16_round_exact(acc))
+                else:
+                    acc = np.float32(0)
+                    for d in owners:
+                        acc = f32_round_exact(Fraction(float(acc)) + bf16_bits_to_fraction(partials[(s, t, d)][h]))
+                    row.append(bf16_round_exact(Fraction(float(acc))))
+            rows.append(row)
+        out.append(rows)
+    return np.array(out, np.uint16), partials

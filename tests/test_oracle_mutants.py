@@ -39,6 +39,12 @@ MUTANTS = {
     "combine_weight_of_slot0": ("acc += (double)topk_w[base + k] * y;", "acc += (double)topk_w[base] * y;"),
     "combine_drops_last_slot": ("for (int k = 0; k < R; ++k) {\n                    long row",
                                 "for (int k = 0; k < R - 1; ++k) {\n                    long row"),
+    "acc_sums_every_slot": ("                    if (!is_first) continue;\n", ""),
+    "acc_group_weight_of_first_row": ("if (mode == 0) acc += (double)topk_w[si] * y;\n                    else accf = fmaf(topk_w[si], (float)y, accf);",
+                                      "if (mode == 0) acc += (double)topk_w[si - i] * y;\n                    else accf = fmaf(topk_w[si - i], (float)y, accf);"),
+    "acc_rows_never_grouped": ("while (r + c < total && expert_src[rrow0(sh, d) + qof[r + c]] / R == tok) ++c;",
+                               "while (0) ++c;"),
+    "acc_net_sends_other_rows": ("if (!first[d][r0 + i]) continue;", "if (first[d][r0 + i] && i > 0) continue;"),
     "bf16_truncates": ("double q = nearbyint(ldexp(a, -ulp_exp));", "double q = floor(ldexp(a, -ulp_exp));"),
     "bf16_one_bit_short": ("int ulp_exp = ex - 8;", "int ulp_exp = ex - 7;"),
     "e4m3_wrong_bias": ("ldexp((double)(8 + m), e - 10)", "ldexp((double)(8 + m), e - 9)"),

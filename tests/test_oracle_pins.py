@@ -657,6 +657,98 @@ def test_random_expert_outputs_brute(case):
                 assert out1["out"][s, t, h] == brute.bf16_round_exact(Fraction(float(acc)))
 
 
+# ------------------------------------------------------------------ combine, sum on the sending side
+
+
+def _combine_acc(res, y, mode):
+    return oracle.combine_acc(res["sh"], mode, y, res["expert_src"], res["expert_rpos"],
+                              res["recv_off"], res["send_off"], res["idx"], res["send_pos"], res["w"])
+
+
+def _y_lookup(res, N, T, E, R, y):
+    bf = brute.dispatch(N, T, E, R, res["idx"])
+    where = {}
+    for d in range(N):
+        for q, (s, t, k, e) in enumerate(bf["expert_order"][d]):
+            where[(s, t, k)] = (d, q)
+
+    def y_of(s, t, k):
+        d, q = where[(s, t, k)]
+        return [int(v) for v in y[d, q]]
+    return bf, y_of
+
+
+# shapes where a token's slots share owner ranks (L = 4, 3, 2, 2, 4)
+ACC = [SMALL[1], SMALL[2], SMALL[3], SMALL[6], SMALL[8]]
+
+
+@pytest.mark.parametrize("case", ACC)
+def test_combine_acc_brute(case):
+    # arbitrary expert outputs: every token's partial per owner rank and the final sum equal the
+    # definition worked out with exact rationals; the partial sits at the receive position of the
+    # token's first row at that rank and at the send position of its first slot owned there
+    N, T, H, E, R, fp8 = case
+    L = E // N
+    res = run_small(*case, seed=17)
+    y = ms.random_y(N, res["sh"].B, H, seed=5)
+    bf, y_of = _y_lookup(res, N, T, E, R, y)
+    for mode in (0, 1):
+        o = _combine_acc(res, y, mode)
+        want, parts = brute.combine_acc_exact(N, T, R, L, res["idx"], y_of, res["w"], mode)
+        assert np.array_equal(o["out"], want), mode
+        for (s, t, d), prow in parts.items():
+            k0 = min(k for k in range(R) if int(res["idx"][s, t * R + k]) // L == d)
+            assert list(o["cr_buf"][s, res["send_pos"][s, t * R + k0]]) == prow, (mode, s, t, d)
+            r0 = bf["recv_order"][d].index((s, t, k0, int(res["idx"][s, t * R + k0])))
+            assert list(o["cs_buf"][d, r0]) == prow, (mode, s, t, d)
+
+
+@pytest.mark.parametrize("case", [SMALL[4], (3, 6, 16, 9, 1, False)])
+def test_combine_acc_one_slot_equals_combine(case):
+    # R = 1: one row per token, the partial is bf16(w * y) and the final sum adds nothing to it,
+    # so both modes equal the receive-side combine bit for bit
+    N, T, H, E, R, fp8 = case
+    res = run_small(*case, seed=19)
+    y = ms.random_y(N, res["sh"].B, H, seed=6)
+    for mode in (0, 1):
+        _, ref = _combine(res, None, mode, y=y)
+        assert np.array_equal(_combine_acc(res, y, mode)["out"], ref["out"]), mode
+
+
+@pytest.mark.parametrize("case", [SMALL[0], (1, 9, 16, 12, 6, False)])
+def test_combine_acc_one_rank_equals_combine(case):
+    # N = 1: every slot has the same owner, one partial per token holds the whole weighted sum,
+    # rounded once; the final sum of one bf16 value is exact, so the result equals the
+    # receive-side combine in both modes
+    N, T, H, E, R, fp8 = case
+    res = run_small(*case, seed=21)
+    y = ms.random_y(N, res["sh"].B, H, seed=7)
+    for mode in (0, 1):
+        _, ref = _combine(res, None, mode, y=y)
+        assert np.array_equal(_combine_acc(res, y, mode)["out"], ref["out"]), mode
+
+
+@pytest.mark.parametrize("case", [SMALL[1], SMALL[3], SMALL[8]])
+def test_combine_acc_identity_error_bound(case):
+    # identity experts: every contribution of a token has the sign of its value, so each bf16
+    # rounding (one per partial, one at the end) adds at most 2^-8 relative error:
+    # |out - y * sum_k w_k| <= (2^-8 + 2^-8 + 2^-16) * |y * sum_k w_k| (plus fp32 terms in mode 1)
+    N, T, H, E, R, fp8 = case
+    res = run_small(*case, seed=23)
+    y = oracle.expert(res["sh"], 0, res["expert_x"], res["expert_scale"], res["expert_off"])
+    for mode in (0, 1):
+        out = _combine_acc(res, y, mode)["out"]
+        for s in range(N):
+            for t in range(T):
+                yv = _dequant_bf16(res["inp"], s, t, fp8)
+                sw = sum(Fraction(float(res["w"][s * T + t, k])) for k in range(R))
+                for h in range(H):
+                    exact = brute.bf16_bits_to_fraction(int(yv[h])) * sw
+                    got = brute.bf16_bits_to_fraction(int(out[s, t, h]))
+                    assert abs(got - exact) <= abs(exact) * (Fraction(2, 2**8) + Fraction(1, 2**15)), \
+                        (mode, s, t, h)
+
+
 # ------------------------------------------------------------------ the pages' arithmetic
 
 
