@@ -64,6 +64,9 @@ _SIGS = {
     "moe_combine": [ctypes.POINTER(moe_shape)] + [_vp] * 10,
     "moe_combine_send": [ctypes.POINTER(moe_shape)] + [_vp] * 7,
     "moe_combine_recv": [ctypes.POINTER(moe_shape)] + [_vp] * 5,
+    "moe_combine_acc": [ctypes.POINTER(moe_shape)] + [_vp] * 13,
+    "moe_combine_acc_send": [ctypes.POINTER(moe_shape)] + [_vp] * 10,
+    "moe_combine_acc_recv": [ctypes.POINTER(moe_shape)] + [_vp] * 5,
     "moe_expert_stub": [ctypes.POINTER(moe_shape), ctypes.c_int32] + [_vp] * 5,
     "moe_prefill_dispatch": [ctypes.POINTER(moe_shape)] + [_vp] * 11,
     "moe_prefill_combine_local": [ctypes.POINTER(moe_shape)] + [_vp] * 6,
@@ -184,6 +187,28 @@ def moe_combine_send(shape, expert_y, expert_rpos, recv_off, send_off, cs_buf, c
 def moe_combine_recv(shape, cr_buf, send_pos, topk_w, out, stream=None):
     _check("moe_combine_recv", _lib.moe_combine_recv(
         ctypes.byref(shape), _ptr(cr_buf), _ptr(send_pos), _ptr(topk_w), _ptr(out),
+        _stream(stream)))
+
+
+def moe_combine_acc(shape, expert_y, recv_meta, counts, recv_off, expert_off, send_off, topk_w,
+                    topk_idx, send_pos, cs_buf, cr_buf, out, stream=None):
+    _check("moe_combine_acc", _lib.moe_combine_acc(
+        ctypes.byref(shape), _ptr(expert_y), _ptr(recv_meta), _ptr(counts), _ptr(recv_off),
+        _ptr(expert_off), _ptr(send_off), _ptr(topk_w), _ptr(topk_idx), _ptr(send_pos),
+        _ptr(cs_buf), _ptr(cr_buf), _ptr(out), _stream(stream)))
+
+
+def moe_combine_acc_send(shape, expert_y, recv_meta, counts, recv_off, expert_off, send_off, topk_w,
+                         cs_buf, cr_buf, stream=None):
+    _check("moe_combine_acc_send", _lib.moe_combine_acc_send(
+        ctypes.byref(shape), _ptr(expert_y), _ptr(recv_meta), _ptr(counts), _ptr(recv_off),
+        _ptr(expert_off), _ptr(send_off), _ptr(topk_w), _ptr(cs_buf), _ptr(cr_buf),
+        _stream(stream)))
+
+
+def moe_combine_acc_recv(shape, cr_buf, topk_idx, send_pos, out, stream=None):
+    _check("moe_combine_acc_recv", _lib.moe_combine_acc_recv(
+        ctypes.byref(shape), _ptr(cr_buf), _ptr(topk_idx), _ptr(send_pos), _ptr(out),
         _stream(stream)))
 
 
@@ -344,3 +369,10 @@ def run_combine(b: Buffers, expert_y=None, stream=None):
     y = b.expert_y if expert_y is None else expert_y
     moe_combine(b.shape, y, b.expert_rpos, b.recv_off, b.send_off, b.send_pos, b.topk_w,
                 b.cs_buf, b.cr_buf, b.out, stream)
+
+
+def run_combine_acc(b: Buffers, expert_y=None, stream=None):
+    """The combine with the sum taken on the sending side, on the same buffers."""
+    y = b.expert_y if expert_y is None else expert_y
+    moe_combine_acc(b.shape, y, b.recv_meta, b.counts, b.recv_off, b.expert_off, b.send_off,
+                    b.topk_w, b.topk_idx, b.send_pos, b.cs_buf, b.cr_buf, b.out, stream)

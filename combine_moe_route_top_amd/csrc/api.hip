@@ -23,6 +23,11 @@ hipError_t launch_combine_send(const Dims&, const uint16_t*, const int32_t*, con
                                const int32_t*, uint16_t*, uint16_t*, hipStream_t);
 hipError_t launch_combine_recv(const Dims&, const uint16_t*, const int32_t*, const float*, uint16_t*,
                                hipStream_t);
+hipError_t launch_combine_acc_send(const Dims&, const uint16_t*, const int32_t*, const int32_t*, const int32_t*,
+                                   const int32_t*, const int32_t*, const float*, uint16_t*, uint16_t*,
+                                   hipStream_t);
+hipError_t launch_combine_acc_recv(const Dims&, const uint16_t*, const int32_t*, const int32_t*, uint16_t*,
+                                   hipStream_t);
 size_t prefill_workspace_bytes(const Dims&);
 hipError_t launch_prefill_dispatch(const Dims&, const void*, const float*, const int32_t*, int32_t*, void*,
                                    float*, int32_t*, int32_t*, int32_t*, void*, hipStream_t);
@@ -262,6 +267,58 @@ int moe_combine(const moe_shape* shape, const uint16_t* expert_y, const int32_t*
                                              cr_buf, (hipStream_t)stream));
     if (rc) return rc;
     return hip_status(moe::launch_combine_recv(D, cr_buf, send_pos, topk_w, out, (hipStream_t)stream));
+}
+
+static bool acc_send_aligned(const uint16_t* expert_y, const int32_t* recv_meta, const int32_t* counts,
+                             const int32_t* recv_off, const int32_t* expert_off, const int32_t* send_off,
+                             const float* topk_w, const uint16_t* cs_buf, const uint16_t* cr_buf) {
+    return aligned(expert_y, 16) && aligned(recv_meta, 8) && aligned(counts, 4) && aligned(recv_off, 4) &&
+           aligned(expert_off, 4) && aligned(send_off, 4) && aligned(topk_w, 4) && aligned(cs_buf, 16) &&
+           aligned(cr_buf, 16);
+}
+
+int moe_combine_acc_send(const moe_shape* shape, const uint16_t* expert_y, const int32_t* recv_meta,
+                         const int32_t* counts, const int32_t* recv_off, const int32_t* expert_off,
+                         const int32_t* send_off, const float* topk_w, uint16_t* cs_buf,
+                         uint16_t* cr_buf, void* stream) {
+    Dims D;
+    int rc = make_dims(shape, &D);
+    if (rc) return rc;
+    if (D.prefill) return MOE_EINVAL;  // the decode layout only
+    if (!acc_send_aligned(expert_y, recv_meta, counts, recv_off, expert_off, send_off, topk_w, cs_buf, cr_buf))
+        return MOE_EINVAL;
+    return hip_status(moe::launch_combine_acc_send(D, expert_y, recv_meta, counts, recv_off, expert_off,
+                                                   send_off, topk_w, cs_buf, cr_buf, (hipStream_t)stream));
+}
+
+int moe_combine_acc_recv(const moe_shape* shape, const uint16_t* cr_buf, const int32_t* topk_idx,
+                         const int32_t* send_pos, uint16_t* out, void* stream) {
+    Dims D;
+    int rc = make_dims(shape, &D);
+    if (rc) return rc;
+    if (D.prefill) return MOE_EINVAL;  // the decode layout only
+    if (!aligned(cr_buf, 16) || !aligned(topk_idx, 4) || !aligned(send_pos, 4) || !aligned(out, 16))
+        return MOE_EINVAL;
+    return hip_status(moe::launch_combine_acc_recv(D, cr_buf, send_pos, topk_idx, out, (hipStream_t)stream));
+}
+
+int moe_combine_acc(const moe_shape* shape, const uint16_t* expert_y, const int32_t* recv_meta,
+                    const int32_t* counts, const int32_t* recv_off, const int32_t* expert_off,
+                    const int32_t* send_off, const float* topk_w, const int32_t* topk_idx,
+                    const int32_t* send_pos, uint16_t* cs_buf, uint16_t* cr_buf, uint16_t* out,
+                    void* stream) {
+    Dims D;
+    int rc = make_dims(shape, &D);
+    if (rc) return rc;
+    if (D.prefill) return MOE_EINVAL;  // the decode layout only
+    // validate both halves before launching either
+    if (!acc_send_aligned(expert_y, recv_meta, counts, recv_off, expert_off, send_off, topk_w, cs_buf, cr_buf) ||
+        !aligned(topk_idx, 4) || !aligned(send_pos, 4) || !aligned(out, 16))
+        return MOE_EINVAL;
+    rc = hip_status(moe::launch_combine_acc_send(D, expert_y, recv_meta, counts, recv_off, expert_off, send_off,
+                                                 topk_w, cs_buf, cr_buf, (hipStream_t)stream));
+    if (rc) return rc;
+    return hip_status(moe::launch_combine_acc_recv(D, cr_buf, send_pos, topk_idx, out, (hipStream_t)stream));
 }
 
 int moe_expert_stub(const moe_shape* shape, int32_t mode, const void* expert_x,

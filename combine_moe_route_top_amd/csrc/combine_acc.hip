@@ -1,0 +1,294 @@
+// combine_acc.hip -- combine with the sum taken on the sending side: the expert rank forms one
+// bf16 partial row per token it holds rows for (the router-weighted sum of those rows), sends
+// only the partials back, and the source adds them.  Fewer rows cross the network; each partial
+// is rounded to bf16 once more than in the receive-side combine (the accuracy cost).
+//
+// Pages: [EFA] = "Enabling trillion-parameter models on AWS EFA" (results under the EP64 prefill
+// latency figure: another library accumulates on the sending side to cut the data moved, which
+// can cost accuracy; the page's own decode kernels accumulate on the receiving side only).
+//
+// Layout (no new tables): rank d's rows of one token (s, t) are consecutive in its receive order
+// (segment s, then (token, slot)).  The partial takes the receive position of the token's first
+// row at d in the combine send buffer and, through the network, the send position of the token's
+// first slot owned by d in the combine receive buffer; the other rows are not written.  The
+// weights of a row come from the source's topk_w (in a deployment they travel with the
+// dispatched row: 4 bytes).
+#include <algorithm>
+
+#include "common.cuh"
+
+namespace moe {
+
+// The token (t) of a receive row from its metadata (e * T*R + t*R + k).
+__device__ __forceinline__ int meta_token(int2 m, int TR, int R) { return (m.x % TR) / R; }
+
+// One wave's part of the partial row of receive row G (a global index over the call's ranks), if
+// G is its token's first row at its rank d.  Lane j < c holds the token's j-th row there
+// (consecutive rows, c <= min(R, L)), its expert-major position
+//   expert_off[d][e - d*L] + (rows of expert e from sources s' < s) + rank_e (metadata)
+// and its weight; the wave's chunks of the row are summed over j in slot order with fp32 fused
+// multiply-adds, up to 8 rows' loads in flight, and rounded once to bf16.
+__device__ __forceinline__ void acc_partial_row(const Dims& D, int WW, int part, long G, const int* gb,
+                                                const uint16_t* __restrict__ expert_y,
+                                                const int32_t* __restrict__ recv_meta,
+                                                const int32_t* __restrict__ counts,
+                                                const int32_t* __restrict__ recv_off,
+                                                const int32_t* __restrict__ expert_off,
+                                                const float* __restrict__ topk_w,
+                                                uint16_t* __restrict__ cs_buf) {
+    const int N = D.N, L = D.L, E = D.E, TR = D.TR, R = D.R;
+    const int lane = lane_id();
+    const int dl = wave_count_le(gb + 1, D.rc, G);
+    const int d = D.rb + dl;
+    const long r = G - gb[dl];
+    const int32_t* ro = recv_off + (long)d * (N + 1);
+    const int s = wave_count_le(ro, N, r) - 1;
+    if (s < 0 || r >= D.B) {
+        set_status(D.status, MOE_EINVAL);
+        return;
+    }
+    const long seg0 = ro[s], seg1 = ro[s + 1];
+    const int2* meta = reinterpret_cast<const int2*>(recv_meta) + (size_t)d * D.B;
+    const int t = meta_token(meta[r], TR, R);
+    if (r > seg0 && meta_token(meta[r - 1], TR, R) == t) return;  // not the token's first row here
+
+    int2 mj = {0, 0};
+    bool mine = false;
+    if (lane < R && r + lane < seg1) {
+        mj = meta[r + lane];
+        mine = meta_token(mj, TR, R) == t;
+    }
+    const int c = __popcll(ballot(mine));  // lanes 0 .. c-1: the token's rows are consecutive
+    const int e = mine ? mj.x / TR : 0;
+    // rows of expert e from earlier sources: one wave sum per row of the token
+    int q = -1;
+    for (int j = 0; j < c; ++j) {
+        const int ej = readlane(e, j);
+        int v = 0;
+        for (int sp = lane; sp < s; sp += kWave) v += counts[(long)sp * E + ej];
+        const int before = wave_sum(v);
+        if (lane == j) {
+            const int jl = ej - d * L;
+            const long qq = (jl >= 0 && jl < L) ? (long)expert_off[(long)d * (L + 1) + jl] + before + mj.y : -1;
+            q = (qq >= 0 && qq < D.B) ? (int)qq : -1;
+        }
+    }
+    if (ballot(mine && q < 0)) {
+        set_status(D.status, MOE_EINVAL);
+        return;
+    }
+    const float wj = mine ? topk_w[(size_t)s * TR + (mj.x - e * TR)] : 0.0f;
+
+    const u32x4* yrank = reinterpret_cast<const u32x4*>(expert_y + (size_t)d * D.B * D.H);
+    u32x4* orow = reinterpret_cast<u32x4*>(cs_buf + ((size_t)d * D.B + r) * D.H);
+    const int n16 = D.Y16;
+    for (int c0 = part * kWave + lane; c0 < n16; c0 += kWave * WW) {
+        float acc[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc[u] = 0.0f;
+        for (int j0 = 0; j0 < c; j0 += 8) {
+            u32x4 v[8];
+            float wk[8];
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                const int j = j0 + jj;
+                const int qj = j < c ? readlane(q, j) : -1;
+                wk[jj] = j < c ? readlane_f(wj, j) : 0.0f;
+                if (qj >= 0) v[jj] = ld_nt(yrank + (size_t)qj * n16 + c0);
+            }
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                if (j0 + jj >= c) continue;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const float y = bf16_to_f32((v[jj][u >> 1] >> (16 * (u & 1))) & 0xFFFF);
+                    acc[u] = __builtin_fmaf(wk[jj], y, acc[u]);
+                }
+            }
+        }
+        u32x4 o;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) o[u] = f32_to_bf16(acc[2 * u]) | (f32_to_bf16(acc[2 * u + 1]) << 16);
+        st_nt(orow + c0, o);
+    }
+}
+
+// Partial rows: WW waves per receive row of the call's ranks; waves step over the (row, part)
+// tasks (the grid is capped for calls on a subset of ranks, whose receive rows are few).
+__global__ __launch_bounds__(kBlock) void k_acc_partial(Dims D, int WW, const uint16_t* __restrict__ expert_y,
+                                                        const int32_t* __restrict__ recv_meta,
+                                                        const int32_t* __restrict__ counts,
+                                                        const int32_t* __restrict__ recv_off,
+                                                        const int32_t* __restrict__ expert_off,
+                                                        const float* __restrict__ topk_w,
+                                                        uint16_t* __restrict__ cs_buf) {
+    extern __shared__ int gb[];
+    rank_bases(recv_off + (long)D.rb * (D.N + 1), D.N + 1, D.N, D.rc, gb);
+    __syncthreads();
+    const long tasks = (long)gb[D.rc] * WW;
+    for (long gw = (long)blockIdx.x * kWavesPerBlock + wave_id(); gw < tasks;
+         gw += (long)gridDim.x * kWavesPerBlock) {
+        const long G = gw / WW;
+        acc_partial_row(D, WW, (int)(gw - G * WW), G, gb, expert_y, recv_meta, counts, recv_off, expert_off,
+                        topk_w, cs_buf);
+    }
+}
+
+// Network back for the partials: as the receive-side combine's network step (row r of segment
+// (s -> d) to send_off[s][d] + (r - recv_off[d][s]) in rank s's combine receive buffer), but a
+// row moves only if it is its token's first row at d.  STRIDE: blocks stride over a capped grid.
+template <int RPB, int U, bool STRIDE>
+__global__ __launch_bounds__(kBlock) void k_acc_net(Dims D, const uint16_t* __restrict__ cs_buf,
+                                                    const int32_t* __restrict__ recv_meta,
+                                                    const int32_t* __restrict__ recv_off,
+                                                    const int32_t* __restrict__ send_off,
+                                                    uint16_t* __restrict__ cr_buf) {
+    extern __shared__ int gb[];
+    __shared__ RowDesc rows[RPB];
+    const int N = D.N;
+    rank_bases(recv_off + (long)D.rb * (N + 1), N + 1, N, D.rc, gb);
+    __syncthreads();
+    const long total = gb[D.rc];
+    auto pass = [&](long base) {
+        const long G = base + wave_id();
+        RowDesc rd = {0, 0, 0, 0};
+        if (wave_id() < RPB && G < total) {
+            const int dl = wave_count_le(gb + 1, D.rc, G);
+            const int d = D.rb + dl;
+            const long r = G - gb[dl];
+            const int32_t* ro = recv_off + (long)d * (N + 1);
+            const int s = wave_count_le(ro, N, r) - 1;
+            const long i = s >= 0 ? send_off[(long)s * (N + 1) + d] + (r - ro[s]) : -1;
+            if (i >= 0 && i < D.TR) {
+                const int2* meta = reinterpret_cast<const int2*>(recv_meta) + (size_t)d * D.B;
+                const bool first = r == ro[s] || meta_token(meta[r - 1], D.TR, D.R) != meta_token(meta[r], D.TR, D.R);
+                if (first) {
+                    rd.src_a = rd.src_b = (uint64_t)(cs_buf + ((size_t)d * D.B + r) * D.H);
+                    rd.dst_a = rd.dst_b = (uint64_t)(cr_buf + ((size_t)s * D.TR + i) * D.H);
+                }
+            } else {
+                set_status(D.status, MOE_EINVAL);
+            }
+        }
+        if (wave_id() < RPB && lane_id() == 0) rows[wave_id()] = rd;
+        __syncthreads();
+        block_stream_rows<U>(rows, RPB, D.Y16, D.Y16, D.Y16);
+    };
+    if constexpr (STRIDE) {
+        for (long base = (long)blockIdx.x * RPB; base < total; base += (long)gridDim.x * RPB) {
+            pass(base);
+            if (base + (long)gridDim.x * RPB < total) __syncthreads();  // rows[] is rewritten
+        }
+    } else {
+        pass((long)blockIdx.x * RPB);
+    }
+}
+
+// The source's sum: out[s][t] = bf16(fp32 sum of the token's partials in the order of their first
+// slots).  Slot k holds a partial if it is valid and no earlier valid slot of the token has the
+// same owner rank (one ballot per owner bit finds the lower lanes with the same owner).  WW waves
+// per token as in the receive-side weighted sum.
+__global__ __launch_bounds__(kBlock) void k_acc_sum(Dims D, int WW, const uint16_t* __restrict__ cr_buf,
+                                                    const int32_t* __restrict__ send_pos,
+                                                    const int32_t* __restrict__ topk_idx,
+                                                    uint16_t* __restrict__ out) {
+    const long gw = (long)blockIdx.x * kWavesPerBlock + wave_id();
+    const long tok = gw / WW;  // within the call's ranks
+    const int part = (int)(gw - tok * WW);
+    if (tok >= (long)D.rc * D.T) return;
+    const int lane = lane_id();
+    const int R = D.R;
+    const long s = tok / D.T;
+    if (tok - s * D.T >= rank_tokens(D, D.rb + s)) return;  // absent token: its row is not written
+    const int pos = lane < R ? send_pos[tok * R + lane] : -1;
+    const bool valid = pos >= 0 && pos < D.TR;
+    const int owner = valid ? topk_idx[tok * R + lane] / D.L : 0;
+    uint64_t same = ballot(valid);
+    const int nb = D.N > 1 ? 32 - __clz(D.N - 1) : 0;
+    for (int b = 0; b < nb; ++b) {
+        const bool bit = (owner >> b) & 1;
+        const uint64_t ones = ballot(bit);
+        same &= bit ? ones : ~ones;
+    }
+    const int my_pos = valid && (same & lanemask_lt()) == 0 ? pos : -1;
+    const u32x4* rank_rows = reinterpret_cast<const u32x4*>(cr_buf + (size_t)s * D.TR * D.H);
+    u32x4* orow = reinterpret_cast<u32x4*>(out + (size_t)tok * D.H);
+    const int n16 = D.Y16;
+    for (int c0 = part * kWave + lane; c0 < n16; c0 += kWave * WW) {
+        float acc[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc[u] = 0.0f;
+        for (int k0 = 0; k0 < R; k0 += 8) {
+            u32x4 v[8];
+            bool ok[8];
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                const int k = k0 + kk;
+                const int p = k < R ? readlane(my_pos, k) : -1;
+                ok[kk] = p >= 0;
+                if (ok[kk]) v[kk] = ld_nt(rank_rows + (size_t)p * n16 + c0);
+            }
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                if (!ok[kk]) continue;
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    acc[u] += bf16_to_f32((v[kk][u >> 1] >> (16 * (u & 1))) & 0xFFFF);
+            }
+        }
+        u32x4 o;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) o[u] = f32_to_bf16(acc[2 * u]) | (f32_to_bf16(acc[2 * u + 1]) << 16);
+        st_nt(orow + c0, o);
+    }
+}
+
+// ------------------------------------------------------------------ launchers
+
+// Waves per row for the two sums: the fewest (at most 16) that cover a row with one 8-value chunk
+// per lane.
+static int acc_waves(const Dims& D) {
+    return (int)std::min<long>(16, std::max<long>(1, (D.Y16 + kWave - 1) / kWave));
+}
+
+hipError_t launch_combine_acc_send(const Dims& D, const uint16_t* expert_y, const int32_t* recv_meta,
+                                   const int32_t* counts, const int32_t* recv_off,
+                                   const int32_t* expert_off, const int32_t* send_off,
+                                   const float* topk_w, uint16_t* cs_buf, uint16_t* cr_buf,
+                                   hipStream_t st) {
+    const long rows = recv_rows_bound(D);  // rows the call's ranks received
+    const int WW = acc_waves(D);
+    hipLaunchKernelGGL(k_acc_partial, dim3((unsigned)row_blocks(D, rows * WW, kWavesPerBlock)), dim3(kBlock),
+                       (D.rc + 1) * 4, st, D, WW, expert_y, recv_meta, counts, recv_off, expert_off, topk_w,
+                       cs_buf);
+    const StreamShape sn = stream_shape(D.Y16, MOE_CNET_MIN_CHUNKS);
+#define MOE_LAUNCH_S(R_, U_, S_)                                                                     \
+    hipLaunchKernelGGL((k_acc_net<R_, U_, S_>), dim3(row_blocks(D, rows, R_)), dim3(kBlock), (D.rc + 1) * 4, \
+                       st, D, (const uint16_t*)cs_buf, recv_meta, recv_off, send_off, cr_buf);
+#define MOE_LAUNCH(R_, U_)                                                                          \
+    if (sn.rpb == R_ && sn.u == U_) {                                                               \
+        if (row_blocks(D, rows, R_) * R_ < rows) MOE_LAUNCH_S(R_, U_, true)                         \
+        else MOE_LAUNCH_S(R_, U_, false)                                                            \
+    }
+    MOE_STREAM_SHAPES(MOE_LAUNCH)
+#undef MOE_LAUNCH
+#undef MOE_LAUNCH_S
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_acc_recv(const Dims& D, const uint16_t* cr_buf, const int32_t* send_pos,
+                                   const int32_t* topk_idx, uint16_t* out, hipStream_t st) {
+    // the tokens of ranks [rb, rb + rc)
+    const long rb = D.rb;
+    cr_buf += rb * D.TR * D.H;
+    send_pos += rb * D.TR;
+    topk_idx += rb * D.TR;
+    out += rb * D.T * D.H;
+    const int WW = acc_waves(D);
+    const long waves = (long)D.rc * D.T * WW;
+    hipLaunchKernelGGL(k_acc_sum, dim3((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock)), dim3(kBlock),
+                       0, st, D, WW, cr_buf, send_pos, topk_idx, out);
+    return hipGetLastError();
+}
+
+}  // namespace moe

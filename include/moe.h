@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 typedef enum {
     MOE_OK = 0,
@@ -207,6 +207,44 @@ int moe_combine_send(const moe_shape* shape, const uint16_t* expert_y, const int
  *   cr_buf, send_pos, topk_w, out   as for moe_combine */
 int moe_combine_recv(const moe_shape* shape, const uint16_t* cr_buf, const int32_t* send_pos,
                      const float* topk_w, uint16_t* out, void* stream);
+
+/* Combine with the sum taken on the sending side ([EFA] results under the EP64 prefill latency
+ * figure: summing a token's expert contributions on the expert side before sending cuts the data
+ * moved, at some cost in accuracy; moe_combine sums on the receiving side only).  Decode layout.
+ * Rank d forms, for every token (s, t) it received rows for, one partial row
+ *     p = bf16(sum over those rows, in slot order, of w[s][t][k] * y)   (fp32 fused multiply-adds)
+ * and only the partials are sent back; rank s then sums the partials of each token:
+ *     out[s][t] = bf16(sum over the token's owner ranks, in the order of their first slots, of p)
+ * (fp32 additions).  Each partial is rounded to bf16 once more than in moe_combine: the results
+ * differ from moe_combine by up to about one bf16 ulp per owner rank of a token.
+ *   expert_y, recv_meta, counts, recv_off, expert_off   from dispatch and the grouped GEMM
+ *   send_off, topk_w     from dispatch (send side) and the router (the weight of a received row is
+ *                        read from its source's topk_w: in a deployment it travels with the row)
+ *   topk_idx, send_pos   from the router and dispatch (send side)
+ *   cs_buf  bf16[N][B][H] (out)   the partial of token (s, t) at the receive position of its first
+ *                                  row at rank d; other rows not written
+ *   cr_buf  bf16[N][T*R][H] (out) the partial from rank d at the send position of the token's
+ *                                  first slot owned by d; other rows not written
+ *   out     bf16[N][T][H] (out)
+ * Errors: as moe_combine; rows whose metadata or tables are inconsistent set MOE_EINVAL in the
+ * status word and are skipped. */
+int moe_combine_acc(const moe_shape* shape, const uint16_t* expert_y, const int32_t* recv_meta,
+                    const int32_t* counts, const int32_t* recv_off, const int32_t* expert_off,
+                    const int32_t* send_off, const float* topk_w, const int32_t* topk_idx,
+                    const int32_t* send_pos, uint16_t* cs_buf, uint16_t* cr_buf, uint16_t* out,
+                    void* stream);  /* = moe_combine_acc_send then moe_combine_acc_recv */
+
+/* Send half of moe_combine_acc: the partial rows and their network step back.
+ *   arguments as for moe_combine_acc */
+int moe_combine_acc_send(const moe_shape* shape, const uint16_t* expert_y, const int32_t* recv_meta,
+                         const int32_t* counts, const int32_t* recv_off, const int32_t* expert_off,
+                         const int32_t* send_off, const float* topk_w, uint16_t* cs_buf,
+                         uint16_t* cr_buf, void* stream);
+
+/* Receive half of moe_combine_acc: the source's sum of the partials.
+ *   arguments as for moe_combine_acc */
+int moe_combine_acc_recv(const moe_shape* shape, const uint16_t* cr_buf, const int32_t* topk_idx,
+                         const int32_t* send_pos, uint16_t* out, void* stream);
 
 /* Stand-in for the grouped GEMM between dispatch and combine (not part of dispatch/combine;
  * [EFA] overview: the grouped GEMM multiplies tokens by expert weights in between).

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strerror():
-    assert moe.moe_abi_version() == 4
+    assert moe.moe_abi_version() == 5
     for code in (0, -1, -2, -3, -5, 42):
         assert isinstance(moe.moe_strerror(code), str)
 
