@@ -772,6 +772,91 @@ def rank_leg(name, steps=20, warmup=3) -> dict:
     return out
 
 
+def acc_combine_leg(name, steps=20, warmup=3) -> dict:
+    """The combine with the sum taken on the sending side ([EFA] results: fewer bytes back, some
+    accuracy lost) beside the receive-side combine, on one dispatched layer of the workload:
+    per-call times (HIP events, means over the steps), rows sent back (one partial per token and
+    owner rank vs one row per routed slot), algorithmic bytes, and the accuracy cost as the bf16
+    ulp distance between the two outputs (identity experts)."""
+    import numpy as np
+    import torch
+
+    import combine_moe_route_top_amd as moe
+    import moe_synth as ms
+
+    c = ms.CONFIGS[name]
+    inp = ms.config_inputs(c)
+    b = moe.alloc_buffers(c.N, c.T, c.H, c.E, c.R, c.fp8)
+    b.logits.copy_(torch.from_numpy(inp["logits"]))
+    use_bias = inp["bias"] is not None
+    if use_bias:
+        b.bias.copy_(torch.from_numpy(inp["bias"]))
+    x = inp["x"]
+    b.x.copy_(torch.from_numpy(x.view(np.int16) if x.dtype == np.uint16 else x))
+    if c.fp8:
+        b.x_scale.copy_(torch.from_numpy(inp["x_scale"]))
+    st = torch.cuda.current_stream()
+    moe.run_dispatch(b, bias=use_bias)
+    if c.rows_fp8:
+        moe.moe_expert_stub(b.shape, 0, b.expert_x, b.expert_scale, b.expert_off, b.expert_y)
+    y = b.expert_y if c.rows_fp8 else b.expert_x   # identity expert: bf16 combine reads expert_x
+    sh = b.shape
+    calls = {
+        "receive_side": [
+            lambda: moe.moe_combine_send(sh, y, b.expert_rpos, b.recv_off, b.send_off, b.cs_buf, b.cr_buf),
+            lambda: moe.moe_combine_recv(sh, b.cr_buf, b.send_pos, b.topk_w, b.out)],
+        "send_side": [
+            lambda: moe.moe_combine_acc_send(sh, y, b.recv_meta, b.counts, b.recv_off, b.expert_off,
+                                             b.send_off, b.topk_w, b.cs_buf, b.cr_buf),
+            lambda: moe.moe_combine_acc_recv(sh, b.cr_buf, b.topk_idx, b.send_pos, b.out)],
+    }
+    res = {}
+    outs = {}
+    for kind, fns in calls.items():
+        for _ in range(warmup):
+            for f in fns:
+                f()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        for k in range(steps):
+            for i, f in enumerate(fns):
+                evs[k][i].record(st)
+                f()
+            evs[k][2].record(st)
+        torch.cuda.synchronize()
+        send = sum(evs[k][0].elapsed_time(evs[k][1]) for k in range(steps)) * 1e3 / steps
+        recv = sum(evs[k][1].elapsed_time(evs[k][2]) for k in range(steps)) * 1e3 / steps
+        res[kind] = {"send_us": round(send, 2), "recv_us": round(recv, 2), "combine_us": round(send + recv, 2)}
+        outs[kind] = b.out.clone()
+    status = int(b.status.item())
+    if status != 0:
+        raise RuntimeError(f"device status word {status}")
+    # rows back: one per routed slot, or one per (token, owner rank)
+    idx = b.topk_idx.cpu().numpy().reshape(c.N * c.T, c.R)
+    owners = np.sort(idx // c.L, axis=1)
+    G = int(c.N * c.T + (owners[:, 1:] != owners[:, :-1]).sum())
+    NT, M, Pc = c.N * c.T, c.N * c.T * c.R, 2 * c.H
+    acc_bytes = (M * Pc + M * 12 + G * Pc) + (2 * G * Pc + M * 8) + (G * Pc + NT * Pc + M * 8)
+    std_bytes = alg_bytes(c)["combine"]
+    res["receive_side"]["alg_bytes"] = std_bytes
+    res["send_side"]["alg_bytes"] = acc_bytes
+    for kind in res:
+        res[kind]["gbs"] = round(res[kind]["alg_bytes"] / (res[kind]["combine_us"] * 1e3), 1)
+
+    def key(t):
+        u = t.view(torch.int16).to(torch.int32) & 0xFFFF
+        return torch.where(u >= 0x8000, -(u & 0x7FFF), u)
+    dist = (key(outs["send_side"]) - key(outs["receive_side"])).abs()
+    out = {"workload": name, "rows_sent_back": {"receive_side": M, "send_side": G},
+           "us": res, "speedup": round(res["receive_side"]["combine_us"] / res["send_side"]["combine_us"], 3),
+           "accuracy_vs_receive_side": {"max_bf16_ulp": int(dist.max().item()),
+                                        "frac_equal": round(float((dist == 0).float().mean().item()), 4)},
+           "experts": "identity"}
+    del b, outs
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -789,6 +874,8 @@ def main():
                     help="skip the one-rank-share timing leg")
     ap.add_argument("--no-microbatch", action="store_true",
                     help="skip the two-micro-batch pipelining leg")
+    ap.add_argument("--no-acc-combine", action="store_true",
+                    help="skip the leg timing the combine with the sum on the sending side")
     ap.add_argument("--flush-mall", action="store_true",
                     help="read a 1 GiB scratch buffer between timed steps (untimed by the "
                          "per-call events; included in ms_per_step)")
@@ -862,6 +949,8 @@ def main():
         line["micro_batches"] = microbatch_leg(HEADLINE)
     if not args.no_rank_leg:
         line["one_rank_share"] = [rank_leg(w) for w in (HEADLINE, "kimi_k2_worst")]
+    if not args.no_acc_combine:
+        line["acc_combine"] = [acc_combine_leg(w) for w in (HEADLINE, "kimi_k2_worst")]
     if calib is not None:
         line["plain_copy"] = calib
         line["frac_of_plain_copy"] = round(head["gbs"] / calib["gbs"], 4)

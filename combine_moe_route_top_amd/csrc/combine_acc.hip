@@ -22,22 +22,42 @@ namespace moe {
 // The token (t) of a receive row from its metadata (e * T*R + t*R + k).
 __device__ __forceinline__ int meta_token(int2 m, int TR, int R) { return (m.x % TR) / R; }
 
-// One wave's part of the partial row of receive row G (a global index over the call's ranks), if
-// G is its token's first row at its rank d.  Lane j < c holds the token's j-th row there
-// (consecutive rows, c <= min(R, L)), its expert-major position
+// Launch constants, overridable at build time for experiments: the partial kernel's blocks at most
+// (blocks step over the receive rows), and the chunks the network kernel's blocks aim for (several
+// rows per block: many rows move nothing).
+#ifndef MOE_ACC_PARTIAL_BLOCKS
+#define MOE_ACC_PARTIAL_BLOCKS 1048576
+#endif
+#ifndef MOE_ACC_NET_MIN_CHUNKS
+#define MOE_ACC_NET_MIN_CHUNKS 1792
+#endif
+
+// What a block needs to form one partial: where it goes, how many rows, their expert-major
+// positions and weights (c = 0: the row holds no partial).
+struct PartialDesc {
+    uint64_t src, dst;  // rank d's expert outputs; the partial's row in the combine send buffer
+    int c;
+    int q[64];
+    float w[64];
+};
+
+// Resolve receive row G (a global index over the call's ranks) into a PartialDesc, one wave.  The
+// row holds a partial if it is its token's first row at its rank d; lane j < c then takes the
+// token's j-th row there (consecutive rows, c <= min(R, L)): its expert-major position
 //   expert_off[d][e - d*L] + (rows of expert e from sources s' < s) + rank_e (metadata)
-// and its weight; the wave's chunks of the row are summed over j in slot order with fp32 fused
-// multiply-adds, up to 8 rows' loads in flight, and rounded once to bf16.
-__device__ __forceinline__ void acc_partial_row(const Dims& D, int WW, int part, long G, const int* gb,
-                                                const uint16_t* __restrict__ expert_y,
+// (the middle term: lanes hold sources, 8 rows' counts loaded together, one wave sum per row) and
+// its weight.
+__device__ __forceinline__ void resolve_partial(const Dims& D, long G, const int* gb,
                                                 const int32_t* __restrict__ recv_meta,
                                                 const int32_t* __restrict__ counts,
                                                 const int32_t* __restrict__ recv_off,
                                                 const int32_t* __restrict__ expert_off,
                                                 const float* __restrict__ topk_w,
-                                                uint16_t* __restrict__ cs_buf) {
+                                                const uint16_t* __restrict__ expert_y,
+                                                uint16_t* __restrict__ cs_buf, PartialDesc* pd) {
     const int N = D.N, L = D.L, E = D.E, TR = D.TR, R = D.R;
     const int lane = lane_id();
+    if (lane == 0) pd->c = 0;
     const int dl = wave_count_le(gb + 1, D.rc, G);
     const int d = D.rb + dl;
     const long r = G - gb[dl];
@@ -60,62 +80,113 @@ __device__ __forceinline__ void acc_partial_row(const Dims& D, int WW, int part,
     }
     const int c = __popcll(ballot(mine));  // lanes 0 .. c-1: the token's rows are consecutive
     const int e = mine ? mj.x / TR : 0;
-    // rows of expert e from earlier sources: one wave sum per row of the token
     int q = -1;
-    for (int j = 0; j < c; ++j) {
-        const int ej = readlane(e, j);
-        int v = 0;
-        for (int sp = lane; sp < s; sp += kWave) v += counts[(long)sp * E + ej];
-        const int before = wave_sum(v);
-        if (lane == j) {
-            const int jl = ej - d * L;
-            const long qq = (jl >= 0 && jl < L) ? (long)expert_off[(long)d * (L + 1) + jl] + before + mj.y : -1;
-            q = (qq >= 0 && qq < D.B) ? (int)qq : -1;
+    for (int j0 = 0; j0 < c; j0 += 8) {
+        int ej[8], cnt[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            ej[jj] = j0 + jj < c ? readlane(e, j0 + jj) : 0;
+            cnt[jj] = 0;
+        }
+        for (int sp0 = 0; sp0 < s; sp0 += kWave) {
+            const int sp = sp0 + lane;
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj)
+                if (sp < s && j0 + jj < c) cnt[jj] += counts[(long)sp * E + ej[jj]];
+        }
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            if (j0 + jj >= c) break;
+            const int before = wave_sum(cnt[jj]);
+            if (lane == j0 + jj) {
+                const int jl = ej[jj] - d * L;
+                const long qq = (jl >= 0 && jl < L) ? (long)expert_off[(long)d * (L + 1) + jl] + before + mj.y : -1;
+                q = (qq >= 0 && qq < D.B) ? (int)qq : -1;
+            }
         }
     }
     if (ballot(mine && q < 0)) {
         set_status(D.status, MOE_EINVAL);
         return;
     }
-    const float wj = mine ? topk_w[(size_t)s * TR + (mj.x - e * TR)] : 0.0f;
-
-    const u32x4* yrank = reinterpret_cast<const u32x4*>(expert_y + (size_t)d * D.B * D.H);
-    u32x4* orow = reinterpret_cast<u32x4*>(cs_buf + ((size_t)d * D.B + r) * D.H);
-    const int n16 = D.Y16;
-    for (int c0 = part * kWave + lane; c0 < n16; c0 += kWave * WW) {
-        float acc[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) acc[u] = 0.0f;
-        for (int j0 = 0; j0 < c; j0 += 8) {
-            u32x4 v[8];
-            float wk[8];
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                const int j = j0 + jj;
-                const int qj = j < c ? readlane(q, j) : -1;
-                wk[jj] = j < c ? readlane_f(wj, j) : 0.0f;
-                if (qj >= 0) v[jj] = ld_nt(yrank + (size_t)qj * n16 + c0);
-            }
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                if (j0 + jj >= c) continue;
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const float y = bf16_to_f32((v[jj][u >> 1] >> (16 * (u & 1))) & 0xFFFF);
-                    acc[u] = __builtin_fmaf(wk[jj], y, acc[u]);
-                }
-            }
-        }
-        u32x4 o;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) o[u] = f32_to_bf16(acc[2 * u]) | (f32_to_bf16(acc[2 * u + 1]) << 16);
-        st_nt(orow + c0, o);
+    if (mine) {
+        pd->q[lane] = q;
+        pd->w[lane] = topk_w[(size_t)s * TR + (mj.x - e * TR)];
+    }
+    if (lane == 0) {
+        pd->src = (uint64_t)(expert_y + (size_t)d * D.B * D.H);
+        pd->dst = (uint64_t)(cs_buf + ((size_t)d * D.B + r) * D.H);
+        pd->c = c;
     }
 }
 
-// Partial rows: WW waves per receive row of the call's ranks; waves step over the (row, part)
-// tasks (the grid is capped for calls on a subset of ranks, whose receive rows are few).
-__global__ __launch_bounds__(kBlock) void k_acc_partial(Dims D, int WW, const uint16_t* __restrict__ expert_y,
+// The block's threads form the partial row: UE chunks per thread per step, every load of a step
+// (UE * c <= 8, or the rows in groups of 8 when UE == 1) issued at once, each chunk's rows summed
+// in slot order with fp32 fused multiply-adds and rounded once to bf16.
+template <int UE>
+__device__ __forceinline__ void partial_stream(const PartialDesc* pd, int c, const u32x4* __restrict__ yrank,
+                                               int n16) {
+    u32x4* orow = reinterpret_cast<u32x4*>(pd->dst);
+    for (int cb = threadIdx.x; cb < n16; cb += kBlock * UE) {
+        if constexpr (UE > 1) {
+            u32x4 v[8];
+#pragma unroll
+            for (int n = 0; n < 8; ++n) {
+                const int j = n / UE, ch = cb + (n % UE) * kBlock;
+                if (j < c && ch < n16) v[n] = ld_nt(yrank + (size_t)pd->q[j] * n16 + ch);
+            }
+#pragma unroll
+            for (int u = 0; u < UE; ++u) {
+                const int ch = cb + u * kBlock;
+                float acc[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) acc[k] = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 8 / UE; ++j) {
+                    if (j >= c) break;
+                    const float w = pd->w[j];
+#pragma unroll
+                    for (int k = 0; k < 8; ++k)
+                        acc[k] = __builtin_fmaf(w, bf16_to_f32((v[j * UE + u][k >> 1] >> (16 * (k & 1))) & 0xFFFF),
+                                                acc[k]);
+                }
+                if (ch < n16) {
+                    u32x4 o;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) o[k] = f32_to_bf16(acc[2 * k]) | (f32_to_bf16(acc[2 * k + 1]) << 16);
+                    st_nt(orow + ch, o);
+                }
+            }
+        } else {
+            const int ch = cb;
+            float acc[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc[k] = 0.0f;
+            for (int j0 = 0; j0 < c; j0 += 8) {
+                u32x4 v[8];
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj)
+                    if (j0 + jj < c) v[jj] = ld_nt(yrank + (size_t)pd->q[j0 + jj] * n16 + ch);
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) {
+                    if (j0 + jj >= c) break;
+                    const float w = pd->w[j0 + jj];
+#pragma unroll
+                    for (int k = 0; k < 8; ++k)
+                        acc[k] = __builtin_fmaf(w, bf16_to_f32((v[jj][k >> 1] >> (16 * (k & 1))) & 0xFFFF), acc[k]);
+                }
+            }
+            u32x4 o;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) o[k] = f32_to_bf16(acc[2 * k]) | (f32_to_bf16(acc[2 * k + 1]) << 16);
+            st_nt(orow + ch, o);
+        }
+    }
+}
+
+// Partial rows: four receive rows per block and step (blocks step over the rows of the call's
+// ranks); each wave resolves one row, then the whole block streams the partials among them.
+__global__ __launch_bounds__(kBlock) void k_acc_partial(Dims D, const uint16_t* __restrict__ expert_y,
                                                         const int32_t* __restrict__ recv_meta,
                                                         const int32_t* __restrict__ counts,
                                                         const int32_t* __restrict__ recv_off,
@@ -123,14 +194,26 @@ __global__ __launch_bounds__(kBlock) void k_acc_partial(Dims D, int WW, const ui
                                                         const float* __restrict__ topk_w,
                                                         uint16_t* __restrict__ cs_buf) {
     extern __shared__ int gb[];
+    __shared__ PartialDesc pd[kWavesPerBlock];
     rank_bases(recv_off + (long)D.rb * (D.N + 1), D.N + 1, D.N, D.rc, gb);
     __syncthreads();
-    const long tasks = (long)gb[D.rc] * WW;
-    for (long gw = (long)blockIdx.x * kWavesPerBlock + wave_id(); gw < tasks;
-         gw += (long)gridDim.x * kWavesPerBlock) {
-        const long G = gw / WW;
-        acc_partial_row(D, WW, (int)(gw - G * WW), G, gb, expert_y, recv_meta, counts, recv_off, expert_off,
-                        topk_w, cs_buf);
+    const long total = gb[D.rc];
+    for (long G0 = (long)blockIdx.x * kWavesPerBlock; G0 < total; G0 += (long)gridDim.x * kWavesPerBlock) {
+        PartialDesc* mine = &pd[wave_id()];
+        if (G0 + wave_id() < total)
+            resolve_partial(D, G0 + wave_id(), gb, recv_meta, counts, recv_off, expert_off, topk_w, expert_y,
+                            cs_buf, mine);
+        else if (lane_id() == 0)
+            mine->c = 0;
+        __syncthreads();
+        for (int w = 0; w < kWavesPerBlock; ++w) {
+            const int c = pd[w].c;  // block-uniform
+            const u32x4* yrank = reinterpret_cast<const u32x4*>(pd[w].src);
+            if (c == 1 || c == 2) partial_stream<4>(&pd[w], c, yrank, D.Y16);
+            else if (c == 3 || c == 4) partial_stream<2>(&pd[w], c, yrank, D.Y16);
+            else if (c > 4) partial_stream<1>(&pd[w], c, yrank, D.Y16);
+        }
+        __syncthreads();  // pd is rewritten by the next step
     }
 }
 
@@ -245,8 +328,8 @@ __global__ __launch_bounds__(kBlock) void k_acc_sum(Dims D, int WW, const uint16
 
 // ------------------------------------------------------------------ launchers
 
-// Waves per row for the two sums: the fewest (at most 16) that cover a row with one 8-value chunk
-// per lane.
+// Waves per token for the source's sum: the fewest (at most 16) that cover a row with one
+// 8-value chunk per lane.
 static int acc_waves(const Dims& D) {
     return (int)std::min<long>(16, std::max<long>(1, (D.Y16 + kWave - 1) / kWave));
 }
@@ -257,11 +340,10 @@ hipError_t launch_combine_acc_send(const Dims& D, const uint16_t* expert_y, cons
                                    const float* topk_w, uint16_t* cs_buf, uint16_t* cr_buf,
                                    hipStream_t st) {
     const long rows = recv_rows_bound(D);  // rows the call's ranks received
-    const int WW = acc_waves(D);
-    hipLaunchKernelGGL(k_acc_partial, dim3((unsigned)row_blocks(D, rows * WW, kWavesPerBlock)), dim3(kBlock),
-                       (D.rc + 1) * 4, st, D, WW, expert_y, recv_meta, counts, recv_off, expert_off, topk_w,
-                       cs_buf);
-    const StreamShape sn = stream_shape(D.Y16, MOE_CNET_MIN_CHUNKS);
+    const long blocks = std::min<long>(MOE_ACC_PARTIAL_BLOCKS, row_blocks(D, rows, kWavesPerBlock));
+    hipLaunchKernelGGL(k_acc_partial, dim3((unsigned)blocks), dim3(kBlock), (D.rc + 1) * 4, st, D, expert_y,
+                       recv_meta, counts, recv_off, expert_off, topk_w, cs_buf);
+    const StreamShape sn = stream_shape(D.Y16, MOE_ACC_NET_MIN_CHUNKS);
 #define MOE_LAUNCH_S(R_, U_, S_)                                                                     \
     hipLaunchKernelGGL((k_acc_net<R_, U_, S_>), dim3(row_blocks(D, rows, R_)), dim3(kBlock), (D.rc + 1) * 4, \
                        st, D, (const uint16_t*)cs_buf, recv_meta, recv_off, send_off, cr_buf);
