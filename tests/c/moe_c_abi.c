@@ -214,8 +214,25 @@ static void decode_path(void) {
         if (dd > worst) worst = dd;
     }
     CHECK(worst <= 1, "combine out differs by %d bf16 ulp", worst);
+
+    /* the combine with the sum on the sending side, on the same dispatched buffers: bit for bit
+     * against the oracle's fp32 steps for every token whose router weights are identical */
+    MOE(moe_combine_acc(&sh, d_ey, d_rmeta, d_counts, d_roff, d_eoff, d_soff, d_w, d_idx, d_spos, d_cs,
+                        d_cr, d_out, st));
+    HIP(hipStreamSynchronize(st));
+    d2h(g_out, d_out, sz.out);
+    d2h(&g_status, status, 4);
+    CHECK(g_status == 0, "status word after the send-side sum %d", g_status);
+    oracle_combine_acc(&osh, 1, o_ey, o_esrc, o_erpos, o_roff, o_soff, o_idx, o_spos, o_w, o_cs, o_cr, o_out);
+    int64_t acc_tokens = 0;
+    for (int64_t tok = 0; tok < (int64_t)N * T; ++tok) {
+        if (memcmp(g_w + tok * R, o_w + tok * R, 4 * R)) continue;
+        CHECK(!memcmp(g_out + tok * H, o_out + tok * H, 2 * H), "send-side sum, token %lld", (long long)tok);
+        ++acc_tokens;
+    }
     (void)L;
-    printf("decode path: N%d T%d H%d E%d R%d checked (max %d bf16 ulp)\n", N, T, H, E, R, worst);
+    printf("decode path: N%d T%d H%d E%d R%d checked (max %d bf16 ulp); send-side sum bit-exact on %lld tokens\n",
+           N, T, H, E, R, worst, (long long)acc_tokens);
     HIP(hipStreamDestroy(st));
 }
 
