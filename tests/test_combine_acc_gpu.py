@@ -217,3 +217,78 @@ def test_acc_full_workload(name):
     parity.compare(g_std, o, c.N, c.T, c.H, c.E, c.R, c.fp8)
     g = _acc_run(b, c.N, c.T, c.H, c.E, c.R)
     print(_check_acc(g, g_std, o, c.N, c.T, c.H, c.E, c.R), flush=True)
+
+
+def test_acc_bad_expert_ids():
+    # dropped slots (out-of-range, negative and repeated ids) add nothing; a token's output depends
+    # only on its own rows, so tokens whose ids are untouched match the clean run bit for bit, and
+    # a token left with one valid slot of weight 1/2 gives exactly x / 2 (identity experts)
+    import combine_moe_route_top_amd as moe
+    N, T, H, E, R = 2, 8, 64, 8, 2
+    print("\ncase acc bad ids", flush=True)
+    inp = ms.make_inputs(N, T, H, E, R, False, "none", 0)
+    clean = ms.random_topk(N, T, E, R, seed=1)
+    bad = clean.copy()
+    bad[0, 0, 0] = E             # out of range
+    bad[1, 2, 1] = bad[1, 2, 0]  # repeated within a token
+    bad[1, 3, 0] = -1            # negative
+    outs = {}
+    for name, idx in (("clean", clean), ("bad", bad)):
+        b, g = parity.gpu_run(N, T, H, E, R, False, inp, topk_idx=idx)
+        assert g["status"][0] == (moe.MOE_EBADIDX if name == "bad" else 0), name
+        outs[name] = _acc_run(b, N, T, H, E, R)  # the combine itself finds nothing wrong
+        assert outs[name]["status"][0] == 0, name
+    touched = np.any(bad != clean, axis=2)
+    go, gc = outs["bad"]["out"], outs["clean"]["out"]
+    assert np.array_equal(go[~touched], gc[~touched])
+    half = ms.to_bf16_bits(ms.bf16_bits_to_f32(inp["x"]) * np.float32(0.5))
+    for s, t in zip(*np.nonzero(touched)):
+        assert np.array_equal(go[s, t], half[s, t]), (s, t)
+
+
+def test_acc_graph_replay_matches_eager():
+    # the layer with the send-side-sum combine captured in a HIP graph and replayed for new inputs
+    import combine_moe_route_top_amd as moe
+    N, T, H, E, R = 8, 64, 512, 64, 8
+    print("\ncase acc graph", flush=True)
+    g_buf = moe.alloc_buffers(N, T, H, E, R)
+    e_buf = moe.alloc_buffers(N, T, H, E, R)
+    inputs = [ms.make_inputs(N, T, H, E, R, False, "zipf", seed) for seed in range(3)]
+
+    def layer(b):
+        moe.moe_route(b.shape, b.logits, b.bias, b.topk_idx, b.topk_w)
+        moe.moe_dispatch_send(b.shape, b.x, None, b.topk_idx, b.counts, b.send_off, b.send_pos, b.send_buf,
+                              b.send_meta, b.workspace)
+        moe.moe_net_dispatch(b.shape, b.send_off, b.send_buf, b.send_meta, b.recv_buf, b.recv_meta, b.recv_off)
+        moe.moe_dispatch_recv(b.shape, b.counts, b.recv_off, b.recv_buf, b.recv_meta, b.expert_x, None,
+                              b.expert_cnt, b.expert_off, b.expert_src, b.expert_rpos, b.workspace)
+        moe.moe_expert_stub(b.shape, 1, b.expert_x, None, b.expert_off, b.expert_y)
+        moe.run_combine_acc(b)
+
+    parity.upload_inputs(g_buf, inputs[0])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer(g_buf)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer(g_buf)
+    torch.cuda.synchronize()
+    for i, inp in enumerate(inputs * 2):
+        parity.upload_inputs(g_buf, inp)
+        graph.replay()
+        parity.upload_inputs(e_buf, inp)
+        layer(e_buf)
+        torch.cuda.synchronize()
+        assert np.array_equal(g_buf.out.cpu().numpy(), e_buf.out.cpu().numpy()), i
+        assert int(g_buf.status.item()) == 0
+    # and the last replay against the oracle's fp32 steps
+    o = parity.oracle_run(N, T, H, E, R, False, inputs[-1], expert_mode=1)
+    g = parity.fetch(g_buf, N, T, R)
+    acc = oracle.combine_acc(o["shape"], 1, o["expert_y"], o["expert_src"], o["expert_rpos"], o["recv_off"],
+                             o["send_off"], o["topk_idx"].reshape(N, T * R), o["send_pos"], o["topk_w"])
+    same_w = np.all(g["topk_w"].reshape(N * T, R) == o["topk_w"], axis=1)
+    assert same_w.mean() > 0.99
+    assert np.array_equal(g["out"].reshape(N * T, H)[same_w], acc["out"].reshape(N * T, H)[same_w])
