@@ -678,8 +678,9 @@ def microbatch_leg(name, steps=10, warmup=2, inter=2048) -> dict:
 def rank_leg(name, steps=20, warmup=3) -> dict:
     """One rank's share at its real shape: every call restricted to a single rank (as each GPU of
     an expert-parallel deployment runs it), timed with HIP events, for the rank that receives the
-    most rows and for the median rank (by rows received).  The other ranks' data are in place
-    from a full step first; the network time between GPUs is not part of this."""
+    most rows and for the median rank (by rows received), and the rank's combine with the sum on
+    the sending side in place of its combine.  The other ranks' data are in place from a full step
+    first; the network time between GPUs is not part of this."""
     import numpy as np
     import torch
 
@@ -760,9 +761,26 @@ def rank_leg(name, steps=20, warmup=3) -> dict:
             graph.replay()
         g1.record(st)
         torch.cuda.synchronize()
+        # the rank's combine with the sum on the sending side instead (its two halves)
+        acc_fns = [lambda: moe.moe_combine_acc_send(sh, y, b.recv_meta, b.counts, b.recv_off, b.expert_off,
+                                                    b.send_off, b.topk_w, b.cs_buf, b.cr_buf, st),
+                   lambda: moe.moe_combine_acc_recv(sh, b.cr_buf, b.topk_idx, b.send_pos, b.out, st)]
+        for _ in range(warmup):
+            for f in acc_fns:
+                f()
+        torch.cuda.synchronize()
+        aev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        for k in range(steps):
+            for i, f in enumerate(acc_fns):
+                aev[k][i].record(st)
+                f()
+            aev[k][2].record(st)
+        torch.cuda.synchronize()
+        acc = {n: round(sum(aev[k][i].elapsed_time(aev[k][i + 1]) for k in range(steps)) * 1e3 / steps, 2)
+               for i, n in enumerate(["combine_acc_send", "combine_acc_recv"])}
         out[label] = {"rank": r, "rows_received": int(recv[r]), "us_per_layer": round(sum(per.values()), 2),
                       "graph_replay_us_per_layer": round(g0.elapsed_time(g1) * 1e3 / steps, 2),
-                      "per_call_us": per}
+                      "per_call_us": per, "send_side_sum_combine_us": acc}
         del graph
     status = int(b.status.item())
     if status != 0:
