@@ -69,23 +69,28 @@ __device__ __forceinline__ void resolve_partial(const Dims& D, long G, const int
     }
     const long seg0 = ro[s], seg1 = ro[s + 1];
     const int2* meta = reinterpret_cast<const int2*>(recv_meta) + (size_t)d * D.B;
-    const int t = meta_token(meta[r], TR, R);
-    if (r > seg0 && meta_token(meta[r - 1], TR, R) == t) return;  // not the token's first row here
-
+    // the metadata of row r - 1 (every lane) and of rows r + lane, loaded together
+    const int2 mprev = r > seg0 ? meta[r - 1] : make_int2(-1, 0);
+    const bool in = lane < R && r + lane < seg1;
     int2 mj = {0, 0};
-    bool mine = false;
-    if (lane < R && r + lane < seg1) {
-        mj = meta[r + lane];
-        mine = meta_token(mj, TR, R) == t;
-    }
+    if (in) mj = meta[r + lane];
+    const int t = meta_token(make_int2(readlane(mj.x, 0), 0), TR, R);  // lane 0 holds row r
+    if (r > seg0 && meta_token(mprev, TR, R) == t) return;  // not the token's first row here
+    const bool mine = in && meta_token(mj, TR, R) == t;
     const int c = __popcll(ballot(mine));  // lanes 0 .. c-1: the token's rows are consecutive
+    // row j's expert, its offset, weight and rank, issued before the counts' wave sums
     const int e = mine ? mj.x / TR : 0;
-    int q = -1;
+    const int jl = e - d * L, i = mj.x - e * TR;  // local expert; slot t*R + k of the source
+    const bool e_ok = !mine || (jl >= 0 && jl < L && i >= 0);
+    const int eoff = mine && e_ok ? expert_off[(long)d * (L + 1) + jl] : 0;
+    const float wj = mine && e_ok ? topk_w[(size_t)s * TR + i] : 0.0f;
+    const int ec = (e >= 0 && e < E) ? e : 0;  // counts are read in range whatever the metadata
+    int before = 0;
     for (int j0 = 0; j0 < c; j0 += 8) {
         int ej[8], cnt[8];
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
-            ej[jj] = j0 + jj < c ? readlane(e, j0 + jj) : 0;
+            ej[jj] = j0 + jj < c ? readlane(ec, j0 + jj) : 0;
             cnt[jj] = 0;
         }
         for (int sp0 = 0; sp0 < s; sp0 += kWave) {
@@ -97,21 +102,19 @@ __device__ __forceinline__ void resolve_partial(const Dims& D, long G, const int
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
             if (j0 + jj >= c) break;
-            const int before = wave_sum(cnt[jj]);
-            if (lane == j0 + jj) {
-                const int jl = ej[jj] - d * L;
-                const long qq = (jl >= 0 && jl < L) ? (long)expert_off[(long)d * (L + 1) + jl] + before + mj.y : -1;
-                q = (qq >= 0 && qq < D.B) ? (int)qq : -1;
-            }
+            const int b = wave_sum(cnt[jj]);
+            if (lane == j0 + jj) before = b;
         }
     }
+    const long qq = (long)eoff + before + mj.y;
+    const int q = mine && e_ok && qq >= 0 && qq < D.B ? (int)qq : -1;
     if (ballot(mine && q < 0)) {
         set_status(D.status, MOE_EINVAL);
         return;
     }
     if (mine) {
         pd->q[lane] = q;
-        pd->w[lane] = topk_w[(size_t)s * TR + (mj.x - e * TR)];
+        pd->w[lane] = wj;
     }
     if (lane == 0) {
         pd->src = (uint64_t)(expert_y + (size_t)d * D.B * D.H);
@@ -184,8 +187,11 @@ __device__ __forceinline__ void partial_stream(const PartialDesc* pd, int c, con
     }
 }
 
-// Partial rows: four receive rows per block and step (blocks step over the rows of the call's
-// ranks); each wave resolves one row, then the whole block streams the partials among them.
+// Partial rows: rpb receive rows per block and step (blocks step over the rows of the call's
+// ranks); wave w < rpb resolves one row, then the whole block streams the partials among them in
+// turn.  Four rows per step hide the resolve latency when every block has several rows to do; one
+// row per step keeps a small call (one rank's few rows) short.  The choice follows the device-side
+// row count, the same for every block.
 __global__ __launch_bounds__(kBlock) void k_acc_partial(Dims D, const uint16_t* __restrict__ expert_y,
                                                         const int32_t* __restrict__ recv_meta,
                                                         const int32_t* __restrict__ counts,
@@ -198,15 +204,18 @@ __global__ __launch_bounds__(kBlock) void k_acc_partial(Dims D, const uint16_t* 
     rank_bases(recv_off + (long)D.rb * (D.N + 1), D.N + 1, D.N, D.rc, gb);
     __syncthreads();
     const long total = gb[D.rc];
-    for (long G0 = (long)blockIdx.x * kWavesPerBlock; G0 < total; G0 += (long)gridDim.x * kWavesPerBlock) {
-        PartialDesc* mine = &pd[wave_id()];
-        if (G0 + wave_id() < total)
-            resolve_partial(D, G0 + wave_id(), gb, recv_meta, counts, recv_off, expert_off, topk_w, expert_y,
-                            cs_buf, mine);
-        else if (lane_id() == 0)
-            mine->c = 0;
+    const int rpb = total >= (long)gridDim.x * kWavesPerBlock ? kWavesPerBlock : 1;
+    for (long G0 = (long)blockIdx.x * rpb; G0 < total; G0 += (long)gridDim.x * rpb) {
+        if (wave_id() < rpb) {
+            PartialDesc* mine = &pd[wave_id()];
+            if (G0 + wave_id() < total)
+                resolve_partial(D, G0 + wave_id(), gb, recv_meta, counts, recv_off, expert_off, topk_w, expert_y,
+                                cs_buf, mine);
+            else if (lane_id() == 0)
+                mine->c = 0;
+        }
         __syncthreads();
-        for (int w = 0; w < kWavesPerBlock; ++w) {
+        for (int w = 0; w < rpb; ++w) {
             const int c = pd[w].c;  // block-uniform
             const u32x4* yrank = reinterpret_cast<const u32x4*>(pd[w].src);
             if (c == 1 || c == 2) partial_stream<4>(&pd[w], c, yrank, D.Y16);
