@@ -120,6 +120,10 @@ def test_prefill_layout_sizes_and_guards():
         lambda: moe.moe_prefill_allreduce(dsh, good, good, stream=0),
         lambda: moe.moe_prefill_combine(dsh, good, good, good, good, good, good, stream=0),
         lambda: moe.moe_prefill_combine(psh, good, good, good, good, good, good + 4, stream=0),
+        lambda: moe.moe_combine_acc(psh, good, good, good, good, good, good, good, good, good, good, good,
+                                    good, stream=0),
+        lambda: moe.moe_combine_acc_send(psh, good, good, good, good, good, good, good, good, good, stream=0),
+        lambda: moe.moe_combine_acc_recv(psh, good, good, good, good, stream=0),
         lambda: moe.moe_prefill_dispatch(psh, good + 4, None, good, good, good, None, good, good,
                                          good, good, stream=0),
     ]
@@ -168,6 +172,17 @@ def test_null_and_misaligned_pointers_rejected_before_launch():
         lambda: moe.moe_combine_send(sh, good, None, good, good, good, good, stream=0),
         lambda: moe.moe_combine_recv(sh, good, good, good, bad, stream=0),
         lambda: moe.moe_combine_recv(sh, good, good, None, good, stream=0),
+        # the send-side-sum combine: metadata 8-byte aligned, every pointer present
+        lambda: moe.moe_combine_acc(sh, good, good + 4, good, good, good, good, good, good, good, good, good,
+                                    good, stream=0),
+        lambda: moe.moe_combine_acc(sh, good, good, good, good, good, good, good, None, good, good, good,
+                                    good, stream=0),
+        lambda: moe.moe_combine_acc(sh, good, good, good, good, good, good, good, good, good, good, good,
+                                    bad, stream=0),
+        lambda: moe.moe_combine_acc_send(sh, good, good, good, good, None, good, good, good, good, stream=0),
+        lambda: moe.moe_combine_acc_send(sh, good, good, good, good, good, good, good, bad, good, stream=0),
+        lambda: moe.moe_combine_acc_recv(sh, good, good, good, bad, stream=0),
+        lambda: moe.moe_combine_acc_recv(sh, good, None, good, good, stream=0),
     ]
     for fn in cases:
         with pytest.raises(moe.MoeError) as ex:
