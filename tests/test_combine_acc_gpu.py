@@ -123,6 +123,8 @@ SMALL = [  # N, T, H, E, R, fp8, bias
     (2, 3, 16, 6, 6, False, "none"),          # R = E: 3 rows per token and owner
     (16, 32, 512, 96, 8, True, "kimi"),       # Kimi-shaped: 6 rows of each token at rank 0
     (65, 3, 8, 130, 3, False, "none"),        # 65 ranks
+    (2, 20, 256, 64, 16, False, "none"),      # up to 16 rows of a token at one rank (two groups of 8)
+    (2, 5, 64, 128, 64, False, "zipf"),       # R = 64: up to 64 rows of a token at one rank
 ]
 
 
