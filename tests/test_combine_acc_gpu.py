@@ -294,3 +294,27 @@ def test_acc_graph_replay_matches_eager():
     same_w = np.all(g["topk_w"].reshape(N * T, R) == o["topk_w"], axis=1)
     assert same_w.mean() > 0.99
     assert np.array_equal(g["out"].reshape(N * T, H)[same_w], acc["out"].reshape(N * T, H)[same_w])
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_acc_random_shape_sweep(seed):
+    # seeded random configurations: ranks, experts per rank, slots, tokens, hidden size, payload,
+    # bias and per-rank token counts drawn together
+    rng = np.random.default_rng(2000 + seed)
+    N = int(rng.choice([1, 2, 3, 5, 8, 16, 33]))
+    L = int(rng.integers(1, 9))
+    E = N * L
+    R = int(rng.integers(1, min(E, 12) + 1))
+    T = int(rng.integers(1, 130))
+    fp8 = bool(rng.random() < 0.3)
+    H = int(rng.choice([512, 1024])) if fp8 else 8 * int(rng.integers(1, 97))
+    bias = str(rng.choice(["none", "zipf"]))
+    tokens = rng.integers(0, T + 1, N).astype(np.int32) if rng.random() < 0.4 else None
+    print(f"\ncase acc sweep {seed}: N{N} T{T} H{H} E{E} R{R} fp8 {fp8} {bias} tokens "
+          f"{None if tokens is None else tokens.tolist()}", flush=True)
+    inp = ms.make_inputs(N, T, H, E, R, fp8, bias, seed)
+    b, g_std = parity.gpu_run(N, T, H, E, R, fp8, inp, expert_mode=1, tokens=tokens)
+    o = parity.oracle_run(N, T, H, E, R, fp8, inp, expert_mode=1, tokens=tokens)
+    parity.compare(g_std, o, N, T, H, E, R, fp8)
+    g = _acc_run(b, N, T, H, E, R, split=bool(seed % 2))
+    print(_check_acc(g, g_std, o, N, T, H, E, R, tokens=tokens), flush=True)
