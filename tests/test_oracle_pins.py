@@ -657,6 +657,34 @@ def test_random_expert_outputs_brute(case):
                 assert out1["out"][s, t, h] == brute.bf16_round_exact(Fraction(float(acc)))
 
 
+# ------------------------------------------------------------------ random small configurations
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_small_configurations_brute(seed):
+    # seeded random tiny shapes (ranks, experts per rank, slots, tokens, bias): the whole layout
+    # against the brute-force sort, both combines against their exact-rational definitions
+    rng = np.random.default_rng(3000 + seed)
+    N = int(rng.integers(1, 7))
+    L = int(rng.integers(1, 5))
+    E = N * L
+    R = int(rng.integers(1, min(E, 5) + 1))
+    T = int(rng.integers(1, 10))
+    H = int(rng.choice([8, 16]))
+    bias = str(rng.choice(["none", "zipf"]))
+    case = (N, T, H, E, R, False)
+    res = run_small(*case, seed=seed, bias=bias)
+    bf = brute.dispatch(N, T, E, R, res["idx"])
+    check_layout_brute(res, case, bf)
+    y = ms.random_y(N, res["sh"].B, H, seed=seed)
+    _, y_of = _y_lookup(res, N, T, E, R, y)
+    _, out0 = _combine(res, None, 0, y=y)
+    assert np.array_equal(out0["out"], brute.combine_exact(N, T, R, E, y_of, res["w"]))
+    for mode in (0, 1):
+        want, _ = brute.combine_acc_exact(N, T, R, L, res["idx"], y_of, res["w"], mode)
+        assert np.array_equal(_combine_acc(res, y, mode)["out"], want), mode
+
+
 # ------------------------------------------------------------------ combine, sum on the sending side
 
 
