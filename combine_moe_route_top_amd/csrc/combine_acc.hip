@@ -16,6 +16,7 @@
 #include <algorithm>
 
 #include "common.cuh"
+#include "slots.cuh"
 
 namespace moe {
 
@@ -295,13 +296,7 @@ __global__ __launch_bounds__(kBlock) void k_acc_sum(Dims D, int WW, const uint16
     const int pos = lane < R ? send_pos[tok * R + lane] : -1;
     const bool valid = pos >= 0 && pos < D.TR;
     const int owner = valid ? topk_idx[tok * R + lane] / D.L : 0;
-    uint64_t same = ballot(valid);
-    const int nb = D.N > 1 ? 32 - __clz(D.N - 1) : 0;
-    for (int b = 0; b < nb; ++b) {
-        const bool bit = (owner >> b) & 1;
-        const uint64_t ones = ballot(bit);
-        same &= bit ? ones : ~ones;
-    }
+    const uint64_t same = same_key_lanes(valid, owner, key_bits(D.N));
     const int my_pos = valid && (same & lanemask_lt()) == 0 ? pos : -1;
     const u32x4* rank_rows = reinterpret_cast<const u32x4*>(cr_buf + (size_t)s * D.TR * D.H);
     u32x4* orow = reinterpret_cast<u32x4*>(out + (size_t)tok * D.H);

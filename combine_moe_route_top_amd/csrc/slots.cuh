@@ -32,18 +32,23 @@ __device__ __forceinline__ long stage_chunk(const int32_t* __restrict__ idx_s, i
 // Bits needed to hold the keys 0 .. n-1.
 __device__ __forceinline__ int key_bits(int n) { return n > 1 ? 32 - __clz(n - 1) : 0; }
 
-// Stable rank of this lane's key among the active lanes of the wave with the same key (lower
-// lanes first); the lowest lane of each key group also stores the group's size in cnt_row[key].
-// Keys lie in [0, 2^nbits).  The lanes sharing a key are found in constant time, one ballot per
-// key bit (the ballot form of a multisplit): a lane keeps the lanes that agree with it on every
-// bit.
-__device__ __forceinline__ int wave_key_rank(bool active, int key, int nbits, int* cnt_row) {
+// The active lanes of the wave whose key equals this lane's (keys in [0, 2^nbits)), found in
+// constant time with one ballot per key bit (the ballot form of a multisplit): a lane keeps the
+// lanes that agree with it on every bit.
+__device__ __forceinline__ uint64_t same_key_lanes(bool active, int key, int nbits) {
     uint64_t same = ballot(active);
     for (int b = 0; b < nbits; ++b) {
         const bool bit = (key >> b) & 1;
         const uint64_t ones = ballot(bit);
         same &= bit ? ones : ~ones;
     }
+    return same;
+}
+
+// Stable rank of this lane's key among the active lanes of the wave with the same key (lower
+// lanes first); the lowest lane of each key group also stores the group's size in cnt_row[key].
+__device__ __forceinline__ int wave_key_rank(bool active, int key, int nbits, int* cnt_row) {
+    const uint64_t same = same_key_lanes(active, key, nbits);
     const uint64_t lower = same & lanemask_lt();
     if (active && lower == 0) cnt_row[key] = __popcll(same);
     return __popcll(lower);
