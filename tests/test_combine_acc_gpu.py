@@ -318,3 +318,16 @@ def test_acc_random_shape_sweep(seed):
     parity.compare(g_std, o, N, T, H, E, R, fp8)
     g = _acc_run(b, N, T, H, E, R, split=bool(seed % 2))
     print(_check_acc(g, g_std, o, N, T, H, E, R, tokens=tokens), flush=True)
+
+
+def test_acc_no_tokens_anywhere():
+    # every rank dispatches zero tokens: nothing is received, no partial formed, no output written
+    N, T, H, E, R = 4, 16, 64, 8, 2
+    print("\ncase acc no tokens", flush=True)
+    tokens = np.zeros(N, np.int32)
+    inp = ms.make_inputs(N, T, H, E, R, False, "none", 1)
+    b, g_std = parity.gpu_run(N, T, H, E, R, False, inp, tokens=tokens)
+    assert g_std["status"][0] == 0 and np.all(g_std["recv_off"] == 0)
+    g = _acc_run(b, N, T, H, E, R, split=True)
+    assert g["status"][0] == 0
+    assert np.all(g["out"] == POISON)
