@@ -102,10 +102,17 @@ def moe_abi_version() -> int:
 
 
 def _ptr(t):
+    """A device address: None, an int (a raw device pointer), or a contiguous GPU tensor.  Host
+    tensors and strided views are refused here: the kernels would read host addresses or assume
+    the wrong layout."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if not t.is_cuda:
+        raise ValueError("libmoe takes device memory: got a tensor on " + str(t.device))
+    if not t.is_contiguous():
+        raise ValueError("libmoe takes dense row-major buffers: got a strided view")
     return t.data_ptr()
 
 

@@ -6,6 +6,7 @@ import subprocess
 import sys
 
 import pytest
+import torch
 
 import combine_moe_route_top_amd as moe
 
@@ -227,3 +228,12 @@ def test_product_does_not_import_oracle():
             if f.endswith((".py", ".hip", ".cuh", ".h", ".cpp")):
                 src = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in src.replace("oracle/", ""), f
+
+
+def test_binding_refuses_host_tensors():
+    # a host tensor would hand the kernels a host address: refused before any call
+    sh = moe.make_shape(2, 16, 256, 8, 2)
+    good = 1 << 20
+    host = torch.zeros(2 * 16 * 8, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        moe.moe_route(sh, host, None, good, good, stream=0)
