@@ -137,6 +137,12 @@ inline long row_blocks(const Dims& D, long rows_bound, int rpb) {
     return b > D.rc ? b : D.rc;
 }
 
+// The routed rows of a whole exchange (N token sets of T*R rows) fit in the 256 MB memory-side
+// cache: the network kernel then stores them cached and the unpack reads them cached, so they need
+// not travel to HBM and back between the two (e4m3 DeepSeek-V3 rows: 242 MB).
+constexpr long kMallBytes = 256L << 20;
+inline bool exchange_fits_mall(const Dims& D) { return (long)D.N * D.TR * D.P <= kMallBytes; }
+
 // ------------------------------------------------------------------ block row streaming
 
 // Nontemporal 16-byte accesses: streamed data does not stay in the caches, and the stores do not
@@ -155,8 +161,10 @@ struct RowDesc {
     uint64_t src_a, src_b, dst_a, dst_b;
 };
 
-// Stream nrows resolved rows of n16 chunks each, flat over (row, chunk).
-template <int U>
+// Stream nrows resolved rows of n16 chunks each, flat over (row, chunk).  NTLD / NTST: nontemporal
+// loads / stores (the default); cached ones where the rows should stay in the memory-side cache
+// for the next kernel.
+template <int U, bool NTLD = true, bool NTST = true>
 __device__ __forceinline__ void block_stream_rows(const RowDesc* rows, int nrows, int n16,
                                                   int split_src, int split_dst) {
     const int total = nrows * n16;
@@ -175,7 +183,7 @@ __device__ __forceinline__ void block_stream_rows(const RowDesc* rows, int nrows
                 const int c = k - r * n16;
                 const u32x4* src = c < split_src ? (const u32x4*)rows[r].src_a + c
                                                  : (const u32x4*)rows[r].src_b + (c - split_src);
-                v[u] = ld_nt(src);
+                v[u] = NTLD ? ld_nt(src) : *src;
             }
         }
 #pragma unroll
@@ -186,7 +194,8 @@ __device__ __forceinline__ void block_stream_rows(const RowDesc* rows, int nrows
                 const int c = k - r * n16;
                 u32x4* dst = c < split_dst ? (u32x4*)rows[r].dst_a + c
                                            : (u32x4*)rows[r].dst_b + (c - split_dst);
-                st_nt(dst, v[u]);
+                if (NTST) st_nt(dst, v[u]);
+                else *dst = v[u];
             }
         }
     }

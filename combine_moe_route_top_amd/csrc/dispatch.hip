@@ -282,7 +282,7 @@ __device__ __forceinline__ int recv_offset(const int32_t* __restrict__ send_off,
 // found by a ballot over send_off[s] and it lands at recv_off[d][s] + (i - send_off[s][d]) in
 // rank d's receive buffer, metadata alongside; then the block streams the rows.  Blocks 0..N-1
 // also write row d = blockIdx of the recv_off output (a wave scan over sources).
-template <int RPB, int U>
+template <int RPB, int U, bool CACHED>
 __global__ __launch_bounds__(kBlock) void k_net_dispatch(Dims D, const int32_t* __restrict__ send_off,
                                                          const uint8_t* __restrict__ send_buf,
                                                          const int32_t* __restrict__ send_meta,
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(kBlock) void k_net_dispatch(Dims D, const int32_t* 
     }
     if (wave_id() < RPB && lane_id() == 0) rows[wave_id()] = rd;
     __syncthreads();
-    block_stream_rows<U>(rows, RPB, D.P16, D.P16, D.P16);
+    block_stream_rows<U, true, !CACHED>(rows, RPB, D.P16, D.P16, D.P16);
 }
 
 // ------------------------------------------------------------------ receive side
@@ -355,7 +355,7 @@ __device__ __forceinline__ long expert_base(const int32_t* __restrict__ counts, 
 // the expert_cnt and expert_off of rank rank_begin + b.  STRIDE: blocks stride over the rows
 // (a capped grid, for calls on a subset of ranks); otherwise the grid covers every row once, a
 // shape that keeps fewer registers live.
-template <int RPB, int U, bool STRIDE>
+template <int RPB, int U, bool STRIDE, bool CACHED>
 __global__ __launch_bounds__(kBlock) void k_unpack(Dims D, const int32_t* __restrict__ counts,
                                                    const int32_t* __restrict__ recv_off,
                                                    const uint8_t* __restrict__ recv_buf,
@@ -422,7 +422,7 @@ __global__ __launch_bounds__(kBlock) void k_unpack(Dims D, const int32_t* __rest
         }
         if (wave_id() < RPB && lane_id() == 0) rows[wave_id()] = rd;
         __syncthreads();
-        block_stream_rows<U>(rows, RPB, D.P16, D.P16, D.X16);
+        block_stream_rows<U, !CACHED, true>(rows, RPB, D.P16, D.P16, D.X16);
     };
     if constexpr (STRIDE) {
         for (long base = (long)blockIdx.x * RPB; base < total; base += (long)gridDim.x * RPB) {
@@ -509,12 +509,17 @@ hipError_t launch_net_dispatch(const Dims& D, const int32_t* send_off, const voi
     const long rows = (long)D.rc * D.TR;  // the send rows of the call's ranks
     const StreamShape sh = stream_shape(D.P16, MOE_NET_MIN_CHUNKS);
     const long blocks = std::max<long>((rows + sh.rpb - 1) / sh.rpb, D.rc);
-#define MOE_LAUNCH(R_, U_)                                                                         \
-    if (sh.rpb == R_ && sh.u == U_)                                                                \
-        hipLaunchKernelGGL((k_net_dispatch<R_, U_>), dim3(blocks), dim3(kBlock), 0, st, D, send_off, \
-                           (const uint8_t*)send_buf, send_meta, (uint8_t*)recv_buf, recv_meta, recv_off);
+    const bool cached = exchange_fits_mall(D);
+#define MOE_LAUNCH_C(R_, U_, C_)                                                                    \
+    hipLaunchKernelGGL((k_net_dispatch<R_, U_, C_>), dim3(blocks), dim3(kBlock), 0, st, D, send_off, \
+                       (const uint8_t*)send_buf, send_meta, (uint8_t*)recv_buf, recv_meta, recv_off);
+#define MOE_LAUNCH(R_, U_)                                                                          \
+    if (sh.rpb == R_ && sh.u == U_) {                                                               \
+        if (cached) MOE_LAUNCH_C(R_, U_, true) else MOE_LAUNCH_C(R_, U_, false)                     \
+    }
     MOE_STREAM_SHAPES(MOE_LAUNCH)
 #undef MOE_LAUNCH
+#undef MOE_LAUNCH_C
     return hipGetLastError();
 }
 
@@ -529,13 +534,18 @@ hipError_t launch_dispatch_recv(const Dims& D, const int32_t* counts, const int3
     const StreamShape sh = stream_shape(D.P16, MOE_UNPACK_MIN_CHUNKS);
     const long blocks = row_blocks(D, rows, sh.rpb);
     const bool stride = blocks * sh.rpb < rows;
-#define MOE_LAUNCH_S(R_, U_, S_)                                                                    \
-    hipLaunchKernelGGL((k_unpack<R_, U_, S_>), dim3(blocks), dim3(kBlock), (D.rc + 1) * 4, st, D, counts, \
+    const bool cached = exchange_fits_mall(D);  // the network kernel left the rows in the cache
+#define MOE_LAUNCH_S(R_, U_, S_, C_)                                                                \
+    hipLaunchKernelGGL((k_unpack<R_, U_, S_, C_>), dim3(blocks), dim3(kBlock), (D.rc + 1) * 4, st, D, counts, \
                        recv_off, (const uint8_t*)recv_buf, recv_meta, (uint8_t*)expert_x, expert_scale,  \
                        expert_cnt, expert_off, expert_src, expert_rpos);
 #define MOE_LAUNCH(R_, U_)                                                                          \
     if (sh.rpb == R_ && sh.u == U_) {                                                               \
-        if (stride) MOE_LAUNCH_S(R_, U_, true) else MOE_LAUNCH_S(R_, U_, false)                     \
+        if (stride) {                                                                               \
+            if (cached) MOE_LAUNCH_S(R_, U_, true, true) else MOE_LAUNCH_S(R_, U_, true, false)     \
+        } else {                                                                                    \
+            if (cached) MOE_LAUNCH_S(R_, U_, false, true) else MOE_LAUNCH_S(R_, U_, false, false)   \
+        }                                                                                           \
     }
     MOE_STREAM_SHAPES(MOE_LAUNCH)
 #undef MOE_LAUNCH
