@@ -190,21 +190,25 @@ __global__ __launch_bounds__(kBlock) void k_combine_net(Dims D, const uint16_t* 
 
 // Weighted sum: out[s][t] = bf16(sum_k w[k] * cr[s][send_pos[k]]), fp32 fused multiply-adds in
 // slot order k = 0..R-1; dropped slots (send_pos < 0) add nothing.  WW waves per token, each
-// owning every WW-th group of 64 chunks; a lane keeps MOE_WSUM_CHUNKS chunks (8 hidden values
-// each) and up to 8 slots' loads in flight.  The launcher picks the fewest waves that cover the
-// row in one pass, at most MOE_WSUM_MAX_WAVES, so that short rows leave no wave idle.
-#ifndef MOE_WSUM_MAX_WAVES
-#define MOE_WSUM_MAX_WAVES 16
-#endif
-#ifndef MOE_WSUM_CHUNKS
-#define MOE_WSUM_CHUNKS 1
+// owning every WW-th group of 64 chunks; a lane keeps CU chunks (8 hidden values each) and, for
+// each, up to 8 slots' loads in flight.  The launcher picks CU by the size of the call and then
+// the fewest waves that cover the row in one pass (at most 16 waves at one chunk per lane, at
+// most 4 at four), so that short rows leave no wave idle.  Four chunks per lane over four waves
+// (a 7168-wide row in one pass) beat one chunk per lane over fourteen waves by 10-12% on the
+// full-size decode layers with the memory-side cache flushed before each call (equal without):
+// fewer, longer-lived waves pay the per-token table loads once for four chunks, at the same
+// loads in flight per SIMD (179 VGPRs, two waves per SIMD).  A call on one rank's 128 tokens has
+// too few of those waves to fill the GPU (8.0 against 11.3 us), so calls that would launch fewer
+// than MOE_WSUM_WIDE_MIN_WAVES waves in the four-chunk shape keep one chunk per lane.
+#ifndef MOE_WSUM_WIDE_MIN_WAVES
+#define MOE_WSUM_WIDE_MIN_WAVES 4096
 #endif
 
+template <int CU>
 __global__ __launch_bounds__(kBlock) void k_wsum(Dims D, int WW, const uint16_t* __restrict__ cr_buf,
                                                  const int32_t* __restrict__ send_pos,
                                                  const float* __restrict__ topk_w,
                                                  uint16_t* __restrict__ out) {
-    constexpr int CU = MOE_WSUM_CHUNKS;
     const long gw = (long)blockIdx.x * kWavesPerBlock + wave_id();
     const long tok = gw / WW;  // within the call's ranks
     const int part = (int)(gw - tok * WW);
@@ -317,11 +321,22 @@ hipError_t launch_combine_recv(const Dims& D, const uint16_t* cr_buf, const int3
     send_pos += rb * D.TR;
     topk_w += rb * D.T * D.R;
     out += rb * D.T * D.H;
-    const int WW = (int)std::min<long>(MOE_WSUM_MAX_WAVES, std::max<long>(1, (D.Y16 + MOE_WSUM_CHUNKS * kWave - 1) /
-                                                                      (MOE_WSUM_CHUNKS * kWave)));
-    const long waves = (long)D.rc * D.T * WW;
-    hipLaunchKernelGGL(k_wsum, dim3((waves + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock), 0, st, D,
-                       WW, cr_buf, send_pos, topk_w, out);
+    // waves per token covering the row in one pass at cu chunks per lane, at most max_ww
+    auto waves_per_token = [&](int cu, int max_ww) {
+        return (int)std::min<long>(max_ww, std::max<long>(1, (D.Y16 + cu * kWave - 1) / (cu * kWave)));
+    };
+    const long ntok = (long)D.rc * D.T;
+    const int ww4 = waves_per_token(4, 4);
+    if (ntok * ww4 >= MOE_WSUM_WIDE_MIN_WAVES) {
+        const long waves = ntok * ww4;
+        hipLaunchKernelGGL(k_wsum<4>, dim3((waves + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock), 0, st,
+                           D, ww4, cr_buf, send_pos, topk_w, out);
+    } else {
+        const int ww1 = waves_per_token(1, 16);
+        const long waves = ntok * ww1;
+        hipLaunchKernelGGL(k_wsum<1>, dim3((waves + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock), 0, st,
+                           D, ww1, cr_buf, send_pos, topk_w, out);
+    }
     return hipGetLastError();
 }
 
