@@ -265,7 +265,7 @@ __global__ __launch_bounds__(kBlock) void k_acc_net(Dims D, const uint16_t* __re
         }
         if (wave_id() < RPB && lane_id() == 0) rows[wave_id()] = rd;
         __syncthreads();
-        block_stream_rows<U>(rows, RPB, D.Y16, D.Y16, D.Y16);
+        block_stream_rows<U>(rows, RPB, D.Y16, D.Y16, D.Y16, cs_buf);
     };
     if constexpr (STRIDE) {
         for (long base = (long)blockIdx.x * RPB; base < total; base += (long)gridDim.x * RPB) {
@@ -280,7 +280,10 @@ __global__ __launch_bounds__(kBlock) void k_acc_net(Dims D, const uint16_t* __re
 // The source's sum: out[s][t] = bf16(fp32 sum of the token's partials in the order of their first
 // slots).  Slot k holds a partial if it is valid and no earlier valid slot of the token has the
 // same owner rank (one ballot per owner bit finds the lower lanes with the same owner).  WW waves
-// per token as in the receive-side weighted sum.
+// per token and CU chunks per lane, chosen as in the receive-side weighted sum, whose load
+// pattern it shares: a skipped slot contributes a zero chunk (exact, as the sums start at +0.0
+// and so are never -0.0) and a lane past the row's end reads the row's last chunk and drops it.
+template <int CU>
 __global__ __launch_bounds__(kBlock) void k_acc_sum(Dims D, int WW, const uint16_t* __restrict__ cr_buf,
                                                     const int32_t* __restrict__ send_pos,
                                                     const int32_t* __restrict__ topk_idx,
@@ -301,42 +304,64 @@ __global__ __launch_bounds__(kBlock) void k_acc_sum(Dims D, int WW, const uint16
     const u32x4* rank_rows = reinterpret_cast<const u32x4*>(cr_buf + (size_t)s * D.TR * D.H);
     u32x4* orow = reinterpret_cast<u32x4*>(out + (size_t)tok * D.H);
     const int n16 = D.Y16;
-    for (int c0 = part * kWave + lane; c0 < n16; c0 += kWave * WW) {
-        float acc[8];
+    for (int c0 = part * kWave + lane; c0 < n16; c0 += kWave * WW * CU) {
+        float acc[CU][8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) acc[u] = 0.0f;
+        for (int cu = 0; cu < CU; ++cu)
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc[cu][u] = 0.0f;
         for (int k0 = 0; k0 < R; k0 += 8) {
-            u32x4 v[8];
+            u32x4 v[CU][8];
             bool ok[8];
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
                 const int k = k0 + kk;
-                const int p = k < R ? readlane(my_pos, k) : -1;
+                const int pr = readlane(my_pos, k);  // k < 64 as R <= 64
+                const int p = k < R ? pr : -1;
                 ok[kk] = p >= 0;
-                if (ok[kk]) v[kk] = ld_nt(rank_rows + (size_t)p * n16 + c0);
+#pragma unroll
+                for (int cu = 0; cu < CU; ++cu) {
+                    const int c = min(c0 + cu * kWave * WW, n16 - 1);
+                    v[cu][kk] = u32x4{0u, 0u, 0u, 0u};
+                    if (ok[kk]) v[cu][kk] = ld_nt(rank_rows + (size_t)p * n16 + c);
+                }
             }
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
-                if (!ok[kk]) continue;
 #pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    acc[u] += bf16_to_f32((v[kk][u >> 1] >> (16 * (u & 1))) & 0xFFFF);
+                for (int cu = 0; cu < CU; ++cu)
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        acc[cu][u] += bf16_to_f32((v[cu][kk][u >> 1] >> (16 * (u & 1))) & 0xFFFF);
             }
         }
-        u32x4 o;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) o[u] = f32_to_bf16(acc[2 * u]) | (f32_to_bf16(acc[2 * u + 1]) << 16);
-        st_nt(orow + c0, o);
+        for (int cu = 0; cu < CU; ++cu) {
+            const int c = c0 + cu * kWave * WW;
+            if (c < n16) {
+                u32x4 o;
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    o[u] = f32_to_bf16(acc[cu][2 * u]) | (f32_to_bf16(acc[cu][2 * u + 1]) << 16);
+                st_nt(orow + c, o);
+            }
+        }
     }
 }
 
 // ------------------------------------------------------------------ launchers
 
-// Waves per token for the source's sum: the fewest (at most 16) that cover a row with one
-// 8-value chunk per lane.
-static int acc_waves(const Dims& D) {
-    return (int)std::min<long>(16, std::max<long>(1, (D.Y16 + kWave - 1) / kWave));
+// Waves per token for the source's sum: the fewest (at most max_ww) that cover a row with cu
+// 8-value chunks per lane.
+static int acc_waves(const Dims& D, int cu, int max_ww) {
+    return (int)std::min<long>(max_ww, std::max<long>(1, (D.Y16 + cu * kWave - 1) / (cu * kWave)));
 }
+#ifndef MOE_ACC_SUM_WIDE
+#define MOE_ACC_SUM_WIDE 1
+#endif
+#ifndef MOE_ACC_SUM_WIDE_MIN_WAVES
+#define MOE_ACC_SUM_WIDE_MIN_WAVES 4096
+#endif
 
 hipError_t launch_combine_acc_send(const Dims& D, const uint16_t* expert_y, const int32_t* recv_meta,
                                    const int32_t* counts, const int32_t* recv_off,
@@ -370,10 +395,18 @@ hipError_t launch_combine_acc_recv(const Dims& D, const uint16_t* cr_buf, const 
     send_pos += rb * D.TR;
     topk_idx += rb * D.TR;
     out += rb * D.T * D.H;
-    const int WW = acc_waves(D);
-    const long waves = (long)D.rc * D.T * WW;
-    hipLaunchKernelGGL(k_acc_sum, dim3((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock)), dim3(kBlock),
-                       0, st, D, WW, cr_buf, send_pos, topk_idx, out);
+    const long ntok = (long)D.rc * D.T;
+    const int ww4 = acc_waves(D, 4, 4);
+    if (MOE_ACC_SUM_WIDE && ntok * ww4 >= MOE_ACC_SUM_WIDE_MIN_WAVES) {
+        const long waves = ntok * ww4;
+        hipLaunchKernelGGL(k_acc_sum<4>, dim3((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock)),
+                           dim3(kBlock), 0, st, D, ww4, cr_buf, send_pos, topk_idx, out);
+    } else {
+        const int ww1 = acc_waves(D, 1, 16);
+        const long waves = ntok * ww1;
+        hipLaunchKernelGGL(k_acc_sum<1>, dim3((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock)),
+                           dim3(kBlock), 0, st, D, ww1, cr_buf, send_pos, topk_idx, out);
+    }
     return hipGetLastError();
 }
 

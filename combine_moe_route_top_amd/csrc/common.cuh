@@ -150,6 +150,22 @@ inline bool exchange_fits_mall(const Dims& D) { return (long)D.N * D.TR * D.P <=
 __device__ __forceinline__ u32x4 ld_nt(const u32x4* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void st_nt(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
 
+// The same through global-address-space pointers: the compiler then emits global_ (not flat_)
+// instructions, which it does not also count against the LDS counter.
+typedef __attribute__((address_space(1))) u32x4 g_u32x4;
+__device__ __forceinline__ const g_u32x4* as_global(const void* p) { return (const g_u32x4*)p; }
+__device__ __forceinline__ g_u32x4* as_global(void* p) { return (g_u32x4*)p; }
+template <bool NT>
+__device__ __forceinline__ u32x4 ld_g(const g_u32x4* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+template <bool NT>
+__device__ __forceinline__ void st_g(g_u32x4* p, u32x4 v) {
+    if constexpr (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
 // A row-copy kernel block (256 threads) handles RPB consecutive rows of its source: one row is
 // resolved per wave (its source and destination found), then all 256 threads stream the rows'
 // 16-byte chunks, U loads in flight per thread.  Launchers pick (RPB, U) from the row size:
@@ -163,10 +179,14 @@ struct RowDesc {
 
 // Stream nrows resolved rows of n16 chunks each, flat over (row, chunk).  NTLD / NTST: nontemporal
 // loads / stores (the default); cached ones where the rows should stay in the memory-side cache
-// for the next kernel.
+// for the next kernel.  `dummy` points at n16 readable chunks (the first row of the source
+// buffer): a lane past the block's chunks, or on a row that did not resolve (dst_a == 0), loads
+// from there and stores nothing, so that every load is unconditional.  With loads under the
+// per-lane test instead, the compiler could not tell which loaded registers were still in flight
+// and waited for each load before issuing the next, leaving one 16-byte load per thread in flight.
 template <int U, bool NTLD = true, bool NTST = true>
 __device__ __forceinline__ void block_stream_rows(const RowDesc* rows, int nrows, int n16,
-                                                  int split_src, int split_dst) {
+                                                  int split_src, int split_dst, const void* dummy) {
     const int total = nrows * n16;
     const float inv = 1.0f / (float)n16;
     for (int k0 = threadIdx.x; k0 < total; k0 += blockDim.x * U) {
@@ -175,16 +195,17 @@ __device__ __forceinline__ void block_stream_rows(const RowDesc* rows, int nrows
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int k = k0 + u * blockDim.x;
-            int r = (int)((float)k * inv);  // k / n16, corrected below (k < 2^24)
-            if (r * n16 > k) --r;
-            else if ((r + 1) * n16 <= k) ++r;
+            const int kc = k < total ? k : total - 1;
+            int r = (int)((float)kc * inv);  // kc / n16, corrected below (kc < 2^24)
+            if (r * n16 > kc) --r;
+            else if ((r + 1) * n16 <= kc) ++r;
             rr[u] = r;
-            if (k < total && rows[r].dst_a) {
-                const int c = k - r * n16;
-                const u32x4* src = c < split_src ? (const u32x4*)rows[r].src_a + c
-                                                 : (const u32x4*)rows[r].src_b + (c - split_src);
-                v[u] = NTLD ? ld_nt(src) : *src;
-            }
+            const int c = kc - r * n16;
+            const bool live = k < total && rows[r].dst_a;
+            const g_u32x4* src = !live ? as_global(dummy) + c
+                                 : c < split_src ? as_global((const void*)rows[r].src_a) + c
+                                                 : as_global((const void*)rows[r].src_b) + (c - split_src);
+            v[u] = ld_g<NTLD>(src);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -192,10 +213,9 @@ __device__ __forceinline__ void block_stream_rows(const RowDesc* rows, int nrows
             const int r = rr[u];
             if (k < total && rows[r].dst_a) {
                 const int c = k - r * n16;
-                u32x4* dst = c < split_dst ? (u32x4*)rows[r].dst_a + c
-                                           : (u32x4*)rows[r].dst_b + (c - split_dst);
-                if (NTST) st_nt(dst, v[u]);
-                else *dst = v[u];
+                g_u32x4* dst = c < split_dst ? as_global((void*)rows[r].dst_a) + c
+                                             : as_global((void*)rows[r].dst_b) + (c - split_dst);
+                st_g<NTST>(dst, v[u]);
             }
         }
     }

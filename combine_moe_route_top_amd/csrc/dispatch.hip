@@ -327,7 +327,7 @@ __global__ __launch_bounds__(kBlock) void k_net_dispatch(Dims D, const int32_t* 
     }
     if (wave_id() < RPB && lane_id() == 0) rows[wave_id()] = rd;
     __syncthreads();
-    block_stream_rows<U, true, !CACHED>(rows, RPB, D.P16, D.P16, D.P16);
+    block_stream_rows<U, true, !CACHED>(rows, RPB, D.P16, D.P16, D.P16, send_buf);
 }
 
 // ------------------------------------------------------------------ receive side
@@ -422,7 +422,7 @@ __global__ __launch_bounds__(kBlock) void k_unpack(Dims D, const int32_t* __rest
         }
         if (wave_id() < RPB && lane_id() == 0) rows[wave_id()] = rd;
         __syncthreads();
-        block_stream_rows<U, !CACHED, true>(rows, RPB, D.P16, D.P16, D.X16);
+        block_stream_rows<U, !CACHED, true>(rows, RPB, D.P16, D.P16, D.X16, recv_buf);
     };
     if constexpr (STRIDE) {
         for (long base = (long)blockIdx.x * RPB; base < total; base += (long)gridDim.x * RPB) {
