@@ -200,11 +200,6 @@ __global__ __launch_bounds__(kBlock) void k_combine_net(Dims D, const uint16_t* 
 // loads in flight per SIMD (179 VGPRs, two waves per SIMD).  A call on one rank's 128 tokens has
 // too few of those waves to fill the GPU (8.0 against 11.3 us), so calls that would launch fewer
 // than MOE_WSUM_WIDE_MIN_WAVES waves in the four-chunk shape keep one chunk per lane.
-// Every slot of the unrolled group adds: a dropped slot adds weight 0 times a zero chunk, which
-// leaves the sum exact (it starts at +0.0 and so is never -0.0), and a lane past the row's end
-// reads the row's last chunk and drops the result.  With loads and their use under the same
-// condition instead, the compiler could not prove that a loaded register was consumed before the
-// next group reused it and waited for every load in turn.
 #ifndef MOE_WSUM_WIDE_MIN_WAVES
 #define MOE_WSUM_WIDE_MIN_WAVES 4096
 #endif
@@ -240,20 +235,18 @@ __global__ __launch_bounds__(kBlock) void k_wsum(Dims D, int WW, const uint16_t*
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
                 const int k = k0 + kk;
-                const int pr = readlane(my_pos, k);  // k < 64 as R <= 64
-                const float wr = readlane_f(my_w, k);
-                const int pos = k < R ? pr : -1;
+                const int pos = k < R ? readlane(my_pos, k) : -1;
                 ok[kk] = pos >= 0 && pos < D.TR;
-                wk[kk] = ok[kk] ? wr : 0.0f;
+                wk[kk] = k < R ? readlane_f(my_w, k) : 0.0f;
 #pragma unroll
                 for (int cu = 0; cu < CU; ++cu) {
-                    const int c = min(c0 + cu * kWave * WW, n16 - 1);
-                    v[cu][kk] = u32x4{0u, 0u, 0u, 0u};
-                    if (ok[kk]) v[cu][kk] = ld_nt(rank_rows + (size_t)pos * n16 + c);
+                    const int c = c0 + cu * kWave * WW;
+                    if (ok[kk] && c < n16) v[cu][kk] = ld_nt(rank_rows + (size_t)pos * n16 + c);
                 }
             }
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
+                if (!ok[kk]) continue;
 #pragma unroll
                 for (int cu = 0; cu < CU; ++cu)
 #pragma unroll

@@ -23,12 +23,6 @@
 #ifndef MOE_PF_LOCAL_WAVES
 #define MOE_PF_LOCAL_WAVES 16
 #endif
-#ifndef MOE_PF_LOCAL_WIDE
-#define MOE_PF_LOCAL_WIDE 1
-#endif
-#ifndef MOE_PF_LOCAL_WIDE_MIN_WAVES
-#define MOE_PF_LOCAL_WIDE_MIN_WAVES 4096
-#endif
 #ifndef MOE_PF_PACK_MIN_WAVES
 #define MOE_PF_PACK_MIN_WAVES 4096
 #endif
@@ -164,11 +158,9 @@ __global__ __launch_bounds__(kBlock) void k_pf_pack(Dims D, int WPT, const uint8
 
 // partial[d][t] = the fp32 fused-multiply-add chain, in slot order, of w[t][k] * y[d][pos(t, k)]
 // over the token's slots k owned by rank d (zero when there are none).  LW waves per (rank,
-// token), each owning every LW-th group of 64 chunks of 8 hidden values; a lane keeps CU chunks
-// (8 fp32 sums each) and loads every owned slot's chunk before the multiply-adds.  Every slot of
-// the unrolled group adds (another rank's slot adds weight 0 times a zero chunk: exact, the sums
-// being never -0.0), so the compiler keeps all loads in flight.
-template <int CU>
+// token), each owning every LW-th group of 64 chunks of 8 hidden values (the launcher picks LW
+// so that a lane has one chunk where it can); a lane keeps one chunk (8 fp32 sums) and loads
+// every owned slot's chunk before the multiply-adds.
 __global__ __launch_bounds__(kBlock) void k_pf_local(Dims D, int LW, const uint16_t* __restrict__ expert_y,
                                                      const int32_t* __restrict__ topk_idx,
                                                      const int32_t* __restrict__ slot_pos,
@@ -189,52 +181,38 @@ __global__ __launch_bounds__(kBlock) void k_pf_local(Dims D, int LW, const uint1
     const u32x4* yrows = reinterpret_cast<const u32x4*>(expert_y + (size_t)d * D.B * D.H);
     u32x4* prow = reinterpret_cast<u32x4*>(partial + ((size_t)d * D.T + t) * D.H);
     const int n16 = D.Y16;
-    for (int c0 = part * kWave + lane; c0 < n16; c0 += kWave * LW * CU) {
-        float acc[CU][8];
+    for (int c = part * kWave + lane; c < n16; c += kWave * LW) {
+        float acc[8];
 #pragma unroll
-        for (int cu = 0; cu < CU; ++cu)
-#pragma unroll
-            for (int u = 0; u < 8; ++u) acc[cu][u] = 0.0f;
+        for (int u = 0; u < 8; ++u) acc[u] = 0.0f;
         for (int k0 = 0; k0 < R; k0 += 8) {
-            u32x4 v[CU][8];
+            u32x4 v[8];
             float wk[8];
+            bool ok[8];
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
                 const int k = k0 + kk;
-                const bool ok = k < R && ((slots >> k) & 1);
-                const float wr = readlane_f(wl, k);  // k < 64 as R <= 64
-                const int pr = readlane(pos, k);
-                wk[kk] = ok ? wr : 0.0f;
-                const int p = ok ? pr : 0;
+                ok[kk] = k < R && ((slots >> k) & 1);
+                wk[kk] = k < R ? readlane_f(wl, k) : 0.0f;
+                const int p = k < R ? readlane(pos, k) : 0;
+                if (ok[kk]) v[kk] = ld_nt(yrows + (size_t)p * n16 + c);
+            }
 #pragma unroll
-                for (int cu = 0; cu < CU; ++cu) {
-                    const int c = min(c0 + cu * kWave * LW, n16 - 1);
-                    v[cu][kk] = u32x4{0u, 0u, 0u, 0u};
-                    if (ok) v[cu][kk] = ld_nt(yrows + (size_t)p * n16 + c);
+            for (int kk = 0; kk < 8; ++kk) {
+                if (!ok[kk]) continue;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const float y = bf16_to_f32((v[kk][u >> 1] >> (16 * (u & 1))) & 0xFFFFu);
+                    acc[u] = __builtin_fmaf(wk[kk], y, acc[u]);
                 }
             }
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk)
-#pragma unroll
-                for (int cu = 0; cu < CU; ++cu)
-#pragma unroll
-                    for (int u = 0; u < 8; ++u) {
-                        const float y = bf16_to_f32((v[cu][kk][u >> 1] >> (16 * (u & 1))) & 0xFFFFu);
-                        acc[cu][u] = __builtin_fmaf(wk[kk], y, acc[cu][u]);
-                    }
         }
-#pragma unroll
-        for (int cu = 0; cu < CU; ++cu) {
-            const int c = c0 + cu * kWave * LW;
-            if (c < n16) {
-                u32x4 o0 = {__float_as_uint(acc[cu][0]), __float_as_uint(acc[cu][1]), __float_as_uint(acc[cu][2]),
-                            __float_as_uint(acc[cu][3])};
-                u32x4 o1 = {__float_as_uint(acc[cu][4]), __float_as_uint(acc[cu][5]), __float_as_uint(acc[cu][6]),
-                            __float_as_uint(acc[cu][7])};
-                st_nt(prow + 2 * c, o0);
-                st_nt(prow + 2 * c + 1, o1);
-            }
-        }
+        u32x4 o0 = {__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
+                    __float_as_uint(acc[3])};
+        u32x4 o1 = {__float_as_uint(acc[4]), __float_as_uint(acc[5]), __float_as_uint(acc[6]),
+                    __float_as_uint(acc[7])};
+        st_nt(prow + 2 * c, o0);
+        st_nt(prow + 2 * c + 1, o1);
     }
 }
 
@@ -303,21 +281,10 @@ hipError_t launch_prefill_dispatch(const Dims& D, const void* x, const float* x_
 hipError_t launch_prefill_local(const Dims& D, const uint16_t* expert_y, const int32_t* topk_idx,
                                 const int32_t* slot_pos, const float* topk_w, float* partial,
                                 hipStream_t st) {
-    auto waves_per_item = [&](int cu, int max_lw) {
-        return (int)std::min<long>(max_lw, std::max<long>(1, (D.Y16 + cu * kWave - 1) / (cu * kWave)));
-    };
-    const long items = (long)D.rc * D.T;
-    const int lw4 = waves_per_item(4, 4);
-    if (MOE_PF_LOCAL_WIDE && items * lw4 >= MOE_PF_LOCAL_WIDE_MIN_WAVES) {
-        const long waves = items * lw4;
-        hipLaunchKernelGGL(k_pf_local<4>, dim3((waves + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock), 0,
-                           st, D, lw4, expert_y, topk_idx, slot_pos, topk_w, partial);
-    } else {
-        const int lw1 = waves_per_item(1, MOE_PF_LOCAL_WAVES);
-        const long waves = items * lw1;
-        hipLaunchKernelGGL(k_pf_local<1>, dim3((waves + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock), 0,
-                           st, D, lw1, expert_y, topk_idx, slot_pos, topk_w, partial);
-    }
+    const int LW = (int)std::min<long>(MOE_PF_LOCAL_WAVES, std::max<long>(1, (D.Y16 + kWave - 1) / kWave));
+    const long waves = (long)D.rc * D.T * LW;
+    hipLaunchKernelGGL(k_pf_local, dim3((waves + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock), 0,
+                       st, D, LW, expert_y, topk_idx, slot_pos, topk_w, partial);
     return hipGetLastError();
 }
 
