@@ -228,7 +228,24 @@ __global__ __launch_bounds__(kBlock) void k_pf_allreduce(Dims D, const float* __
     float s[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) s[u] = 0.0f;
-    for (int d = 0; d < D.N; ++d) {
+    // four ranks' chunks in flight at a time, added in rank order
+    int d = 0;
+    for (; d + 4 <= D.N; d += 4) {
+        u32x4 a[4], b[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            a[j] = ld_nt(p + (d + j) * plane + 2 * g);
+            b[j] = ld_nt(p + (d + j) * plane + 2 * g + 1);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                s[u] = s[u] + __uint_as_float(a[j][u]);
+                s[4 + u] = s[4 + u] + __uint_as_float(b[j][u]);
+            }
+    }
+    for (; d < D.N; ++d) {
         const u32x4 a = ld_nt(p + d * plane + 2 * g);
         const u32x4 b = ld_nt(p + d * plane + 2 * g + 1);
 #pragma unroll
