@@ -280,9 +280,11 @@ __global__ __launch_bounds__(kBlock) void k_acc_net(Dims D, const uint16_t* __re
 // The source's sum: out[s][t] = bf16(fp32 sum of the token's partials in the order of their first
 // slots).  Slot k holds a partial if it is valid and no earlier valid slot of the token has the
 // same owner rank (one ballot per owner bit finds the lower lanes with the same owner).  WW waves
-// per token and CU chunks per lane, chosen as in the receive-side weighted sum, whose load
-// pattern it shares: a skipped slot contributes a zero chunk (exact, as the sums start at +0.0
-// and so are never -0.0) and a lane past the row's end reads the row's last chunk and drops it.
+// per token and CU chunks per lane, chosen as in the receive-side weighted sum.  Every slot of
+// the unrolled group adds: a skipped slot adds a zero chunk (exact, as the sums start at +0.0 and
+// so are never -0.0), and a lane past the row's end reads the row's last chunk and drops it.
+// With the loads and the adds both under the slot test, the generated code waited for each load
+// before issuing the next.
 template <int CU>
 __global__ __launch_bounds__(kBlock) void k_acc_sum(Dims D, int WW, const uint16_t* __restrict__ cr_buf,
                                                     const int32_t* __restrict__ send_pos,
