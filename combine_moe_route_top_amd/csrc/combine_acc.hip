@@ -358,9 +358,7 @@ __global__ __launch_bounds__(kBlock) void k_acc_sum(Dims D, int WW, const uint16
 static int acc_waves(const Dims& D, int cu, int max_ww) {
     return (int)std::min<long>(max_ww, std::max<long>(1, (D.Y16 + cu * kWave - 1) / (cu * kWave)));
 }
-#ifndef MOE_ACC_SUM_WIDE
-#define MOE_ACC_SUM_WIDE 1
-#endif
+// Calls with at least this many waves in the four-chunk shape take it (as the weighted sum does).
 #ifndef MOE_ACC_SUM_WIDE_MIN_WAVES
 #define MOE_ACC_SUM_WIDE_MIN_WAVES 4096
 #endif
@@ -399,7 +397,7 @@ hipError_t launch_combine_acc_recv(const Dims& D, const uint16_t* cr_buf, const 
     out += rb * D.T * D.H;
     const long ntok = (long)D.rc * D.T;
     const int ww4 = acc_waves(D, 4, 4);
-    if (MOE_ACC_SUM_WIDE && ntok * ww4 >= MOE_ACC_SUM_WIDE_MIN_WAVES) {
+    if (ntok * ww4 >= MOE_ACC_SUM_WIDE_MIN_WAVES) {
         const long waves = ntok * ww4;
         hipLaunchKernelGGL(k_acc_sum<4>, dim3((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock)),
                            dim3(kBlock), 0, st, D, ww4, cr_buf, send_pos, topk_idx, out);
