@@ -1,0 +1,92 @@
+"""Generated-code guards for the HIP kernels (CPU only: hipcc cross-compiles gfx950 here).
+
+Two properties that no parity test can see but that bound the kernels' speed:
+
+- no kernel spills to scratch (private) memory;
+- in the row-copy kernels, no 16-byte load is issued right after a wait for every outstanding
+  memory operation (``s_waitcnt vmcnt(0)``).  That pattern means the compiler could not keep the
+  thread's loads in flight together and issued them one at a time; it appeared when each load sat
+  under a per-lane condition, and cost the network and unpack kernels 5-10%.
+"""
+import importlib.util
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "combine_moe_route_top_amd", "csrc")
+
+
+def _build_module():
+    spec = importlib.util.spec_from_file_location(
+        "moe_build_flags", os.path.join(ROOT, "combine_moe_route_top_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def _hipcc():
+    b = _build_module()
+    if not (os.path.exists(b.HIPCC) or shutil.which(b.HIPCC)):
+        pytest.skip("hipcc not available")
+    return b
+
+
+def _device_asm(tmp_path, source):
+    """gfx950 assembly of one source and the compiler's resource-usage remarks."""
+    b = _hipcc()
+    flags = [f for f in b.FLAGS if f not in ("-fPIC", "-shared")]
+    out = os.path.join(str(tmp_path), os.path.basename(source) + ".s")
+    cmd = [b.HIPCC, *flags, "--offload-device-only", "-S", "-Rpass-analysis=kernel-resource-usage",
+           "-I", os.path.join(ROOT, "include"), os.path.join(CSRC, source), "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    return open(out).read(), r.stderr
+
+
+def _functions(asm):
+    """(mangled name, instruction lines) of every kernel in the assembly."""
+    for name in re.findall(r"^(_ZN3moe\w+):", asm, re.M):
+        i = asm.index(name + ":")
+        j = asm.index(".Lfunc_end", i)
+        lines = [l.strip() for l in asm[i:j].splitlines()]
+        yield name, [l for l in lines if l and not l.startswith((";", "."))]
+
+
+SOURCES = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
+
+
+@pytest.mark.parametrize("source", SOURCES)
+def test_no_kernel_spills_to_scratch(tmp_path, source):
+    asm, remarks = _device_asm(tmp_path, source)
+    sizes = [int(x) for x in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", remarks)]
+    if not sizes:  # a source with host code only (the entry points)
+        assert not list(_functions(asm)), "kernels found but no resource-usage remarks"
+        return
+    assert max(sizes) == 0, f"{source}: a kernel uses {max(sizes)} bytes of scratch per lane"
+
+
+COPY_KERNELS = {
+    "dispatch.hip": r"k_net_dispatch|k_unpack",
+    "combine.hip": r"k_combine_pack|k_combine_net",
+    "combine_acc.hip": r"k_acc_net",
+}
+
+
+@pytest.mark.parametrize("source", sorted(COPY_KERNELS))
+def test_row_copy_loads_stay_in_flight(tmp_path, source):
+    asm, _ = _device_asm(tmp_path, source)
+    checked, serial = 0, []
+    for name, lines in _functions(asm):
+        if not re.search(COPY_KERNELS[source], name):
+            continue
+        for k, line in enumerate(lines):
+            if re.match(r"(global|flat|buffer)_load_dwordx4", line):
+                checked += 1
+                if any(re.match(r"s_waitcnt vmcnt\(0\)", p) for p in lines[max(0, k - 2):k]):
+                    serial.append(name)
+    assert checked > 0, "no 16-byte loads found in the row-copy kernels"
+    assert not serial, f"loads issued after a full wait in {sorted(set(serial))[:4]}"
