@@ -348,7 +348,7 @@ def _sweep_case(seed):
     return N, T, H, E, R, str(kind), bias, tokens, tight, split
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(96))
 def test_random_shape_sweep(seed):
     # random configurations, each compared with the oracle stage by stage
     N, T, H, E, R, kind, bias, tokens, tight, split = _sweep_case(seed)
