@@ -135,3 +135,31 @@ def test_prefill_full_workload():
     o = parity.oracle_run_prefill(c.N, c.T, c.H, c.E, c.R, c.fp8, inp)
     print("  oracle done", flush=True)
     print(" ", parity.compare_prefill(g, o, c.N, c.T, c.H, c.E, c.R, c.fp8), flush=True)
+
+
+def _sweep_case(seed):
+    """A seeded random replicated-token configuration: ranks, experts per rank, slots, tokens,
+    hidden size, payload and bias drawn together (ranks up to 33, slot counts up to several
+    count chunks, hidden sizes that are not multiples of the 64-lane chunk groups)."""
+    rng = np.random.default_rng(3000 + seed)
+    N = int(rng.choice([1, 2, 3, 4, 5, 8, 16, 33]))
+    L = int(rng.integers(1, 9))
+    E = N * L
+    R = int(rng.integers(1, min(E, 9) + 1))
+    T = int(rng.integers(1, 700))
+    fp8 = bool(rng.random() < 0.3)
+    H = int(rng.choice([512, 1024])) if fp8 else 8 * int(rng.integers(1, 97))
+    bias = str(rng.choice(["none", "zipf"]))
+    split = bool(rng.random() < 0.5)
+    return N, T, H, E, R, fp8, bias, split
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_prefill_random_shape_sweep(seed):
+    N, T, H, E, R, fp8, bias, split = _sweep_case(seed)
+    case = (N, T, H, E, R, fp8, bias)
+    print(f"\ncase prefill sweep {seed}: {_id(case)} split {split}", flush=True)
+    inp = parity.prefill_inputs(T, H, E, R, fp8, bias, 10 + seed)
+    _, g = parity.gpu_run_prefill(N, T, H, E, R, fp8, inp, split=split)
+    o = parity.oracle_run_prefill(N, T, H, E, R, fp8, inp)
+    parity.compare_prefill(g, o, N, T, H, E, R, fp8)
