@@ -21,7 +21,9 @@
  *  - Payload buffers (x, x_scale, send_buf, recv_buf, expert_x, expert_scale, expert_y,
  *    cs_buf, cr_buf, out) must be 16-byte aligned; metadata 8-byte; everything else 4-byte.
  *  - Index types are int32.  Rows are addressed as [rank][row] with the row strides given by
- *    moe_sizes().
+ *    moe_sizes().  Every buffer must be the full size moe_sizes() gives, also for a call on a
+ *    rank range: the row-copy kernels may read the first row of their source buffer (for lanes
+ *    that have no row to move) and never write outside the call's rows.
  *  - Device-detected errors (an expert id outside [0, E), or the same expert twice in one
  *    token's R slots) set *shape->status to MOE_EBADIDX if it is still 0 (sticky) and drop the
  *    offending slot: it is not counted, not sent, gets send_pos = -1 and adds nothing to the
