@@ -200,7 +200,7 @@ def run_workload(name, steps, warmup, check=True, flush_mall=False):
         rec(3)
         moe.moe_dispatch_recv(sh, b.counts, b.recv_off, b.recv_buf, b.recv_meta, b.expert_x,
                               b.expert_scale, b.expert_cnt, b.expert_off, b.expert_src,
-                              b.expert_rpos, b.workspace, st)
+                              b.expert_rpos, st)
         rec(4)
         if c.rows_fp8:
             moe.moe_expert_stub(sh, 0, b.expert_x, b.expert_scale, b.expert_off, b.expert_y, st)
@@ -498,7 +498,7 @@ def overlap_leg(name, steps=10, warmup=2, inter=2048) -> dict:
                              b.recv_off, s1)
         moe.moe_dispatch_recv(sh, b.counts, b.recv_off, b.recv_buf, b.recv_meta, b.expert_x,
                               b.expert_scale, b.expert_cnt, b.expert_off, b.expert_src,
-                              b.expert_rpos, b.workspace, s1)
+                              b.expert_rpos, s1)
 
     def c_send():
         moe.moe_combine_send(sh, b.expert_x, b.expert_rpos, b.recv_off, b.send_off, b.cs_buf,
@@ -599,7 +599,7 @@ def microbatch_leg(name, steps=10, warmup=2, inter=2048) -> dict:
                              b.recv_off, st)
         moe.moe_dispatch_recv(b.shape, b.counts, b.recv_off, b.recv_buf, b.recv_meta, b.expert_x,
                               None, b.expert_cnt, b.expert_off, b.expert_src, b.expert_rpos,
-                              b.workspace, st)
+                              st)
 
     def compute(mb, st):
         _, xs, ys = mb
@@ -722,7 +722,7 @@ def rank_leg(name, steps=20, warmup=3) -> dict:
                                              b.recv_meta, b.recv_off, s_),
                 lambda: moe.moe_dispatch_recv(sh, b.counts, b.recv_off, b.recv_buf, b.recv_meta,
                                               b.expert_x, b.expert_scale, b.expert_cnt, b.expert_off,
-                                              b.expert_src, b.expert_rpos, b.workspace, s_),
+                                              b.expert_src, b.expert_rpos, s_),
                 lambda: moe.moe_combine_send(sh, y, b.expert_rpos, b.recv_off, b.send_off, b.cs_buf,
                                              b.cr_buf, s_),
                 lambda: moe.moe_combine_recv(sh, b.cr_buf, b.send_pos, b.topk_w, b.out, s_),

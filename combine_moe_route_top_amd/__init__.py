@@ -60,7 +60,7 @@ _SIGS = {
     "moe_route": [ctypes.POINTER(moe_shape), _vp, _vp, _vp, _vp, _vp],
     "moe_dispatch_send": [ctypes.POINTER(moe_shape)] + [_vp] * 10,
     "moe_net_dispatch": [ctypes.POINTER(moe_shape)] + [_vp] * 7,
-    "moe_dispatch_recv": [ctypes.POINTER(moe_shape)] + [_vp] * 12,
+    "moe_dispatch_recv": [ctypes.POINTER(moe_shape)] + [_vp] * 11,
     "moe_combine": [ctypes.POINTER(moe_shape)] + [_vp] * 10,
     "moe_combine_send": [ctypes.POINTER(moe_shape)] + [_vp] * 7,
     "moe_combine_recv": [ctypes.POINTER(moe_shape)] + [_vp] * 5,
@@ -170,11 +170,11 @@ def moe_net_dispatch(shape, send_off, send_buf, send_meta, recv_buf, recv_meta, 
 
 
 def moe_dispatch_recv(shape, counts, recv_off, recv_buf, recv_meta, expert_x, expert_scale,
-                      expert_cnt, expert_off, expert_src, expert_rpos, workspace, stream=None):
+                      expert_cnt, expert_off, expert_src, expert_rpos, stream=None):
     _check("moe_dispatch_recv", _lib.moe_dispatch_recv(
         ctypes.byref(shape), _ptr(counts), _ptr(recv_off), _ptr(recv_buf), _ptr(recv_meta),
         _ptr(expert_x), _ptr(expert_scale), _ptr(expert_cnt), _ptr(expert_off),
-        _ptr(expert_src), _ptr(expert_rpos), _ptr(workspace), _stream(stream)))
+        _ptr(expert_src), _ptr(expert_rpos), _stream(stream)))
 
 
 def moe_combine(shape, expert_y, expert_rpos, recv_off, send_off, send_pos, topk_w, cs_buf,
@@ -369,7 +369,7 @@ def run_dispatch(b: Buffers, bias=True, stream=None):
                      b.recv_off, stream)
     moe_dispatch_recv(b.shape, b.counts, b.recv_off, b.recv_buf, b.recv_meta, b.expert_x,
                       b.expert_scale, b.expert_cnt, b.expert_off, b.expert_src, b.expert_rpos,
-                      b.workspace, stream)
+                      stream)
 
 
 def run_combine(b: Buffers, expert_y=None, stream=None):

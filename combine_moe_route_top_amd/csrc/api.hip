@@ -4,19 +4,18 @@
 #include <limits.h>
 #include <stdint.h>
 
-#include "common.cuh"
+#include "common.hpp"
 
 namespace moe {
 hipError_t launch_route(const Dims&, const float*, const float*, int32_t*, float*, hipStream_t);
 size_t send_workspace_bytes(const Dims&);
-size_t recv_workspace_bytes(const Dims&);
 hipError_t launch_dispatch_send(const Dims&, const void*, const float*, const int32_t*, int32_t*,
                                 int32_t*, int32_t*, void*, int32_t*, void*, hipStream_t);
 hipError_t launch_net_dispatch(const Dims&, const int32_t*, const void*, const int32_t*, void*,
                                int32_t*, int32_t*, hipStream_t);
 hipError_t launch_dispatch_recv(const Dims&, const int32_t*, const int32_t*, const void*,
                                 const int32_t*, void*, float*, int32_t*, int32_t*, int32_t*,
-                                int32_t*, void*, hipStream_t);
+                                int32_t*, hipStream_t);
 hipError_t launch_expert_stub(const Dims&, int, const void*, const float*, const int32_t*,
                               uint16_t*, hipStream_t);
 hipError_t launch_combine_send(const Dims&, const uint16_t*, const int32_t*, const int32_t*,
@@ -159,9 +158,7 @@ int moe_sizes(const moe_shape* shape, moe_sizes_t* out) {
     if (D.prefill) {
         out->workspace = (int64_t)moe::prefill_workspace_bytes(D);
     } else {
-        size_t ws = moe::send_workspace_bytes(D);
-        size_t wr = moe::recv_workspace_bytes(D);
-        out->workspace = (int64_t)(ws > wr ? ws : wr);
+        out->workspace = (int64_t)moe::send_workspace_bytes(D);
     }
     return MOE_OK;
 }
@@ -210,7 +207,7 @@ int moe_net_dispatch(const moe_shape* shape, const int32_t* send_off, const void
 int moe_dispatch_recv(const moe_shape* shape, const int32_t* counts, const int32_t* recv_off,
                       const void* recv_buf, const int32_t* recv_meta, void* expert_x,
                       float* expert_scale, int32_t* expert_cnt, int32_t* expert_off,
-                      int32_t* expert_src, int32_t* expert_rpos, void* workspace, void* stream) {
+                      int32_t* expert_src, int32_t* expert_rpos, void* stream) {
     Dims D;
     int rc = make_dims(shape, &D);
     if (rc) return rc;
@@ -219,11 +216,10 @@ int moe_dispatch_recv(const moe_shape* shape, const int32_t* counts, const int32
         !aligned(recv_meta, 8) || !aligned(expert_x, 16) || !aligned(expert_cnt, 4) ||
         !aligned(expert_off, 4) || !aligned(expert_src, 4) || !aligned(expert_rpos, 4))
         return MOE_EINVAL;
-    if (moe::recv_workspace_bytes(D) > 0 && !aligned(workspace, 4)) return MOE_EINVAL;
     if (D.fp8 && !aligned(expert_scale, 16)) return MOE_EINVAL;
     return hip_status(moe::launch_dispatch_recv(D, counts, recv_off, recv_buf, recv_meta, expert_x,
                                                 expert_scale, expert_cnt, expert_off, expert_src,
-                                                expert_rpos, workspace, (hipStream_t)stream));
+                                                expert_rpos, (hipStream_t)stream));
 }
 
 int moe_combine_send(const moe_shape* shape, const uint16_t* expert_y, const int32_t* expert_rpos,
@@ -258,6 +254,7 @@ int moe_combine(const moe_shape* shape, const uint16_t* expert_y, const int32_t*
     int rc = make_dims(shape, &D);
     if (rc) return rc;
     if (D.prefill) return MOE_EINVAL;  // the decode layout only
+    if (D.rc != D.N) return MOE_EINVAL;  // its second half reads what every rank's first half wrote
     // validate both halves before launching either
     if (!aligned(expert_y, 16) || !aligned(expert_rpos, 4) || !aligned(recv_off, 4) ||
         !aligned(send_off, 4) || !aligned(send_pos, 4) || !aligned(topk_w, 4) ||
@@ -311,6 +308,7 @@ int moe_combine_acc(const moe_shape* shape, const uint16_t* expert_y, const int3
     int rc = make_dims(shape, &D);
     if (rc) return rc;
     if (D.prefill) return MOE_EINVAL;  // the decode layout only
+    if (D.rc != D.N) return MOE_EINVAL;  // its second half reads what every rank's first half wrote
     // validate both halves before launching either
     if (!acc_send_aligned(expert_y, recv_meta, counts, recv_off, expert_off, send_off, topk_w, cs_buf, cr_buf) ||
         !aligned(topk_idx, 4) || !aligned(send_pos, 4) || !aligned(out, 16))
@@ -386,6 +384,7 @@ int moe_prefill_combine(const moe_shape* shape, const uint16_t* expert_y, const 
     int rc = make_dims(shape, &D);
     if (rc) return rc;
     if (!D.prefill) return MOE_EINVAL;
+    if (D.rc != D.N) return MOE_EINVAL;  // the all-reduce reads every rank's partial
     // validate both steps before launching either
     if (!aligned(expert_y, 16) || !aligned(topk_idx, 4) || !aligned(slot_pos, 4) ||
         !aligned(topk_w, 4) || !aligned(partial, 16) || !aligned(out, 16))

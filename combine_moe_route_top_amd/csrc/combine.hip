@@ -9,7 +9,7 @@
 // the weighted average of all expert contributions into an externally allocated tensor).
 #include <algorithm>
 
-#include "common.cuh"
+#include "common.hpp"
 
 namespace moe {
 

@@ -15,8 +15,8 @@
 // dispatched row: 4 bytes).
 #include <algorithm>
 
-#include "common.cuh"
-#include "slots.cuh"
+#include "common.hpp"
+#include "slots.hpp"
 
 namespace moe {
 

@@ -1,4 +1,4 @@
-// common.cuh -- shared device helpers for the libmoe kernels (gfx950, wave64).
+// common.hpp -- shared device helpers for the libmoe kernels (gfx950, wave64).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>

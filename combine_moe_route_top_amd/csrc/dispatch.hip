@@ -15,8 +15,8 @@
 //  - expert-major tensor of rank d: by local expert j, then (source, token, slot).
 #include <algorithm>
 
-#include "common.cuh"
-#include "slots.cuh"
+#include "common.hpp"
+#include "slots.hpp"
 
 // Waves the send packs aim for (the grid is one token per wave when there are at least this many
 // tokens); overridable at build time for launch-shape experiments.
@@ -523,13 +523,10 @@ hipError_t launch_net_dispatch(const Dims& D, const int32_t* send_off, const voi
     return hipGetLastError();
 }
 
-size_t recv_workspace_bytes(const Dims&) { return 0; }
-
 hipError_t launch_dispatch_recv(const Dims& D, const int32_t* counts, const int32_t* recv_off,
                                 const void* recv_buf, const int32_t* recv_meta, void* expert_x,
                                 float* expert_scale, int32_t* expert_cnt, int32_t* expert_off,
-                                int32_t* expert_src, int32_t* expert_rpos, void* /*workspace*/,
-                                hipStream_t st) {
+                                int32_t* expert_src, int32_t* expert_rpos, hipStream_t st) {
     const long rows = recv_rows_bound(D);
     const StreamShape sh = stream_shape(D.P16, MOE_UNPACK_MIN_CHUNKS);
     const long blocks = row_blocks(D, rows, sh.rpb);

@@ -15,8 +15,8 @@
 //            slot order), k_pf_allreduce (fp32 sum over ranks 0..N-1, one rounding to bf16).
 #include <algorithm>
 
-#include "common.cuh"
-#include "slots.cuh"
+#include "common.hpp"
+#include "slots.hpp"
 
 // Launch-shape constants, overridable at build time for experiments: the most waves per (rank,
 // token) in the local accumulation, and the waves the pack aims for.

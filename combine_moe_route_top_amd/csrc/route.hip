@@ -13,7 +13,7 @@
 // rotations by 1, 2, 4, 8 inside each 16-lane row (plain VALU moves, no LDS crossbar), and for
 // G > 16 one or two lane swaps across rows.  Weights: softmax over the R selected values in fp64, summed in slot order, rounded
 // once to fp32.
-#include "common.cuh"
+#include "common.hpp"
 
 // Waves below which the launcher gives each token a wider lane group; overridable at build time
 // for launch-shape experiments.

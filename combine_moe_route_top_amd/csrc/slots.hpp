@@ -1,8 +1,8 @@
-// slots.cuh -- per-slot helpers shared by the count kernels of the decode and prefill
+// slots.hpp -- per-slot helpers shared by the count kernels of the decode and prefill
 // dispatches: slot validity, staging a chunk of expert ids in LDS, and stable per-key ranks
 // inside a wave.
 #pragma once
-#include "common.cuh"
+#include "common.hpp"
 
 namespace moe {
 

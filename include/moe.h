@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 5
+#define MOE_ABI_VERSION 6
 
 typedef enum {
     MOE_OK = 0,
@@ -172,12 +172,11 @@ int moe_net_dispatch(const moe_shape* shape, const int32_t* send_off, const void
  *   expert_cnt   i32[N][L] (out)    rows per local expert
  *   expert_off   i32[N][L+1] (out)  exclusive scan of expert_cnt
  *   expert_src   i32[N][B] (out)    s*T*R + t*R + k of each expert-major row
- *   expert_rpos  i32[N][B] (out)    the row's index in recv_buf (its receive position)
- *   workspace    reserved; this call needs none (may be NULL) */
+ *   expert_rpos  i32[N][B] (out)    the row's index in recv_buf (its receive position) */
 int moe_dispatch_recv(const moe_shape* shape, const int32_t* counts, const int32_t* recv_off,
                       const void* recv_buf, const int32_t* recv_meta, void* expert_x,
                       float* expert_scale, int32_t* expert_cnt, int32_t* expert_off,
-                      int32_t* expert_src, int32_t* expert_rpos, void* workspace, void* stream);
+                      int32_t* expert_src, int32_t* expert_rpos, void* stream);
 
 /* Combine.  [EFA] combine paragraphs: with the metadata known from dispatch, shuffle the expert
  * outputs, copy them back with one write per peer, and accumulate the weighted average from the
@@ -193,7 +192,9 @@ int moe_dispatch_recv(const moe_shape* shape, const int32_t* counts, const int32
 int moe_combine(const moe_shape* shape, const uint16_t* expert_y, const int32_t* expert_rpos,
                 const int32_t* recv_off, const int32_t* send_off, const int32_t* send_pos,
                 const float* topk_w, uint16_t* cs_buf, uint16_t* cr_buf, uint16_t* out,
-                void* stream);  /* = moe_combine_send then moe_combine_recv */
+                void* stream);  /* = moe_combine_send then moe_combine_recv.  All ranks only:
+                                   rank_count must be 0 or N (MOE_EINVAL otherwise), since the
+                                   weighted sum reads rows that every rank's send half writes. */
 
 /* Combine, send half: the shuffle and the network back (the first two steps of moe_combine).
  * [PORT] Portable kernels: send halves only issue writes, so other work (the shared expert,
@@ -234,7 +235,9 @@ int moe_combine_acc(const moe_shape* shape, const uint16_t* expert_y, const int3
                     const int32_t* counts, const int32_t* recv_off, const int32_t* expert_off,
                     const int32_t* send_off, const float* topk_w, const int32_t* topk_idx,
                     const int32_t* send_pos, uint16_t* cs_buf, uint16_t* cr_buf, uint16_t* out,
-                    void* stream);  /* = moe_combine_acc_send then moe_combine_acc_recv */
+                    void* stream);  /* = moe_combine_acc_send then moe_combine_acc_recv.  All
+                                       ranks only: rank_count must be 0 or N (MOE_EINVAL
+                                       otherwise), as for moe_combine. */
 
 /* Send half of moe_combine_acc: the partial rows and their network step back.
  *   arguments as for moe_combine_acc */
@@ -294,7 +297,9 @@ int moe_prefill_combine_local(const moe_shape* shape, const uint16_t* expert_y,
  * rank's partial whatever the rank range (each must have been written); out is bf16[T][H]. */
 int moe_prefill_allreduce(const moe_shape* shape, const float* partial, uint16_t* out, void* stream);
 
-/* = moe_prefill_combine_local then moe_prefill_allreduce (all arguments validated first). */
+/* = moe_prefill_combine_local then moe_prefill_allreduce (all arguments validated first).  All
+ * ranks only: rank_count must be 0 or N (MOE_EINVAL otherwise), since the all-reduce reads every
+ * rank's partial. */
 int moe_prefill_combine(const moe_shape* shape, const uint16_t* expert_y, const int32_t* topk_idx,
                         const int32_t* slot_pos, const float* topk_w, float* partial, uint16_t* out,
                         void* stream);

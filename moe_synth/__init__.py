@@ -185,6 +185,44 @@ def random_y(N: int, B: int, H: int, seed: int) -> np.ndarray:
     return to_bf16_bits(rng.standard_normal((N, B, H), dtype=np.float32))
 
 
+TIE_KINDS = ("equal", "levels", "signed_zero", "bias_round")
+
+
+def tie_logits(kind: str, n_tokens: int, E: int, seed: int):
+    """Router scores made to tie, for the selection order's tie rule.  Returns (logits f32
+    [n_tokens][E], bias f32[E] or None).
+      equal        every expert of a row has the same score (one N(0,1) value per row)
+      levels       N(0,1) rounded to multiples of 1/2: a handful of values, many ties per row,
+                   equal scores spread over every lane and lane group
+      signed_zero  negative scores with 2..E experts per row set to +0.0 or -0.0 (random sign),
+                   so the largest scores are zeros of both signs; no bias
+      bias_round   logits 1e-4 * N(0,1) and bias 1000 + (e % 4) * 2^-14 (2^-14 is one fp32 step
+                   at 1000): the fp32 sums fall on a few neighbouring values, so experts whose
+                   logits differ tie once the bias is added"""
+    rng = np.random.default_rng(seed + 31337)
+    if kind == "equal":
+        v = rng.standard_normal((n_tokens, 1), dtype=np.float32)
+        return np.repeat(v, E, axis=1), None
+    if kind == "levels":
+        v = rng.standard_normal((n_tokens, E), dtype=np.float32)
+        return (np.round(v * 2.0) / 2.0).astype(np.float32), None
+    if kind == "signed_zero":
+        v = -np.abs(rng.standard_normal((n_tokens, E), dtype=np.float32)) - np.float32(0.5)
+        nz = rng.integers(min(2, E), E + 1, n_tokens)
+        keys = rng.random((n_tokens, E))
+        ranks = np.argsort(np.argsort(keys, axis=1), axis=1)
+        zero = ranks < nz[:, None]
+        sign = rng.random((n_tokens, E)) < 0.5
+        v[zero & sign] = np.float32(-0.0)
+        v[zero & ~sign] = np.float32(0.0)
+        return v.astype(np.float32), None
+    if kind == "bias_round":
+        v = (rng.standard_normal((n_tokens, E), dtype=np.float32) * np.float32(1e-4)).astype(np.float32)
+        bias = (np.float32(1000.0) + (np.arange(E) % 4).astype(np.float32) * np.float32(2.0 ** -14))
+        return v, bias.astype(np.float32)
+    raise ValueError(kind)
+
+
 def random_topk(N: int, T: int, E: int, R: int, seed: int) -> np.ndarray:
     """R distinct experts per token drawn uniformly: int32[N][T][R]."""
     rng = np.random.default_rng(seed + 104729)

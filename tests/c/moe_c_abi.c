@@ -144,7 +144,7 @@ static void decode_path(void) {
     MOE(moe_dispatch_send(&sh, d_x, NULL, d_idx, d_counts, d_soff, d_spos, d_sbuf, d_smeta, d_ws, st));
     MOE(moe_net_dispatch(&sh, d_soff, d_sbuf, d_smeta, d_rbuf, d_rmeta, d_roff, st));
     MOE(moe_dispatch_recv(&sh, d_counts, d_roff, d_rbuf, d_rmeta, d_ex, NULL, d_ecnt, d_eoff, d_esrc,
-                          d_erpos, d_ws, st));
+                          d_erpos, st));
     MOE(moe_expert_stub(&sh, 1, d_ex, NULL, d_eoff, d_ey, st));
     MOE(moe_combine_send(&sh, d_ey, d_erpos, d_roff, d_soff, d_cs, d_cr, st));
     MOE(moe_combine_recv(&sh, d_cr, d_spos, d_w, d_out, st));

@@ -60,8 +60,7 @@ def gpu_run(N, T, H, E, R, fp8, inp, expert_mode=0, capacity=0, y=None, topk_idx
     moe.moe_net_dispatch(b.shape, b.send_off, b.send_buf, b.send_meta, b.recv_buf, b.recv_meta,
                          b.recv_off)
     moe.moe_dispatch_recv(b.shape, b.counts, b.recv_off, b.recv_buf, b.recv_meta, b.expert_x,
-                          b.expert_scale, b.expert_cnt, b.expert_off, b.expert_src, b.expert_rpos,
-                          b.workspace)
+                          b.expert_scale, b.expert_cnt, b.expert_off, b.expert_src, b.expert_rpos)
     if y is None:
         moe.moe_expert_stub(b.shape, expert_mode, b.expert_x, b.expert_scale, b.expert_off,
                             b.expert_y)

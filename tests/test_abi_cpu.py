@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strerror():
-    assert moe.moe_abi_version() == 5
+    assert moe.moe_abi_version() == 6
     for code in (0, -1, -2, -3, -5, 42):
         assert isinstance(moe.moe_strerror(code), str)
 
@@ -111,7 +111,7 @@ def test_prefill_layout_sizes_and_guards():
         lambda: moe.moe_dispatch_send(psh, good, None, good, good, good, good, good, good, good, stream=0),
         lambda: moe.moe_net_dispatch(psh, good, good, good, good, good, good, stream=0),
         lambda: moe.moe_dispatch_recv(psh, good, good, good, good, good, None, good, good, good,
-                                      good, None, stream=0),
+                                      good, stream=0),
         lambda: moe.moe_combine(psh, good, good, good, good, good, good, good, good, good, stream=0),
         lambda: moe.moe_combine_send(psh, good, good, good, good, good, good, stream=0),
         lambda: moe.moe_combine_recv(psh, good, good, good, good, stream=0),
@@ -164,9 +164,9 @@ def test_null_and_misaligned_pointers_rejected_before_launch():
         lambda: moe.moe_dispatch_send(sh, good, None, good, good, good, good, good, good + 4, good, stream=0),
         lambda: moe.moe_net_dispatch(sh, good, good, good, bad, good, good, stream=0),
         lambda: moe.moe_dispatch_recv(sh, good, good, good, good, bad, None, good, good, good, good,
-                                      good, stream=0),
+                                      stream=0),
         lambda: moe.moe_dispatch_recv(sh, None, good, good, good, good, None, good, good, good, good,
-                                      None, stream=0),
+                                      stream=0),
         lambda: moe.moe_combine(sh, good, good, good, good, good, good, good, good, bad, stream=0),
         lambda: moe.moe_expert_stub(sh, 2, good, None, good, good, stream=0),
         lambda: moe.moe_combine_send(sh, good, good, good, good, bad, good, stream=0),
@@ -225,7 +225,7 @@ def test_product_does_not_import_oracle():
     subprocess.run([sys.executable, "-c", code], cwd=ROOT, check=True)
     for dirpath, _, files in os.walk(os.path.join(ROOT, "combine_moe_route_top_amd")):
         for f in files:
-            if f.endswith((".py", ".hip", ".cuh", ".h", ".cpp")):
+            if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
                 src = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in src.replace("oracle/", ""), f
 
@@ -237,3 +237,22 @@ def test_binding_refuses_host_tensors():
     host = torch.zeros(2 * 16 * 8, dtype=torch.float32)
     with pytest.raises(ValueError):
         moe.moe_route(sh, host, None, good, good, stream=0)
+
+
+def test_composite_calls_need_every_rank():
+    # moe_combine, moe_combine_acc and moe_prefill_combine run a second step that reads what
+    # every rank's first step wrote: a rank range is refused before any launch
+    good = 1 << 20
+    for rb, rc in [(0, 1), (1, 2), (3, 1)]:
+        dsh = moe.make_shape(4, 16, 256, 8, 2, rank_begin=rb, rank_count=rc)
+        psh = moe.make_shape(4, 16, 256, 8, 2, rank_begin=rb, rank_count=rc, prefill=True)
+        calls = [
+            lambda: moe.moe_combine(dsh, good, good, good, good, good, good, good, good, good, stream=0),
+            lambda: moe.moe_combine_acc(dsh, good, good, good, good, good, good, good, good, good, good,
+                                        good, good, stream=0),
+            lambda: moe.moe_prefill_combine(psh, good, good, good, good, good, good, stream=0),
+        ]
+        for fn in calls:
+            with pytest.raises(moe.MoeError) as ex:
+                fn()
+            assert ex.value.code == moe.MOE_EINVAL

@@ -49,7 +49,7 @@ def _device_asm(tmp_path, source):
 
 def _functions(asm):
     """(mangled name, instruction lines) of every kernel in the assembly."""
-    for name in re.findall(r"^(_ZN3moe\w+):", asm, re.M):
+    for name in re.findall(r"^\s*\.type\s+(_ZN3moe\w+),@function", asm, re.M):
         i = asm.index(name + ":")
         j = asm.index(".Lfunc_end", i)
         lines = [l.strip() for l in asm[i:j].splitlines()]

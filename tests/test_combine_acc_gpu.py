@@ -263,7 +263,7 @@ def test_acc_graph_replay_matches_eager():
                               b.send_meta, b.workspace)
         moe.moe_net_dispatch(b.shape, b.send_off, b.send_buf, b.send_meta, b.recv_buf, b.recv_meta, b.recv_off)
         moe.moe_dispatch_recv(b.shape, b.counts, b.recv_off, b.recv_buf, b.recv_meta, b.expert_x, None,
-                              b.expert_cnt, b.expert_off, b.expert_src, b.expert_rpos, b.workspace)
+                              b.expert_cnt, b.expert_off, b.expert_src, b.expert_rpos)
         moe.moe_expert_stub(b.shape, 1, b.expert_x, None, b.expert_off, b.expert_y)
         moe.run_combine_acc(b)
 

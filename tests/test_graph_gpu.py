@@ -19,8 +19,7 @@ def _layer(moe, b, use_bias, fp8):
     moe.moe_net_dispatch(b.shape, b.send_off, b.send_buf, b.send_meta, b.recv_buf, b.recv_meta,
                          b.recv_off)
     moe.moe_dispatch_recv(b.shape, b.counts, b.recv_off, b.recv_buf, b.recv_meta, b.expert_x,
-                          b.expert_scale, b.expert_cnt, b.expert_off, b.expert_src, b.expert_rpos,
-                          b.workspace)
+                          b.expert_scale, b.expert_cnt, b.expert_off, b.expert_src, b.expert_rpos)
     moe.moe_expert_stub(b.shape, 1, b.expert_x, b.expert_scale, b.expert_off, b.expert_y)
     moe.moe_combine(b.shape, b.expert_y, b.expert_rpos, b.recv_off, b.send_off, b.send_pos,
                     b.topk_w, b.cs_buf, b.cr_buf, b.out)
