@@ -30,7 +30,8 @@ if not os.path.exists(LIB_PATH):
 
 _lib = ctypes.CDLL(LIB_PATH)
 
-MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP, MOE_EBADIDX = 0, -1, -2, -3, -5
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP, MOE_EBADIDX, MOE_ENOSCRATCH = 0, -1, -2, -3, -5, -6
+MOE_STATIC_SCRATCH_BYTES = 4 << 20
 MOE_BF16, MOE_FP8_E4M3, MOE_BF16_TO_FP8 = 0, 1, 2
 MOE_LAYOUT_DECODE, MOE_LAYOUT_PREFILL = 0, 1
 
@@ -59,6 +60,7 @@ _SIGS = {
     "moe_sizes": [ctypes.POINTER(moe_shape), ctypes.POINTER(moe_sizes_t)],
     "moe_route": [ctypes.POINTER(moe_shape), _vp, _vp, _vp, _vp, _vp],
     "moe_dispatch_send": [ctypes.POINTER(moe_shape)] + [_vp] * 10,
+    "moe_dispatch_send_noalloc": [ctypes.POINTER(moe_shape)] + [_vp] * 9,
     "moe_net_dispatch": [ctypes.POINTER(moe_shape)] + [_vp] * 7,
     "moe_dispatch_recv": [ctypes.POINTER(moe_shape)] + [_vp] * 11,
     "moe_combine": [ctypes.POINTER(moe_shape)] + [_vp] * 10,
@@ -160,6 +162,13 @@ def moe_dispatch_send(shape, x, x_scale, topk_idx, counts, send_off, send_pos, s
         ctypes.byref(shape), _ptr(x), _ptr(x_scale), _ptr(topk_idx), _ptr(counts),
         _ptr(send_off), _ptr(send_pos), _ptr(send_buf), _ptr(send_meta), _ptr(workspace),
         _stream(stream)))
+
+
+def moe_dispatch_send_noalloc(shape, x, x_scale, topk_idx, counts, send_off, send_pos, send_buf,
+                              send_meta, stream=None):
+    _check("moe_dispatch_send_noalloc", _lib.moe_dispatch_send_noalloc(
+        ctypes.byref(shape), _ptr(x), _ptr(x_scale), _ptr(topk_idx), _ptr(counts), _ptr(send_off),
+        _ptr(send_pos), _ptr(send_buf), _ptr(send_meta), _stream(stream)))
 
 
 def moe_net_dispatch(shape, send_off, send_buf, send_meta, recv_buf, recv_meta, recv_off,

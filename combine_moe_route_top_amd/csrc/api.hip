@@ -9,6 +9,8 @@
 namespace moe {
 hipError_t launch_route(const Dims&, const float*, const float*, int32_t*, float*, hipStream_t);
 size_t send_workspace_bytes(const Dims&);
+size_t send_workspace_bytes_used(const Dims&);
+hipError_t scratch_address(void**);
 hipError_t launch_dispatch_send(const Dims&, const void*, const float*, const int32_t*, int32_t*,
                                 int32_t*, int32_t*, void*, int32_t*, void*, hipStream_t);
 hipError_t launch_net_dispatch(const Dims&, const int32_t*, const void*, const int32_t*, void*,
@@ -113,6 +115,7 @@ const char* moe_strerror(int status) {
         case MOE_EUNSUPPORTED: return "unsupported shape for these kernels";
         case MOE_EHIP: return "HIP launch error";
         case MOE_EBADIDX: return "expert id out of range or repeated within a token";
+        case MOE_ENOSCRATCH: return "the call needs more scratch than the library's static array holds";
         default: return "unknown status";
     }
 }
@@ -188,6 +191,26 @@ int moe_dispatch_send(const moe_shape* shape, const void* x, const float* x_scal
     if (moe::send_workspace_bytes(D) > 0 && !aligned(workspace, 4)) return MOE_EINVAL;
     return hip_status(moe::launch_dispatch_send(D, x, x_scale, topk_idx, counts, send_off, send_pos,
                                                 send_buf, send_meta, workspace, (hipStream_t)stream));
+}
+
+int moe_dispatch_send_noalloc(const moe_shape* shape, const void* x, const float* x_scale,
+                              const int32_t* topk_idx, int32_t* counts, int32_t* send_off,
+                              int32_t* send_pos, void* send_buf, int32_t* send_meta, void* stream) {
+    Dims D;
+    int rc = make_dims(shape, &D);
+    if (rc) return rc;
+    if (D.prefill) return MOE_EINVAL;  // the decode layout only
+    if (!aligned(x, 16) || !aligned(send_buf, 16) || !aligned(send_meta, 8)) return MOE_EINVAL;
+    if (D.fp8 && !D.quant && !aligned(x_scale, 16)) return MOE_EINVAL;
+    if (D.quant && x_scale) return MOE_EINVAL;  // the scales are made here
+    if (!aligned(topk_idx, 4) || !aligned(counts, 4) || !aligned(send_off, 4) || !aligned(send_pos, 4))
+        return MOE_EINVAL;
+    if (moe::send_workspace_bytes_used(D) > MOE_STATIC_SCRATCH_BYTES) return MOE_ENOSCRATCH;
+    // every histogram the kernels read is written earlier in the same call: nothing to clear
+    void* ws = nullptr;
+    if (moe::scratch_address(&ws) != hipSuccess) return MOE_EHIP;
+    return hip_status(moe::launch_dispatch_send(D, x, x_scale, topk_idx, counts, send_off, send_pos,
+                                                send_buf, send_meta, ws, (hipStream_t)stream));
 }
 
 int moe_net_dispatch(const moe_shape* shape, const int32_t* send_off, const void* send_buf,

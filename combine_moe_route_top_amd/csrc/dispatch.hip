@@ -14,6 +14,7 @@
 //  - receive buffer of rank d: the groups (s -> d) one after another by s;
 //  - expert-major tensor of rank d: by local expert j, then (source, token, slot).
 #include <algorithm>
+#include <mutex>
 
 #include "common.hpp"
 #include "slots.hpp"
@@ -457,6 +458,45 @@ size_t send_workspace_bytes(const Dims& D) {
     const int CH = send_chunk(D);
     const long C = (D.TR + CH - 1) / CH;
     return C > 1 ? (size_t)D.N * C * D.E * 4 : 0;
+}
+
+// Bytes of the workspace one call uses: the histograms of its own ranks.
+size_t send_workspace_bytes_used(const Dims& D) {
+    const int CH = send_chunk(D);
+    const long C = (D.TR + CH - 1) / CH;
+    return C > 1 ? (size_t)D.rc * C * D.E * 4 : 0;
+}
+
+// ------------------------------------------------------------------ static scratch
+
+// Device memory the library owns, for the dispatch send of callers that cannot allocate: the
+// per-chunk expert histograms ([rank][chunk][expert] int32) that k_send_hist writes and
+// k_send_rank reads, otherwise kept in the caller's workspace.  Each GPU holds its own copy at its
+// own address until the process ends.  On the host this name is a stand-in, not a device
+// address: host code passes the address scratch_address() looked up, never `scratch` itself.
+static __device__ __align__(256) int32_t scratch[MOE_STATIC_SCRATCH_BYTES / sizeof(int32_t)];
+
+constexpr int kMaxDevices = 64;
+
+// The current device's address of `scratch`, looked up once per device (with that device
+// current) and kept.
+hipError_t scratch_address(void** out) {
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_dispatch_send(const Dims& D, const void* x, const float* x_scale,

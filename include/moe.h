@@ -49,8 +49,13 @@ typedef enum {
                                token count outside [0, T] */
     MOE_EUNSUPPORTED = -2,  /* valid but outside what these kernels implement */
     MOE_EHIP = -3,          /* a HIP launch failed */
-    MOE_EBADIDX = -5        /* (device status word) bad expert id in topk_idx */
+    MOE_EBADIDX = -5,       /* (device status word) bad expert id in topk_idx */
+    MOE_ENOSCRATCH = -6     /* moe_dispatch_send_noalloc: the call needs more than the library's
+                               static scratch (MOE_STATIC_SCRATCH_BYTES) */
 } moe_status;
+
+/* Bytes of device scratch the library holds per GPU for moe_dispatch_send_noalloc. */
+#define MOE_STATIC_SCRATCH_BYTES (4u << 20)
 
 typedef enum {
     MOE_BF16 = 0,       /* dispatch payload: H bf16 values per row */
@@ -148,6 +153,21 @@ int moe_dispatch_send(const moe_shape* shape, const void* x, const float* x_scal
                       const int32_t* topk_idx, int32_t* counts, int32_t* send_off,
                       int32_t* send_pos, void* send_buf, int32_t* send_meta, void* workspace,
                       void* stream);
+
+/* moe_dispatch_send for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): no workspace argument.  The
+ * per-chunk histograms it needs when a rank's T*R slots span several chunks of 1024 (the workspace
+ * of moe_dispatch_send) live in a static device array of MOE_STATIC_SCRATCH_BYTES that the library
+ * holds on each GPU it runs on until the process ends; its address is looked up on the first call
+ * on each device.  The call allocates and frees nothing.
+ *   arguments, outputs and results as for moe_dispatch_send
+ *   MOE_ENOSCRATCH  the call's histograms (rank_count * chunks * E int32) exceed the array
+ * Every call on one GPU shares that array: calls that overlap in time on one GPU (two streams
+ * without an ordering between them) race on it and give undefined results.  Each call writes every
+ * histogram it reads before reading it, so the contents left by an earlier call do not matter. */
+int moe_dispatch_send_noalloc(const moe_shape* shape, const void* x, const float* x_scale,
+                              const int32_t* topk_idx, int32_t* counts, int32_t* send_off,
+                              int32_t* send_pos, void* send_buf, int32_t* send_meta, void* stream);
 
 /* The network stand-in.  [EFA] send-buffer paragraph: after the per-expert counts are
  * exchanged every rank knows where its writes go and where each source's tokens land, and the
