@@ -109,6 +109,7 @@ __global__ __launch_bounds__(kBlock) void k_combine_pack(Dims D, const uint16_t*
                                                          uint16_t* __restrict__ cs_buf) {
     extern __shared__ int gb[];
     __shared__ RowDesc rows[RPB];
+    __shared__ u32x4 stage[stage_len(U)];
     const int N = D.N;
     rank_bases(recv_off + (long)D.rb * (N + 1), N + 1, N, D.rc, gb);
     __syncthreads();
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(kBlock) void k_combine_pack(Dims D, const uint16_t*
         }
         if (wave_id() < RPB && lane_id() == 0) rows[wave_id()] = rd;
         __syncthreads();
-        block_stream_rows<U>(rows, RPB, D.Y16, D.Y16, D.Y16, expert_y);
+        block_stream_rows<U>(rows, RPB, D.Y16, D.Y16, D.Y16, expert_y, stage);
     };
     if constexpr (STRIDE) {
         for (long base = (long)blockIdx.x * RPB; base < total; base += (long)gridDim.x * RPB) {
@@ -153,6 +154,7 @@ __global__ __launch_bounds__(kBlock) void k_combine_net(Dims D, const uint16_t* 
                                                         uint16_t* __restrict__ cr_buf) {
     extern __shared__ int gb[];
     __shared__ RowDesc rows[RPB];
+    __shared__ u32x4 stage[stage_len(U)];
     const int N = D.N;
     rank_bases(recv_off + (long)D.rb * (N + 1), N + 1, N, D.rc, gb);
     __syncthreads();
@@ -176,7 +178,7 @@ __global__ __launch_bounds__(kBlock) void k_combine_net(Dims D, const uint16_t* 
         }
         if (wave_id() < RPB && lane_id() == 0) rows[wave_id()] = rd;
         __syncthreads();
-        block_stream_rows<U>(rows, RPB, D.Y16, D.Y16, D.Y16, cs_buf);
+        block_stream_rows<U>(rows, RPB, D.Y16, D.Y16, D.Y16, cs_buf, stage);
     };
     if constexpr (STRIDE) {
         for (long base = (long)blockIdx.x * RPB; base < total; base += (long)gridDim.x * RPB) {

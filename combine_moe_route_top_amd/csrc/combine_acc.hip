@@ -238,6 +238,7 @@ __global__ __launch_bounds__(kBlock) void k_acc_net(Dims D, const uint16_t* __re
                                                     uint16_t* __restrict__ cr_buf) {
     extern __shared__ int gb[];
     __shared__ RowDesc rows[RPB];
+    __shared__ u32x4 stage[stage_len(U)];
     const int N = D.N;
     rank_bases(recv_off + (long)D.rb * (N + 1), N + 1, N, D.rc, gb);
     __syncthreads();
@@ -265,7 +266,7 @@ __global__ __launch_bounds__(kBlock) void k_acc_net(Dims D, const uint16_t* __re
         }
         if (wave_id() < RPB && lane_id() == 0) rows[wave_id()] = rd;
         __syncthreads();
-        block_stream_rows<U>(rows, RPB, D.Y16, D.Y16, D.Y16, cs_buf);
+        block_stream_rows<U>(rows, RPB, D.Y16, D.Y16, D.Y16, cs_buf, stage);
     };
     if constexpr (STRIDE) {
         for (long base = (long)blockIdx.x * RPB; base < total; base += (long)gridDim.x * RPB) {

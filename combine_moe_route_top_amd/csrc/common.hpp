@@ -168,8 +168,7 @@ __device__ __forceinline__ void st_g(g_u32x4* p, u32x4 v) {
 
 // A row-copy kernel block (256 threads) handles RPB consecutive rows of its source: one row is
 // resolved per wave (its source and destination found), then all 256 threads stream the rows'
-// 16-byte chunks, U loads in flight per thread.  Launchers pick (RPB, U) from the row size:
-// one row per block with just enough loads per thread to cover it measured best on gfx950.
+// 16-byte chunks, U per thread per pass.  Launchers pick (RPB, U) from the row size.
 
 // A resolved row: the source is src_a (its first split_src chunks) then src_b; the destination
 // dst_a (first split_dst chunks) then dst_b.  dst_a == 0 marks "no row".
@@ -177,16 +176,39 @@ struct RowDesc {
     uint64_t src_a, src_b, dst_a, dst_b;
 };
 
+// 1: row chunks pass through LDS: each load is a gfx950 direct-to-LDS load
+// (global_load_lds_dwordx4: 16 bytes per lane from memory into LDS without a register round trip),
+// then each thread reads its own chunks back and stores them.  0 (the default): every load goes
+// into registers, then the stores.  Timed in one process on the same buffers, the LDS path made the
+// dispatch network kernel alone 13% faster on bf16 rows (4 chunks per thread, two passes) but left
+// every kernel of a whole layer within a few microseconds of the register path, so the register
+// path stays; the LDS path is kept as a build option (MOE_STREAM_LDS=1 MOE_STREAM_MAX_U=4).
+#ifndef MOE_STREAM_LDS
+#define MOE_STREAM_LDS 0
+#endif
+// Most chunks per thread per pass (the LDS path holds U * 4 KB of LDS per block).
+#ifndef MOE_STREAM_MAX_U
+#define MOE_STREAM_MAX_U 8
+#endif
+
+// LDS a streaming block declares for U chunks per thread: __shared__ u32x4 stage[stage_len(U)].
+constexpr int stage_len(int U) { return MOE_STREAM_LDS ? U * kBlock : 1; }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
 // Stream nrows resolved rows of n16 chunks each, flat over (row, chunk).  NTLD / NTST: nontemporal
 // loads / stores (the default); cached ones where the rows should stay in the memory-side cache
 // for the next kernel.  `dummy` points at n16 readable chunks (the first row of the source
 // buffer): a lane past the block's chunks, or on a row that did not resolve (dst_a == 0), loads
 // from there and stores nothing, so that every load is unconditional.  With loads under the
-// per-lane test instead, the compiler could not tell which loaded registers were still in flight
-// and waited for each load before issuing the next, leaving one 16-byte load per thread in flight.
+// per-lane test instead, the compiler could not tell which loads were still in flight and waited
+// for each load before issuing the next.  `stage`: stage_len(U) chunks of LDS.  In the LDS path
+// lane l of wave w lands chunk u of a pass at stage[u * kBlock + w * 64 + l], the slot its own
+// thread reads back, so no barrier is needed; a pass reads every chunk back before the next pass
+// loads over them.
 template <int U, bool NTLD = true, bool NTST = true>
-__device__ __forceinline__ void block_stream_rows(const RowDesc* rows, int nrows, int n16,
-                                                  int split_src, int split_dst, const void* dummy) {
+__device__ __forceinline__ void block_stream_rows(const RowDesc* rows, int nrows, int n16, int split_src,
+                                                  int split_dst, const void* dummy, u32x4* stage) {
     const int total = nrows * n16;
     const float inv = 1.0f / (float)n16;
     for (int k0 = threadIdx.x; k0 < total; k0 += blockDim.x * U) {
@@ -205,7 +227,16 @@ __device__ __forceinline__ void block_stream_rows(const RowDesc* rows, int nrows
             const g_u32x4* src = !live ? as_global(dummy) + c
                                  : c < split_src ? as_global((const void*)rows[r].src_a) + c
                                                  : as_global((const void*)rows[r].src_b) + (c - split_src);
-            v[u] = ld_g<NTLD>(src);
+            if constexpr (MOE_STREAM_LDS)
+                __builtin_amdgcn_global_load_lds((const void*)src,
+                                                 (lds_void*)(stage + u * kBlock + wave_id() * kWave), 16, 0,
+                                                 NTLD ? 2 : 0);  // 2: nontemporal
+            else
+                v[u] = ld_g<NTLD>(src);
+        }
+        if constexpr (MOE_STREAM_LDS) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) v[u] = stage[u * kBlock + threadIdx.x];
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -221,9 +252,10 @@ __device__ __forceinline__ void block_stream_rows(const RowDesc* rows, int nrows
     }
 }
 
-// (rows per block, loads per thread) for rows of n16 chunks: the fewest rows (1, 2 or 4) whose
-// chunks reach min_chunks -- enough bytes per block to hide the row-resolve latency -- and just
-// enough loads per thread for the block's 256 threads to cover them in one pass (at most 8).
+// (rows per block, chunks per thread per pass) for rows of n16 chunks: the fewest rows (1, 2 or 4)
+// whose chunks reach min_chunks -- enough bytes per block to hide the row-resolve latency -- and
+// the fewest chunks per thread (at most MOE_STREAM_MAX_U) that cover them in one pass; rows
+// longer than that take several passes.
 struct StreamShape {
     int rpb, u;
 };
@@ -232,7 +264,7 @@ inline StreamShape stream_shape(int n16, int min_chunks) {
     while (rpb < kWavesPerBlock && rpb * n16 < min_chunks) rpb *= 2;
     const int per_thread = (rpb * n16 + kBlock - 1) / kBlock;
     int u = 1;
-    while (u < per_thread && u < 8) u *= 2;
+    while (u < per_thread && u < MOE_STREAM_MAX_U) u *= 2;
     return {rpb, u};
 }
 

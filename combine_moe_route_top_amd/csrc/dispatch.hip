@@ -292,6 +292,7 @@ __global__ __launch_bounds__(kBlock) void k_net_dispatch(Dims D, const int32_t* 
                                                          int32_t* __restrict__ recv_off) {
     static_assert(RPB <= kWavesPerBlock, "one row per wave");
     __shared__ RowDesc rows[RPB];
+    __shared__ u32x4 stage[stage_len(U)];
     const int N = D.N;
     if (blockIdx.x < (unsigned)D.rc && wave_id() == kWavesPerBlock - 1) {
         const int d = D.rb + blockIdx.x;
@@ -328,7 +329,7 @@ __global__ __launch_bounds__(kBlock) void k_net_dispatch(Dims D, const int32_t* 
     }
     if (wave_id() < RPB && lane_id() == 0) rows[wave_id()] = rd;
     __syncthreads();
-    block_stream_rows<U, true, !CACHED>(rows, RPB, D.P16, D.P16, D.P16, send_buf);
+    block_stream_rows<U, true, !CACHED>(rows, RPB, D.P16, D.P16, D.P16, send_buf, stage);
 }
 
 // ------------------------------------------------------------------ receive side
@@ -369,6 +370,7 @@ __global__ __launch_bounds__(kBlock) void k_unpack(Dims D, const int32_t* __rest
                                                    int32_t* __restrict__ expert_rpos) {
     extern __shared__ int gb[];  // [rank_count + 1]
     __shared__ RowDesc rows[RPB];
+    __shared__ u32x4 stage[stage_len(U)];
     const int N = D.N, L = D.L, E = D.E;
     rank_bases(recv_off + (long)D.rb * (N + 1), N + 1, N, D.rc, gb);
     if (blockIdx.x < (unsigned)D.rc && wave_id() == kWavesPerBlock - 1) {
@@ -423,7 +425,7 @@ __global__ __launch_bounds__(kBlock) void k_unpack(Dims D, const int32_t* __rest
         }
         if (wave_id() < RPB && lane_id() == 0) rows[wave_id()] = rd;
         __syncthreads();
-        block_stream_rows<U, !CACHED, true>(rows, RPB, D.P16, D.P16, D.X16, recv_buf);
+        block_stream_rows<U, !CACHED, true>(rows, RPB, D.P16, D.P16, D.X16, recv_buf, stage);
     };
     if constexpr (STRIDE) {
         for (long base = (long)blockIdx.x * RPB; base < total; base += (long)gridDim.x * RPB) {

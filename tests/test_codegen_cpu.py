@@ -90,3 +90,32 @@ def test_row_copy_loads_stay_in_flight(tmp_path, source):
                     serial.append(name)
     assert checked > 0, "no 16-byte loads found in the row-copy kernels"
     assert not serial, f"loads issued after a full wait in {sorted(set(serial))[:4]}"
+
+
+def test_lds_staged_stream_build_uses_direct_to_lds_loads(tmp_path):
+    # the build option MOE_STREAM_LDS=1 stages row chunks through LDS with gfx950 direct-to-LDS
+    # 16-byte loads in every row-copy kernel, spills nothing, and reads each chunk back only after
+    # a wait for the loads (the compiler orders the LDS read after the direct load)
+    b = _hipcc()
+    flags = [f for f in b.FLAGS if f not in ("-fPIC", "-shared")]
+    out = os.path.join(str(tmp_path), "dispatch_lds.s")
+    cmd = [b.HIPCC, *flags, "-DMOE_STREAM_LDS=1", "-DMOE_STREAM_MAX_U=4", "--offload-device-only", "-S",
+           "-Rpass-analysis=kernel-resource-usage", "-I", os.path.join(ROOT, "include"),
+           os.path.join(CSRC, "dispatch.hip"), "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    asm = open(out).read()
+    sizes = [int(x) for x in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", r.stderr)]
+    assert sizes and max(sizes) == 0
+    seen = 0
+    for name, lines in _functions(asm):
+        if not re.search(r"k_net_dispatch|k_unpack", name):
+            continue
+        assert not any(re.match(r"(global|flat|buffer)_load_dwordx4", l) for l in lines), name
+        loads = [k for k, l in enumerate(lines) if l.startswith("global_load_lds_dwordx4")]
+        reads = [k for k, l in enumerate(lines) if l.startswith("ds_read_b128")]
+        assert loads and reads, name
+        first_read = reads[0]
+        assert any(re.match(r"s_waitcnt vmcnt\(0\)", l) for l in lines[loads[0]:first_read]), name
+        seen += 1
+    assert seen > 0
