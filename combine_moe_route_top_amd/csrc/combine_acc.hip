@@ -24,13 +24,16 @@ namespace moe {
 __device__ __forceinline__ int meta_token(int2 m, int TR, int R) { return (m.x % TR) / R; }
 
 // Launch constants, overridable at build time for experiments: the partial kernel's blocks at most
-// (blocks step over the receive rows), and the chunks the network kernel's blocks aim for (several
-// rows per block: many rows move nothing).
+// (blocks step over the receive rows), and the receive rows the network kernel's blocks resolve
+// (several per block: many rows move nothing).
 #ifndef MOE_ACC_PARTIAL_BLOCKS
 #define MOE_ACC_PARTIAL_BLOCKS 1048576
 #endif
-#ifndef MOE_ACC_NET_MIN_CHUNKS
-#define MOE_ACC_NET_MIN_CHUNKS 1792
+// Four rows per block (same-process A/B of 2, 4, 8 and 16, and of 512-thread blocks): Kimi-K2's
+// combine send 402 -> 381 us; DeepSeek-V3's, where nine in ten rows hold a partial and four rows
+// take two streaming passes, 329 -> 338 us.
+#ifndef MOE_ACC_NET_ROWS
+#define MOE_ACC_NET_ROWS 4
 #endif
 
 // What a block needs to form one partial: where it goes, how many rows, their expert-major
@@ -229,64 +232,112 @@ __global__ __launch_bounds__(kBlock) void k_acc_partial(Dims D, const uint16_t* 
 
 // Network back for the partials: as the receive-side combine's network step (row r of segment
 // (s -> d) to send_off[s][d] + (r - recv_off[d][s]) in rank s's combine receive buffer), but a
-// row moves only if it is its token's first row at d.  STRIDE: blocks stride over a capped grid.
-template <int RPB, int U, bool STRIDE>
-__global__ __launch_bounds__(kBlock) void k_acc_net(Dims D, const uint16_t* __restrict__ cs_buf,
+// row moves only if it is its token's first row at d.  W receive rows per block (a global index
+// over the call's ranks) are resolved by wave 0, one per lane; the rows that hold a partial are
+// gathered at the front of the block's row list (a ballot) and only they are streamed, so the
+// rows that move nothing (most of them where a token's rows crowd onto one rank) cost a resolve
+// lane, not a block.  STRIDE: blocks stride over a capped grid.
+// Threads per block of the partial network kernel (512 let four rows stream in one pass but lost
+// the Kimi-K2 gain: 406 us).
+#ifndef MOE_ACC_NET_THREADS
+#define MOE_ACC_NET_THREADS 256
+#endif
+template <int W, int U, bool STRIDE>
+__global__ __launch_bounds__(MOE_ACC_NET_THREADS) void k_acc_net(Dims D, const uint16_t* __restrict__ cs_buf,
                                                     const int32_t* __restrict__ recv_meta,
                                                     const int32_t* __restrict__ recv_off,
                                                     const int32_t* __restrict__ send_off,
                                                     uint16_t* __restrict__ cr_buf) {
-    extern __shared__ int gb[];
-    __shared__ RowDesc rows[RPB];
-    __shared__ u32x4 stage[stage_len(U)];
+    static_assert(W <= kWave, "one row per lane of wave 0");
+    extern __shared__ int lds_an[];  // gb[rank_count + 1], then ro[N + 1] of the block's first rank
+    __shared__ RowDesc rows[W];
+    __shared__ u32x4 stage[stage_len(U, MOE_ACC_NET_THREADS)];
+    __shared__ int nlive;
     const int N = D.N;
+    int* gb = lds_an;
+    int* sro = lds_an + D.rc + 1;
     rank_bases(recv_off + (long)D.rb * (N + 1), N + 1, N, D.rc, gb);
     __syncthreads();
     const long total = gb[D.rc];
     auto pass = [&](long base) {
-        const long G = base + wave_id();
-        RowDesc rd = {0, 0, 0, 0};
-        if (wave_id() < RPB && G < total) {
-            const int dl = wave_count_le(gb + 1, D.rc, G);
-            const int d = D.rb + dl;
-            const long r = G - gb[dl];
-            const int32_t* ro = recv_off + (long)d * (N + 1);
-            const int s = wave_count_le(ro, N, r) - 1;
-            const long i = s >= 0 ? send_off[(long)s * (N + 1) + d] + (r - ro[s]) : -1;
-            if (i >= 0 && i < D.TR) {
-                const int2* meta = reinterpret_cast<const int2*>(recv_meta) + (size_t)d * D.B;
-                const bool first = r == ro[s] || meta_token(meta[r - 1], D.TR, D.R) != meta_token(meta[r], D.TR, D.R);
-                if (first) {
-                    rd.src_a = rd.src_b = (uint64_t)(cs_buf + ((size_t)d * D.B + r) * D.H);
-                    rd.dst_a = rd.dst_b = (uint64_t)(cr_buf + ((size_t)s * D.TR + i) * D.H);
+        if (wave_id() == 0) {
+            const int lane = lane_id();
+            const long G = base + lane;
+            const bool in = lane < W && G < total;
+            // rank of each row: gb[lo] <= G < gb[lo + 1]
+            int lo = 0;
+            if (in) {
+                int hi = D.rc;
+                while (hi - lo > 1) {
+                    const int mid = (lo + hi) >> 1;
+                    if (gb[mid] <= G) lo = mid;
+                    else hi = mid;
                 }
-            } else {
-                set_status(D.status, MOE_EINVAL);
             }
+            // the receive offsets of the rank of the block's first row, staged in LDS
+            const int l0 = readlane(lo, 0);
+            const int32_t* ro0 = recv_off + (long)(D.rb + l0) * (N + 1);
+            for (int k = lane; k <= N; k += kWave) sro[k] = ro0[k];
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            RowDesc rd = {0, 0, 0, 0};
+            bool live = false;
+            if (in) {
+                const int d = D.rb + lo;
+                const long r = G - gb[lo];  // < recv_off[d][N]
+                const int32_t* ro = recv_off + (long)d * (N + 1);
+                const bool staged = lo == l0;
+                // source: ro[s] <= r < ro[s + 1]
+                int s = 0, hi = N;
+                while (hi - s > 1) {
+                    const int mid = (s + hi) >> 1;
+                    if ((staged ? sro[mid] : ro[mid]) <= r) s = mid;
+                    else hi = mid;
+                }
+                const long seg0 = staged ? sro[s] : ro[s];
+                const long i = send_off[(long)s * (N + 1) + d] + (r - seg0);
+                if (i >= 0 && i < D.TR && r < D.B) {
+                    const int2* meta = reinterpret_cast<const int2*>(recv_meta) + (size_t)d * D.B;
+                    live = r == seg0 || meta_token(meta[r - 1], D.TR, D.R) != meta_token(meta[r], D.TR, D.R);
+                    if (live) {
+                        rd.src_a = rd.src_b = (uint64_t)(cs_buf + ((size_t)d * D.B + r) * D.H);
+                        rd.dst_a = rd.dst_b = (uint64_t)(cr_buf + ((size_t)s * D.TR + i) * D.H);
+                    }
+                } else {
+                    set_status(D.status, MOE_EINVAL);
+                }
+            }
+            const uint64_t m = ballot(live);
+            if (live) rows[__popcll(m & lanemask_lt())] = rd;
+            if (lane == 0) nlive = __popcll(m);
         }
-        if (wave_id() < RPB && lane_id() == 0) rows[wave_id()] = rd;
         __syncthreads();
-        block_stream_rows<U>(rows, RPB, D.Y16, D.Y16, D.Y16, cs_buf, stage);
+        block_stream_rows<U>(rows, nlive, D.Y16, D.Y16, D.Y16, cs_buf, stage);
     };
     if constexpr (STRIDE) {
-        for (long base = (long)blockIdx.x * RPB; base < total; base += (long)gridDim.x * RPB) {
+        for (long base = (long)blockIdx.x * W; base < total; base += (long)gridDim.x * W) {
             pass(base);
-            if (base + (long)gridDim.x * RPB < total) __syncthreads();  // rows[] is rewritten
+            if (base + (long)gridDim.x * W < total) __syncthreads();  // rows[], nlive, sro are rewritten
         }
     } else {
-        pass((long)blockIdx.x * RPB);
+        pass((long)blockIdx.x * W);
     }
 }
 
 // The source's sum: out[s][t] = bf16(fp32 sum of the token's partials in the order of their first
 // slots).  Slot k holds a partial if it is valid and no earlier valid slot of the token has the
-// same owner rank (one ballot per owner bit finds the lower lanes with the same owner).  WW waves
-// per token and CU chunks per lane, chosen as in the receive-side weighted sum.  Every slot of
-// the unrolled group adds: a skipped slot adds a zero chunk (exact, as the sums start at +0.0 and
-// so are never -0.0), and a lane past the row's end reads the row's last chunk and drops it.
-// With the loads and the adds both under the slot test, the generated code waited for each load
-// before issuing the next.
-template <int CU>
+// same owner rank (one ballot per owner bit finds the lower lanes with the same owner).  The
+// partial slots (a ballot, in slot order) are taken GP at a time: every load of a group is issued
+// before its adds, a group's unused entries add a zero chunk (exact: the sums start at +0.0 and so
+// are never -0.0), and a lane past the row's end reads the row's last chunk and drops it.  WW waves
+// per token and CU chunks per lane, chosen as in the receive-side weighted sum; walking only the
+// partials (about three of a Kimi-K2 token's eight slots) instead of every slot holds GP * CU
+// chunks per lane instead of 8 * CU: 133 instead of 220 registers in the four-chunk shape, and
+// Kimi-K2's sum 111 -> 81 us (groups of 8: 102 us).
+#ifndef MOE_ACC_SUM_GROUP
+#define MOE_ACC_SUM_GROUP 4
+#endif
+template <int CU, int GP>
 __global__ __launch_bounds__(kBlock) void k_acc_sum(Dims D, int WW, const uint16_t* __restrict__ cr_buf,
                                                     const int32_t* __restrict__ send_pos,
                                                     const int32_t* __restrict__ topk_idx,
@@ -303,7 +354,8 @@ __global__ __launch_bounds__(kBlock) void k_acc_sum(Dims D, int WW, const uint16
     const bool valid = pos >= 0 && pos < D.TR;
     const int owner = valid ? topk_idx[tok * R + lane] / D.L : 0;
     const uint64_t same = same_key_lanes(valid, owner, key_bits(D.N));
-    const int my_pos = valid && (same & lanemask_lt()) == 0 ? pos : -1;
+    const uint64_t pm = ballot(valid && (same & lanemask_lt()) == 0);  // slots holding a partial
+    const int np = __popcll(pm);
     const u32x4* rank_rows = reinterpret_cast<const u32x4*>(cr_buf + (size_t)s * D.TR * D.H);
     u32x4* orow = reinterpret_cast<u32x4*>(out + (size_t)tok * D.H);
     const int n16 = D.Y16;
@@ -313,29 +365,30 @@ __global__ __launch_bounds__(kBlock) void k_acc_sum(Dims D, int WW, const uint16
         for (int cu = 0; cu < CU; ++cu)
 #pragma unroll
             for (int u = 0; u < 8; ++u) acc[cu][u] = 0.0f;
-        for (int k0 = 0; k0 < R; k0 += 8) {
-            u32x4 v[CU][8];
-            bool ok[8];
+        uint64_t m = pm;
+        for (int j0 = 0; j0 < np; j0 += GP) {
+            u32x4 v[CU][GP];
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
-                const int k = k0 + kk;
-                const int pr = readlane(my_pos, k);  // k < 64 as R <= 64
-                const int p = k < R ? pr : -1;
-                ok[kk] = p >= 0;
+            for (int jj = 0; jj < GP; ++jj) {
+                int p = -1;
+                if (m) {
+                    p = readlane(pos, (int)__builtin_ctzll(m));
+                    m &= m - 1;
+                }
 #pragma unroll
                 for (int cu = 0; cu < CU; ++cu) {
                     const int c = min(c0 + cu * kWave * WW, n16 - 1);
-                    v[cu][kk] = u32x4{0u, 0u, 0u, 0u};
-                    if (ok[kk]) v[cu][kk] = ld_nt(rank_rows + (size_t)p * n16 + c);
+                    v[cu][jj] = u32x4{0u, 0u, 0u, 0u};
+                    if (p >= 0) v[cu][jj] = ld_nt(rank_rows + (size_t)p * n16 + c);
                 }
             }
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
+            for (int jj = 0; jj < GP; ++jj) {
 #pragma unroll
                 for (int cu = 0; cu < CU; ++cu)
 #pragma unroll
                     for (int u = 0; u < 8; ++u)
-                        acc[cu][u] += bf16_to_f32((v[cu][kk][u >> 1] >> (16 * (u & 1))) & 0xFFFF);
+                        acc[cu][u] += bf16_to_f32((v[cu][jj][u >> 1] >> (16 * (u & 1))) & 0xFFFF);
             }
         }
 #pragma unroll
@@ -373,16 +426,21 @@ hipError_t launch_combine_acc_send(const Dims& D, const uint16_t* expert_y, cons
     const long blocks = std::min<long>(MOE_ACC_PARTIAL_BLOCKS, row_blocks(D, rows, kWavesPerBlock));
     hipLaunchKernelGGL(k_acc_partial, dim3((unsigned)blocks), dim3(kBlock), (D.rc + 1) * 4, st, D, expert_y,
                        recv_meta, counts, recv_off, expert_off, topk_w, cs_buf);
-    const StreamShape sn = stream_shape(D.Y16, MOE_ACC_NET_MIN_CHUNKS);
-#define MOE_LAUNCH_S(R_, U_, S_)                                                                     \
-    hipLaunchKernelGGL((k_acc_net<R_, U_, S_>), dim3(row_blocks(D, rows, R_)), dim3(kBlock), (D.rc + 1) * 4, \
-                       st, D, (const uint16_t*)cs_buf, recv_meta, recv_off, send_off, cr_buf);
-#define MOE_LAUNCH(R_, U_)                                                                          \
-    if (sn.rpb == R_ && sn.u == U_) {                                                               \
-        if (row_blocks(D, rows, R_) * R_ < rows) MOE_LAUNCH_S(R_, U_, true)                         \
-        else MOE_LAUNCH_S(R_, U_, false)                                                            \
+    // W receive rows per block, at most 8 chunks per thread per pass
+    const int u = (int)std::min<long>(8, std::max<long>(1, (long)D.Y16 * MOE_ACC_NET_ROWS / MOE_ACC_NET_THREADS));
+    const int u2 = u <= 1 ? 1 : u <= 2 ? 2 : u <= 4 ? 4 : 8;
+    const long nb = row_blocks(D, rows, MOE_ACC_NET_ROWS);
+    const bool stride = nb * MOE_ACC_NET_ROWS < rows;
+    const size_t lds = (size_t)(D.rc + 1 + D.N + 1) * 4;
+#define MOE_LAUNCH_S(U_, S_)                                                                         \
+    hipLaunchKernelGGL((k_acc_net<MOE_ACC_NET_ROWS, U_, S_>), dim3(nb), dim3(MOE_ACC_NET_THREADS), lds, st, D, \
+                       (const uint16_t*)cs_buf, recv_meta, recv_off, send_off, cr_buf);
+#define MOE_LAUNCH(U_)                                                                              \
+    if (u2 == U_) {                                                                                 \
+        if (stride) MOE_LAUNCH_S(U_, true)                                                          \
+        else MOE_LAUNCH_S(U_, false)                                                                \
     }
-    MOE_STREAM_SHAPES(MOE_LAUNCH)
+    MOE_LAUNCH(1) MOE_LAUNCH(2) MOE_LAUNCH(4) MOE_LAUNCH(8)
 #undef MOE_LAUNCH
 #undef MOE_LAUNCH_S
     return hipGetLastError();
@@ -400,12 +458,12 @@ hipError_t launch_combine_acc_recv(const Dims& D, const uint16_t* cr_buf, const 
     const int ww4 = acc_waves(D, 4, 4);
     if (ntok * ww4 >= MOE_ACC_SUM_WIDE_MIN_WAVES) {
         const long waves = ntok * ww4;
-        hipLaunchKernelGGL(k_acc_sum<4>, dim3((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock)),
+        hipLaunchKernelGGL((k_acc_sum<4, MOE_ACC_SUM_GROUP>), dim3((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock)),
                            dim3(kBlock), 0, st, D, ww4, cr_buf, send_pos, topk_idx, out);
     } else {
         const int ww1 = acc_waves(D, 1, 16);
         const long waves = ntok * ww1;
-        hipLaunchKernelGGL(k_acc_sum<1>, dim3((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock)),
+        hipLaunchKernelGGL((k_acc_sum<1, MOE_ACC_SUM_GROUP>), dim3((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock)),
                            dim3(kBlock), 0, st, D, ww1, cr_buf, send_pos, topk_idx, out);
     }
     return hipGetLastError();

@@ -191,8 +191,9 @@ struct RowDesc {
 #define MOE_STREAM_MAX_U 8
 #endif
 
-// LDS a streaming block declares for U chunks per thread: __shared__ u32x4 stage[stage_len(U)].
-constexpr int stage_len(int U) { return MOE_STREAM_LDS ? U * kBlock : 1; }
+// LDS a streaming block of `threads` threads declares for U chunks per thread:
+// __shared__ u32x4 stage[stage_len(U, threads)].
+constexpr int stage_len(int U, int threads = kBlock) { return MOE_STREAM_LDS ? U * threads : 1; }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -202,10 +203,10 @@ typedef __attribute__((address_space(3))) void lds_void;
 // buffer): a lane past the block's chunks, or on a row that did not resolve (dst_a == 0), loads
 // from there and stores nothing, so that every load is unconditional.  With loads under the
 // per-lane test instead, the compiler could not tell which loads were still in flight and waited
-// for each load before issuing the next.  `stage`: stage_len(U) chunks of LDS.  In the LDS path
-// lane l of wave w lands chunk u of a pass at stage[u * kBlock + w * 64 + l], the slot its own
-// thread reads back, so no barrier is needed; a pass reads every chunk back before the next pass
-// loads over them.
+// for each load before issuing the next.  `stage`: stage_len(U, blockDim.x) chunks of LDS.  In the
+// LDS path lane l of wave w lands chunk u of a pass at stage[u * blockDim.x + w * 64 + l], the slot
+// its own thread reads back, so no barrier is needed; a pass reads every chunk back before the next
+// pass loads over them.
 template <int U, bool NTLD = true, bool NTST = true>
 __device__ __forceinline__ void block_stream_rows(const RowDesc* rows, int nrows, int n16, int split_src,
                                                   int split_dst, const void* dummy, u32x4* stage) {
@@ -229,14 +230,14 @@ __device__ __forceinline__ void block_stream_rows(const RowDesc* rows, int nrows
                                                  : as_global((const void*)rows[r].src_b) + (c - split_src);
             if constexpr (MOE_STREAM_LDS)
                 __builtin_amdgcn_global_load_lds((const void*)src,
-                                                 (lds_void*)(stage + u * kBlock + wave_id() * kWave), 16, 0,
+                                                 (lds_void*)(stage + u * blockDim.x + wave_id() * kWave), 16, 0,
                                                  NTLD ? 2 : 0);  // 2: nontemporal
             else
                 v[u] = ld_g<NTLD>(src);
         }
         if constexpr (MOE_STREAM_LDS) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) v[u] = stage[u * kBlock + threadIdx.x];
+            for (int u = 0; u < U; ++u) v[u] = stage[u * blockDim.x + threadIdx.x];
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
