@@ -74,6 +74,7 @@ _SIGS = {
     "moe_prefill_combine_local": [ctypes.POINTER(moe_shape)] + [_vp] * 6,
     "moe_prefill_allreduce": [ctypes.POINTER(moe_shape)] + [_vp] * 3,
     "moe_prefill_combine": [ctypes.POINTER(moe_shape)] + [_vp] * 7,
+    "moe_stream_copy": [_vp, _vp, ctypes.c_int64, _vp],
     "moe_strerror": [ctypes.c_int],
     "moe_abi_version": [],
 }
@@ -101,6 +102,10 @@ def moe_strerror(code: int) -> str:
 
 def moe_abi_version() -> int:
     return int(_lib.moe_abi_version())
+
+
+def moe_stream_copy(src, dst, nbytes, stream=None):
+    _check("moe_stream_copy", _lib.moe_stream_copy(_ptr(src), _ptr(dst), int(nbytes), _stream(stream)))
 
 
 def _ptr(t):

@@ -35,6 +35,7 @@ hipError_t launch_prefill_dispatch(const Dims&, const void*, const float*, const
 hipError_t launch_prefill_local(const Dims&, const uint16_t*, const int32_t*, const int32_t*, const float*,
                                 float*, hipStream_t);
 hipError_t launch_prefill_allreduce(const Dims&, const float*, uint16_t*, hipStream_t);
+hipError_t launch_stream_copy(const void*, void*, long, hipStream_t);
 }  // namespace moe
 
 using moe::Dims;
@@ -107,6 +108,15 @@ int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 extern "C" {
 
 int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+int moe_stream_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+    if (bytes < 0 || bytes % 16 != 0 || bytes / 16 > (int64_t)1 << 40) return MOE_EINVAL;
+    if (bytes == 0) return MOE_OK;
+    if (!aligned(src, 16) || !aligned(dst, 16)) return MOE_EINVAL;
+    const uintptr_t s = reinterpret_cast<uintptr_t>(src), d = reinterpret_cast<uintptr_t>(dst);
+    if (s < d + (uintptr_t)bytes && d < s + (uintptr_t)bytes) return MOE_EINVAL;  // overlapping
+    return hip_status(moe::launch_stream_copy(src, dst, (long)bytes, (hipStream_t)stream));
+}
 
 const char* moe_strerror(int status) {
     switch (status) {

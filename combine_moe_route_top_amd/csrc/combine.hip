@@ -272,6 +272,39 @@ __global__ __launch_bounds__(kBlock) void k_wsum(Dims D, int WW, const uint16_t*
     }
 }
 
+// ------------------------------------------------------------------ copy ceiling
+
+// A contiguous copy through the row-streaming engine: the buffer cut into rows of 256 * U chunks,
+// one row per block, U chunks per thread in one pass, nontemporal loads and stores.  Not a step of
+// the path: the same engine on the simplest row map, the practical ceiling the row-copy kernels are
+// measured against.
+template <int U>
+__global__ __launch_bounds__(kBlock) void k_stream_copy(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                                        long n16) {
+    __shared__ RowDesc rows[1];
+    __shared__ u32x4 stage[stage_len(U)];
+    constexpr int ch = kBlock * U;
+    const long c0 = (long)blockIdx.x * ch;
+    const int n = (int)(n16 - c0 < ch ? n16 - c0 : ch);
+    if (threadIdx.x == 0) {
+        rows[0].src_a = rows[0].src_b = (uint64_t)(src + c0 * 16);
+        rows[0].dst_a = rows[0].dst_b = (uint64_t)(dst + c0 * 16);
+    }
+    __syncthreads();
+    // dummy: the block's own source row (n chunks), which every lane may read
+    block_stream_rows<U>(rows, 1, n, n, n, src + c0 * 16, stage);
+}
+
+hipError_t launch_stream_copy(const void* src, void* dst, long bytes, hipStream_t st) {
+    const long n16 = bytes / 16;
+    constexpr int U = MOE_STREAM_MAX_U;
+    const long blocks = (n16 + kBlock * U - 1) / (kBlock * U);
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL((k_stream_copy<U>), dim3(blocks), dim3(kBlock), 0, st, (const uint8_t*)src, (uint8_t*)dst,
+                       n16);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ launchers
 
 hipError_t launch_expert_stub(const Dims& D, int mode, const void* expert_x, const float* expert_scale,

@@ -330,6 +330,13 @@ const char* moe_strerror(int status);
 /* MOE_ABI_VERSION of the loaded library. */
 int moe_abi_version(void);
 
+/* A measurement aid, not a step of the path: copies `bytes` (a multiple of 16) from src to dst
+ * (device pointers, 16-byte aligned, not overlapping) with the row-streaming engine the copy
+ * kernels use, on the simplest row map (contiguous rows of 256 threads' chunks, one per block,
+ * nontemporal), so its rate is the practical copy ceiling the row-copy kernels are measured
+ * against.  Returns MOE_EINVAL for a bad size, alignment or overlap. */
+int moe_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

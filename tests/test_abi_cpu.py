@@ -256,3 +256,16 @@ def test_composite_calls_need_every_rank():
             with pytest.raises(moe.MoeError) as ex:
                 fn()
             assert ex.value.code == moe.MOE_EINVAL
+
+
+def test_stream_copy_rejects_bad_arguments():
+    good = 1 << 20
+    for src, dst, n in [(good, good + (1 << 22), 24),      # not a multiple of 16
+                        (good + 4, good + (1 << 22), 64),  # misaligned source
+                        (good, good + 32, 64),             # overlapping
+                        (good, good, 16),                  # the same buffer
+                        (good, good + (1 << 22), -16)]:
+        with pytest.raises(moe.MoeError) as ex:
+            moe.moe_stream_copy(src, dst, n, stream=0)
+        assert ex.value.code == moe.MOE_EINVAL
+    moe.moe_stream_copy(good, good + 64, 0, stream=0)  # nothing to copy: no launch

@@ -475,3 +475,16 @@ def test_full_workload(name):
     print(" ", st, flush=True)
     if name == "kimi_k2_worst":
         assert g["recv_off"][0, c.N] == 49152
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096 * 16 + 16, (1 << 24) + 48])
+def test_stream_copy_is_exact(nbytes):
+    # the copy-ceiling probe: whole blocks and a ragged last block, byte for byte
+    import combine_moe_route_top_amd as moe
+    print(f"\ncase stream copy {nbytes} bytes", flush=True)
+    src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda")
+    dst = torch.full((nbytes + 64,), 0xA5, dtype=torch.uint8, device="cuda")
+    moe.moe_stream_copy(src, dst, nbytes)
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:nbytes], src)
+    assert bool((dst[nbytes:] == 0xA5).all())
