@@ -492,11 +492,43 @@ def copy_calibration(nbytes=1 << 30, reps=10) -> dict:
     return out
 
 
-def overlap_leg(name, steps=10, warmup=2, inter=2048) -> dict:
+def cu_masked_stream(n_cus: int):
+    """A HIP stream (default priority) whose kernels run only on the first n_cus compute units
+    (hipExtStreamCreateWithCUMask), wrapped for torch; returns (handle, torch stream)."""
+    import ctypes
+
+    import torch
+    hip = ctypes.CDLL("libamdhip64.so.7")   # the runtime torch has loaded (same SONAME)
+    total = torch.cuda.get_device_properties(0).multi_processor_count
+    words = (total + 31) // 32
+    mask = (ctypes.c_uint32 * words)()
+    for i in range(min(n_cus, total)):
+        mask[i // 32] |= 1 << (i % 32)
+    handle = ctypes.c_void_p()
+    hip.hipExtStreamCreateWithCUMask.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint32,
+                                                ctypes.POINTER(ctypes.c_uint32)]
+    rc = hip.hipExtStreamCreateWithCUMask(ctypes.byref(handle), words, mask)
+    if rc != 0:
+        raise RuntimeError(f"hipExtStreamCreateWithCUMask failed: {rc}")
+    return handle.value, torch.cuda.ExternalStream(handle.value)
+
+
+def destroy_stream(handle):
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    hip.hipStreamDestroy.argtypes = [ctypes.c_void_p]
+    hip.hipStreamDestroy(handle)
+
+
+def overlap_leg(name, steps=10, warmup=2, inter=2048, cu_splits=(256, 224, 192, 160, 128)) -> dict:
     """Send/receive split in use: a stand-in shared expert (one MLP, hidden H -> inter -> H, bf16
     GEMMs through torch) runs on a second stream while (a) the dispatch transfer (network
     stand-in + receive) and (b) the combine send half run on the first.  Reports serial and
-    overlapped time and the part of the shared expert hidden behind the transfer."""
+    overlapped time and the part of the shared expert hidden behind the transfer.  On one GPU the
+    copy stand-ins are themselves CU kernels that fill the chip, so the transfer's stream is
+    restricted to a subset of the compute units (a CU-masked stream, swept over cu_splits of the
+    GPU's units; 'all' is the unmasked stream), standing in for a transfer that leaves CUs free;
+    the shared expert's stream is never masked.  Serial references run on the same masked stream."""
     import numpy as np
     import torch
     import torch.nn.functional as F
@@ -519,73 +551,109 @@ def overlap_leg(name, steps=10, warmup=2, inter=2048) -> dict:
     wd = (torch.randn(inter, c.H, device="cuda", generator=gen) * inter ** -0.5).to(torch.bfloat16)
     xs = b.x.view(torch.bfloat16).view(c.N * c.T, c.H)
     ys = torch.empty_like(xs)
-    s1 = torch.cuda.current_stream()
-    s2 = torch.cuda.Stream()   # default priority
+    s2 = torch.cuda.Stream()   # default priority, all compute units
     sh = b.shape
+    total_cus = torch.cuda.get_device_properties(0).multi_processor_count
 
     def shared(st):
         with torch.cuda.stream(st):
             torch.matmul(F.silu(xs @ wg) * (xs @ wu), wd, out=ys)
 
-    def d_send():
-        moe.moe_route(sh, b.logits, b.bias if use_bias else None, b.topk_idx, b.topk_w, s1)
-        moe.moe_dispatch_send(sh, b.x, b.x_scale, b.topk_idx, b.counts, b.send_off, b.send_pos,
-                              b.send_buf, b.send_meta, b.workspace, s1)
+    def measure(s1):
+        def d_send():
+            moe.moe_route(sh, b.logits, b.bias if use_bias else None, b.topk_idx, b.topk_w, s1)
+            moe.moe_dispatch_send(sh, b.x, b.x_scale, b.topk_idx, b.counts, b.send_off, b.send_pos,
+                                  b.send_buf, b.send_meta, b.workspace, s1)
 
-    def d_transfer():
-        moe.moe_net_dispatch(sh, b.send_off, b.send_buf, b.send_meta, b.recv_buf, b.recv_meta,
-                             b.recv_off, s1)
-        moe.moe_dispatch_recv(sh, b.counts, b.recv_off, b.recv_buf, b.recv_meta, b.expert_x,
-                              b.expert_scale, b.expert_cnt, b.expert_off, b.expert_src,
-                              b.expert_rpos, s1)
+        def d_transfer():
+            moe.moe_net_dispatch(sh, b.send_off, b.send_buf, b.send_meta, b.recv_buf, b.recv_meta,
+                                 b.recv_off, s1)
+            moe.moe_dispatch_recv(sh, b.counts, b.recv_off, b.recv_buf, b.recv_meta, b.expert_x,
+                                  b.expert_scale, b.expert_cnt, b.expert_off, b.expert_src,
+                                  b.expert_rpos, s1)
 
-    def c_send():
-        moe.moe_combine_send(sh, b.expert_x, b.expert_rpos, b.recv_off, b.send_off, b.cs_buf,
-                             b.cr_buf, s1)
+        def c_send():
+            moe.moe_combine_send(sh, b.expert_x, b.expert_rpos, b.recv_off, b.send_off, b.cs_buf,
+                                 b.cr_buf, s1)
 
-    def c_recv():
-        moe.moe_combine_recv(sh, b.cr_buf, b.send_pos, b.topk_w, b.out, s1)
+        def c_recv():
+            moe.moe_combine_recv(sh, b.cr_buf, b.send_pos, b.topk_w, b.out, s1)
 
-    def fork_join(first, second):
-        """first() on s1, then the shared expert on s2 concurrently with second() on s1."""
-        first()
-        ev = torch.cuda.Event()
-        ev.record(s1)
-        s2.wait_event(ev)
-        shared(s2)
-        second()
-        s1.wait_stream(s2)
+        def fork_join(first, second):
+            """first() on s1, then the shared expert on s2 concurrently with second() on s1."""
+            first()
+            ev = torch.cuda.Event()
+            ev.record(s1)
+            s2.wait_event(ev)
+            shared(s2)
+            second()
+            s1.wait_stream(s2)
 
-    # dispatch: the shared expert runs while the transfer (network + receive) is in flight;
-    # combine: while the combine send half (shuffle + network back) is, before the weighted sum
-    variants = {
-        "shared_alone": lambda: shared(s1),
-        "dispatch_alone": lambda: (d_send(), d_transfer()),
-        "dispatch_then_shared": lambda: (d_send(), d_transfer(), shared(s1)),
-        "dispatch_overlap": lambda: fork_join(d_send, d_transfer),
-        "combine_alone": lambda: (c_send(), c_recv()),
-        "combine_then_shared": lambda: (c_send(), shared(s1), c_recv()),
-        "combine_overlap": lambda: (fork_join(lambda: None, c_send), c_recv()),
-    }
-    us = {}
-    for k, fn in variants.items():
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(s1)
-        for _ in range(steps):
-            fn()
-        e1.record(s1)
-        torch.cuda.synchronize()
-        us[k] = round(e0.elapsed_time(e1) * 1e3 / steps, 2)
+        def serial(*fns):
+            for fn in fns:
+                fn()
+            shared(s1)
+
+        # dispatch: the shared expert runs while the transfer (network + receive) is in flight;
+        # combine: while the combine send half (shuffle + network back) is, before the weighted sum
+        variants = {
+            "shared_alone": lambda: shared(s1),
+            "dispatch_alone": lambda: (d_send(), d_transfer()),
+            "dispatch_then_shared": lambda: serial(d_send, d_transfer),
+            "dispatch_overlap": lambda: fork_join(d_send, d_transfer),
+            "combine_alone": lambda: (c_send(), c_recv()),
+            "combine_then_shared": lambda: (c_send(), shared(s1), c_recv()),
+            "combine_overlap": lambda: (fork_join(lambda: None, c_send), c_recv()),
+        }
+        us = {}
+        for k, fn in variants.items():
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s1)
+            for _ in range(steps):
+                fn()
+            e1.record(s1)
+            torch.cuda.synchronize()
+            us[k] = round(e0.elapsed_time(e1) * 1e3 / steps, 2)
+        out = {"us": us}
+        for ph in ("dispatch", "combine"):
+            hidden = us[f"{ph}_then_shared"] - us[f"{ph}_overlap"]
+            out[f"{ph}_hidden_us"] = round(hidden, 2)
+            out[f"{ph}_hidden_frac_of_shared"] = round(hidden / us["shared_alone"], 3)
+        return out
+
     res = {"workload": name, "shared_expert": f"bf16 MLP {c.H}->{inter}->{c.H} on {c.N * c.T} tokens "
-                                               f"(torch GEMMs on a second stream)", "us": us}
-    for ph in ("dispatch", "combine"):
-        serial = us[f"{ph}_then_shared"]
-        hidden = serial - us[f"{ph}_overlap"]
-        res[f"{ph}_hidden_us"] = round(hidden, 2)
-        res[f"{ph}_hidden_frac_of_shared"] = round(hidden / us["shared_alone"], 3)
+                                               f"(torch GEMMs on a second stream)",
+           "total_cus": total_cus}
+    res.update(measure(torch.cuda.current_stream()))
+    sweep = {}
+    for n in cu_splits:
+        if n >= total_cus:
+            continue
+        handle, sm = cu_masked_stream(n)
+        try:
+            r = measure(sm)
+        finally:
+            torch.cuda.synchronize()
+            destroy_stream(handle)
+        base = res["us"]
+        r["dispatch_overlap_vs_unmasked_serial_us"] = round(base["dispatch_then_shared"] - r["us"]["dispatch_overlap"], 2)
+        r["combine_overlap_vs_unmasked_serial_us"] = round(base["combine_then_shared"] - r["us"]["combine_overlap"], 2)
+        sweep[f"{n}_cus"] = r
+    res["cu_masked_transfer"] = sweep
+    if sweep:
+        # the split that saves the most against everything run serially on all compute units
+        best = max(sweep.items(), key=lambda kv: kv[1]["dispatch_overlap_vs_unmasked_serial_us"] +
+                   kv[1]["combine_overlap_vs_unmasked_serial_us"])
+        res["best_cu_split"] = {"transfer_cus": int(best[0].split("_")[0]),
+                                "dispatch_saved_us": best[1]["dispatch_overlap_vs_unmasked_serial_us"],
+                                "combine_saved_us": best[1]["combine_overlap_vs_unmasked_serial_us"],
+                                "transfer_alone_us": best[1]["us"]["dispatch_alone"],
+                                "transfer_alone_unmasked_us": res["us"]["dispatch_alone"]}
+    if int(b.status.item()) != 0:
+        raise RuntimeError("device status word set in the overlap leg")
     del b
     torch.cuda.empty_cache()
     return res
