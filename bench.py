@@ -412,7 +412,12 @@ def dominant_kernel(res) -> dict:
 
 
 def cpu_baseline(name, budget_s=20.0) -> dict:
-    """The oracle, as it stands, on one full layer of the workload on the host cores."""
+    """The oracle, as it stands, on one full layer of the workload on the host cores: the
+    single-threaded calls (the baseline), and beside it the same oracle functions with each step's
+    ranks split into one chunk per available core, run on that many threads (each chunk is one C
+    call of the oracle's rank-range form; the steps run one after another)."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
 
     import moe_synth as ms
@@ -421,13 +426,12 @@ def cpu_baseline(name, budget_s=20.0) -> dict:
     inp = ms.config_inputs(c)
     tok = ms.config_tokens(c)
     ab = alg_bytes(c)
-    times = []
-    t_start = time.perf_counter()
-    while True:
-        t0 = time.perf_counter()
+
+    def layer_single():
         x, xs = inp["x"], inp["x_scale"]
         if c.quant:
             x, xs = oracle.quantize_e4m3(x)
+        t0 = time.perf_counter()
         sh = oracle.shape(c.N, c.T, c.H, c.E, c.R, c.rows_fp8, tokens=tok)
         idx, w = oracle.route(inp["logits"], inp["bias"], c.R)
         r = oracle.dispatch_send(sh, x, xs, idx.reshape(c.N, -1))
@@ -438,13 +442,49 @@ def cpu_baseline(name, budget_s=20.0) -> dict:
         t1 = time.perf_counter()
         y = oracle.expert(sh, 0, r["expert_x"], r["expert_scale"], r["expert_off"])
         t2 = time.perf_counter()
-        oracle.combine(sh, 0, y, r["expert_rpos"], r["recv_off"], r["send_off"], r["send_pos"], w)
+        out = oracle.combine(sh, 0, y, r["expert_rpos"], r["recv_off"], r["send_off"], r["send_pos"], w)
         t3 = time.perf_counter()
-        times.append((t1 - t0) + (t3 - t2))
+        return (t1 - t0) + (t3 - t2), y, out["out"]
+
+    def layer_threaded(pool, parts, y):
+        x, xs = inp["x"], inp["x_scale"]
+        if c.quant:
+            x, xs = oracle.quantize_e4m3(x)
+        t0 = time.perf_counter()
+        sh = oracle.shape(c.N, c.T, c.H, c.E, c.R, c.rows_fp8, tokens=tok)
+        idx, w = oracle.route_chunked(inp["logits"], inp["bias"], c.R, pool, parts)
+        r = oracle.dispatch_send_chunked(sh, x, xs, idx.reshape(c.N, -1), pool, parts)
+        sh = oracle.packed_shape(c.N, c.T, c.H, c.E, c.R, c.rows_fp8,
+                                 np.diff(r["send_off"], axis=1).sum(axis=0), tok)
+        r.update(oracle.net_dispatch_chunked(sh, r["send_off"], r["send_buf"], r["send_meta"], pool, parts))
+        r.update(oracle.dispatch_recv_chunked(sh, r["counts"], r["recv_off"], r["recv_buf"], r["recv_meta"],
+                                              pool, parts))
+        # (the stand-in expert's output y is the single run's; it is not part of the timing)
+        out = oracle.combine_chunked(sh, 0, y, r["expert_rpos"], r["recv_off"], r["send_off"], r["send_pos"],
+                                     w, pool, parts)
+        return time.perf_counter() - t0, out["out"]
+
+    times, t_start = [], time.perf_counter()
+    y = out1 = None
+    while True:
+        t, y, out1 = layer_single()
+        times.append(t)
         # about budget_s/2 .. budget_s of host work: at least 3 layers, at most 20
         if len(times) >= 20 or (len(times) >= 3 and time.perf_counter() - t_start > budget_s * 0.5):
             break
-    t = float(np.median(times))
+    t1core = float(np.median(times))
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    ttimes, outn = [], None
+    with ThreadPoolExecutor(max_workers=cores) as pool:
+        t_start = time.perf_counter()
+        while True:
+            t, outn = layer_threaded(pool, cores, y)
+            ttimes.append(t)
+            if len(ttimes) >= 20 or (len(ttimes) >= 3 and time.perf_counter() - t_start > budget_s * 0.25):
+                break
+    if not np.array_equal(outn, out1):
+        raise RuntimeError("threaded oracle output differs from the single-threaded oracle")
+    tn = float(np.median(ttimes))
     model = ""
     try:
         for line in open("/proc/cpuinfo"):
@@ -453,12 +493,17 @@ def cpu_baseline(name, budget_s=20.0) -> dict:
                 break
     except OSError:
         pass
-    return {"value": round(ab["total"] / t / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "host_cpus": os.cpu_count(), "cpu_model": model,
-            "us_per_layer": round(t * 1e6, 1),
+    return {"value": round(ab["total"] / t1core / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "host_cpus": os.cpu_count(), "cpu_share": cores, "cpu_model": model,
+            "us_per_layer": round(t1core * 1e6, 1),
             "sample": f"one full {name} layer (all {c.N} ranks) through the single-threaded C oracle "
                       f"(route, dispatch, network, unpack, combine; stand-in expert excluded), "
-                      f"median of {len(times)}"}
+                      f"median of {len(times)}",
+            "threaded": {"value": round(ab["total"] / tn / 1e9, 3), "unit": "GB/s", "cores": cores,
+                         "us_per_layer": round(tn * 1e6, 1), "speedup": round(t1core / tn, 2),
+                         "sample": f"the same layer with each step's ranks split into {cores} chunks on "
+                                   f"{cores} threads, median of {len(ttimes)}; output equal to the "
+                                   f"single-threaded run"}}
 
 
 def copy_calibration(nbytes=1 << 30, reps=10) -> dict:

@@ -310,3 +310,111 @@ def run_all(sh: Shape, inp: dict, expert_mode: int = 0, combine_mode: int = 0,
     res.update(combine(sh, combine_mode, res["expert_y"], res["expert_rpos"], res["recv_off"],
                        res["send_off"], res["send_pos"], w))
     return res
+
+
+# ------------------------------------------------------------------ the steps over rank chunks
+
+def rank_chunks(n: int, parts: int):
+    """[r0, r1) ranges splitting 0..n into at most `parts` contiguous, non-empty chunks."""
+    parts = max(1, min(int(parts), n))
+    b = [n * i // parts for i in range(parts + 1)]
+    return [(b[i], b[i + 1]) for i in range(parts) if b[i] < b[i + 1]]
+
+
+def _over_chunks(pool, fn, n, parts):
+    """fn(r0, r1) for every chunk, on the pool's threads (each call is one C call, during which
+    ctypes releases the interpreter lock), all finished before returning."""
+    chunks = rank_chunks(n, parts)
+    if pool is None or len(chunks) == 1:
+        for r0, r1 in chunks:
+            fn(r0, r1)
+        return
+    for f in [pool.submit(fn, r0, r1) for r0, r1 in chunks]:
+        f.result()
+
+
+def route_chunked(logits, bias, R, pool, parts):
+    """route() with the tokens split into chunks; the same outputs."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    n, E = logits.shape
+    idx = np.empty((n, R), np.int32)
+    w = np.empty((n, R), np.float32)
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    _over_chunks(pool, lambda t0, t1: lib().oracle_route_tokens(
+        ctypes.c_int(t0), ctypes.c_int(t1), ctypes.c_int(E), ctypes.c_int(R), _p(logits), _p(b),
+        _p(idx), _p(w)), n, parts)
+    return idx, w
+
+
+def dispatch_send_chunked(sh: Shape, x, x_scale, topk_idx, pool, parts):
+    N, T, E, R = sh.N, sh.T, sh.E, sh.R
+    P = row_bytes(sh)
+    x = np.ascontiguousarray(x)
+    xs = None if not sh.fp8 else np.ascontiguousarray(x_scale, dtype=np.float32)
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    counts = np.empty((N, E), np.int32)
+    send_off = np.empty((N, N + 1), np.int32)
+    send_pos = np.full((N, T * R), -1, np.int32)
+    send_buf = np.zeros((N, T * R, P), np.uint8)
+    send_meta = np.zeros((N, T * R, 2), np.int32)
+    _over_chunks(pool, lambda r0, r1: lib().oracle_dispatch_send_ranks(
+        ctypes.byref(sh), ctypes.c_int(r0), ctypes.c_int(r1), _p(x), _p(xs), _p(idx), _p(counts),
+        _p(send_off), _p(send_pos), _p(send_buf), _p(send_meta)), N, parts)
+    return dict(counts=counts, send_off=send_off, send_pos=send_pos, send_buf=send_buf,
+                send_meta=send_meta)
+
+
+def net_dispatch_chunked(sh: Shape, send_off, send_buf, send_meta, pool, parts):
+    N = sh.N
+    P = row_bytes(sh)
+    recv_buf = np.zeros(sh.lead() + (P,), np.uint8)
+    recv_meta = np.zeros(sh.lead() + (2,), np.int32)
+    recv_off = np.empty((N, N + 1), np.int32)
+    _over_chunks(pool, lambda r0, r1: lib().oracle_net_dispatch_ranks(
+        ctypes.byref(sh), ctypes.c_int(r0), ctypes.c_int(r1), _p(send_off), _p(send_buf),
+        _p(send_meta), _p(recv_buf), _p(recv_meta), _p(recv_off)), N, parts)
+    return dict(recv_buf=recv_buf, recv_meta=recv_meta, recv_off=recv_off)
+
+
+def dispatch_recv_chunked(sh: Shape, counts, recv_off, recv_buf, recv_meta, pool, parts):
+    N, H = sh.N, sh.H
+    L = sh.E // N
+    lead = sh.lead()
+    if sh.fp8:
+        expert_x = np.zeros(lead + (H,), np.uint8)
+        expert_scale = np.zeros(lead + (H // 128,), np.float32)
+    else:
+        expert_x = np.zeros(lead + (H,), np.uint16)
+        expert_scale = None
+    expert_cnt = np.empty((N, L), np.int32)
+    expert_off = np.empty((N, L + 1), np.int32)
+    expert_src = np.full(lead, -1, np.int32)
+    expert_rpos = np.full(lead, -1, np.int32)
+    _over_chunks(pool, lambda r0, r1: lib().oracle_dispatch_recv_ranks(
+        ctypes.byref(sh), ctypes.c_int(r0), ctypes.c_int(r1), _p(counts), _p(recv_off),
+        _p(recv_buf), _p(recv_meta), _p(expert_x), _p(expert_scale), _p(expert_cnt),
+        _p(expert_off), _p(expert_src), _p(expert_rpos)), N, parts)
+    return dict(expert_x=expert_x, expert_scale=expert_scale, expert_cnt=expert_cnt,
+                expert_off=expert_off, expert_src=expert_src, expert_rpos=expert_rpos)
+
+
+def combine_chunked(sh: Shape, mode: int, expert_y, expert_rpos, recv_off, send_off, send_pos,
+                    topk_w, pool, parts):
+    """combine() as its three steps, each over rank chunks: the shuffle (by destination), the
+    network back (by source), the weighted sum (by source)."""
+    N, H, T, R = sh.N, sh.H, sh.T, sh.R
+    cs = np.zeros(sh.lead() + (H,), np.uint16)
+    cr = np.zeros((N, T * R, H), np.uint16)
+    out = np.zeros((N, T, H), np.uint16)
+    w = np.ascontiguousarray(topk_w, dtype=np.float32)
+    y = np.ascontiguousarray(expert_y, np.uint16)
+    _over_chunks(pool, lambda r0, r1: lib().oracle_combine_pack_ranks(
+        ctypes.byref(sh), ctypes.c_int(r0), ctypes.c_int(r1), _p(y), _p(expert_rpos),
+        _p(recv_off), _p(cs)), N, parts)
+    _over_chunks(pool, lambda r0, r1: lib().oracle_combine_net_ranks(
+        ctypes.byref(sh), ctypes.c_int(r0), ctypes.c_int(r1), _p(recv_off), _p(send_off), _p(cs),
+        _p(cr)), N, parts)
+    _over_chunks(pool, lambda r0, r1: lib().oracle_combine_sum_ranks(
+        ctypes.byref(sh), ctypes.c_int(r0), ctypes.c_int(r1), ctypes.c_int(mode), _p(send_pos),
+        _p(w), _p(cr), _p(out)), N, parts)
+    return dict(cs_buf=cs, cr_buf=cr, out=out)

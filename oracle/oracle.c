@@ -147,13 +147,13 @@ void oracle_quantize_e4m3(long n_rows, int H, const uint16_t* x, uint8_t* q, flo
  * tracking the indices of the sorted elements.  [PORT] introduction: weights come from the
  * router's probability distribution and the output is a weighted average.
  * Selection: R passes, each taking the best unselected expert under (v desc, e asc). */
-void oracle_route(int n_tokens, int E, int R, const float* logits, const float* bias,
-                  int32_t* topk_idx, float* topk_w) {
-    assert(E >= 1 && R >= 1 && R <= E);
+void oracle_route_tokens(int t0, int t1, int E, int R, const float* logits, const float* bias,
+                         int32_t* topk_idx, float* topk_w) {
+    assert(E >= 1 && R >= 1 && R <= E && 0 <= t0 && t0 <= t1);
     float* v = (float*)malloc(sizeof(float) * E);
     char* taken = (char*)malloc(E);
     double* z = (double*)malloc(sizeof(double) * R);
-    for (int n = 0; n < n_tokens; ++n) {
+    for (int n = t0; n < t1; ++n) {
         for (int e = 0; e < E; ++e) {
             float l = logits[(long)n * E + e];
             assert(isfinite(l));
@@ -183,6 +183,11 @@ void oracle_route(int n_tokens, int E, int R, const float* logits, const float* 
     free(z);
 }
 
+void oracle_route(int n_tokens, int E, int R, const float* logits, const float* bias,
+                  int32_t* topk_idx, float* topk_w) {
+    oracle_route_tokens(0, n_tokens, E, R, logits, bias, topk_idx, topk_w);
+}
+
 /* ---------------------------------------------------------------- dispatch */
 
 /* [EFA] dispatch timing paragraph: the send kernel counts tokens per expert, takes a cumulative
@@ -191,11 +196,12 @@ void oracle_route(int n_tokens, int E, int R, const float* logits, const float* 
  * [PORT] Dispatch: activations, block scales and the token's index travel together.
  * Row metadata: meta[0] = e*T*R + t*R + k (expert and source slot), meta[1] = how many earlier
  * slots of the same source chose the same expert. */
-void oracle_dispatch_send(const oracle_shape* sh, const uint8_t* x, const float* x_scale,
-                          const int32_t* topk_idx, int32_t* counts, int32_t* send_off,
-                          int32_t* send_pos, uint8_t* send_buf, int32_t* send_meta) {
+void oracle_dispatch_send_ranks(const oracle_shape* sh, int r0, int r1, const uint8_t* x,
+                                const float* x_scale, const int32_t* topk_idx, int32_t* counts,
+                                int32_t* send_off, int32_t* send_pos, uint8_t* send_buf,
+                                int32_t* send_meta) {
     const int N = sh->N, T = sh->T, H = sh->H, E = sh->E, R = sh->R;
-    assert(N >= 1 && E % N == 0);
+    assert(N >= 1 && E % N == 0 && 0 <= r0 && r0 <= r1 && r1 <= N);
     const int L = E / N;
     const long P = oracle_row_bytes(sh);
     const long TR = (long)T * R;
@@ -203,7 +209,7 @@ void oracle_dispatch_send(const oracle_shape* sh, const uint8_t* x, const float*
     const int nsc = H / 128;               /* fp8 block scales per token */
     int32_t* fill = (int32_t*)malloc(sizeof(int32_t) * N);
     int32_t* seen = (int32_t*)malloc(sizeof(int32_t) * E);
-    for (int s = 0; s < N; ++s) {
+    for (int s = r0; s < r1; ++s) {
         const int32_t* idx = topk_idx + s * TR;
         int32_t* cnt = counts + (long)s * E;
         int32_t* off = send_off + (long)s * (N + 1);
@@ -250,16 +256,24 @@ void oracle_dispatch_send(const oracle_shape* sh, const uint8_t* x, const float*
     free(seen);
 }
 
+void oracle_dispatch_send(const oracle_shape* sh, const uint8_t* x, const float* x_scale,
+                          const int32_t* topk_idx, int32_t* counts, int32_t* send_off,
+                          int32_t* send_pos, uint8_t* send_buf, int32_t* send_meta) {
+    oracle_dispatch_send_ranks(sh, 0, sh->N, x, x_scale, topk_idx, counts, send_off, send_pos,
+                               send_buf, send_meta);
+}
+
 /* [EFA] send-buffer paragraph: once the per-expert counts are exchanged every rank knows where
  * its writes land and at which offset each source's tokens arrive; the bulk then moves as one
  * write per peer.  recv_off[d][s] = sum over s' < s of what s' sends to d. */
-void oracle_net_dispatch(const oracle_shape* sh, const int32_t* send_off, const uint8_t* send_buf,
-                         const int32_t* send_meta, uint8_t* recv_buf, int32_t* recv_meta,
-                         int32_t* recv_off) {
+void oracle_net_dispatch_ranks(const oracle_shape* sh, int r0, int r1, const int32_t* send_off,
+                               const uint8_t* send_buf, const int32_t* send_meta, uint8_t* recv_buf,
+                               int32_t* recv_meta, int32_t* recv_off) {
     const int N = sh->N;
     const long P = oracle_row_bytes(sh);
     const long TR = (long)sh->T * sh->R;
-    for (int d = 0; d < N; ++d) {
+    assert(0 <= r0 && r0 <= r1 && r1 <= N);
+    for (int d = r0; d < r1; ++d) {
         int32_t* roff = recv_off + (long)d * (N + 1);
         roff[0] = 0;
         for (int s = 0; s < N; ++s) {
@@ -267,35 +281,42 @@ void oracle_net_dispatch(const oracle_shape* sh, const int32_t* send_off, const 
             roff[s + 1] = roff[s] + (soff[d + 1] - soff[d]);
         }
         assert(roff[N] <= rcap(sh, d));
-    }
-    for (int s = 0; s < N; ++s) {
-        const int32_t* soff = send_off + (long)s * (N + 1);
-        for (int d = 0; d < N; ++d) {
+        for (int s = 0; s < N; ++s) {
+            const int32_t* soff = send_off + (long)s * (N + 1);
             long n = soff[d + 1] - soff[d];
             long src = (long)s * TR + soff[d];
-            long dst = rrow0(sh, d) + recv_off[(long)d * (N + 1) + s];
+            long dst = rrow0(sh, d) + roff[s];
             memcpy(recv_buf + dst * P, send_buf + src * P, n * P);
             memcpy(recv_meta + 2 * dst, send_meta + 2 * src, 8 * n);
         }
     }
 }
 
+void oracle_net_dispatch(const oracle_shape* sh, const int32_t* send_off, const uint8_t* send_buf,
+                         const int32_t* send_meta, uint8_t* recv_buf, int32_t* recv_meta,
+                         int32_t* recv_off) {
+    oracle_net_dispatch_ranks(sh, 0, sh->N, send_off, send_buf, send_meta, recv_buf, recv_meta,
+                              recv_off);
+}
+
 /* [PORT] Dispatch: the receiver copies tokens into contiguous buffers that feed the grouped
  * GEMM, grouping tokens of one expert together, and stores source rank, expert index and token
  * index for combine.  Expert-major order: walking the receive rows in order and appending each
  * to its local expert's group keeps (source, token, slot) order inside the group. */
-void oracle_dispatch_recv(const oracle_shape* sh, const int32_t* counts, const int32_t* recv_off,
-                          const uint8_t* recv_buf, const int32_t* recv_meta, uint8_t* expert_x,
-                          float* expert_scale, int32_t* expert_cnt, int32_t* expert_off,
-                          int32_t* expert_src, int32_t* expert_rpos) {
+void oracle_dispatch_recv_ranks(const oracle_shape* sh, int r0, int r1, const int32_t* counts,
+                                const int32_t* recv_off, const uint8_t* recv_buf,
+                                const int32_t* recv_meta, uint8_t* expert_x, float* expert_scale,
+                                int32_t* expert_cnt, int32_t* expert_off, int32_t* expert_src,
+                                int32_t* expert_rpos) {
     const int N = sh->N, H = sh->H, E = sh->E;
+    assert(0 <= r0 && r0 <= r1 && r1 <= N);
     const int L = E / N;
     const long P = oracle_row_bytes(sh);
     const long TR = (long)sh->T * sh->R;
     const long xrow = sh->fp8 ? H : 2L * H;
     const int nsc = H / 128;
     int32_t* fill = (int32_t*)malloc(sizeof(int32_t) * L);
-    for (int d = 0; d < N; ++d) {
+    for (int d = r0; d < r1; ++d) {
         int32_t* ecnt = expert_cnt + (long)d * L;
         int32_t* eoff = expert_off + (long)d * (L + 1);
         const int32_t* roff = recv_off + (long)d * (N + 1);
@@ -327,6 +348,14 @@ void oracle_dispatch_recv(const oracle_shape* sh, const int32_t* counts, const i
         }
     }
     free(fill);
+}
+
+void oracle_dispatch_recv(const oracle_shape* sh, const int32_t* counts, const int32_t* recv_off,
+                          const uint8_t* recv_buf, const int32_t* recv_meta, uint8_t* expert_x,
+                          float* expert_scale, int32_t* expert_cnt, int32_t* expert_off,
+                          int32_t* expert_src, int32_t* expert_rpos) {
+    oracle_dispatch_recv_ranks(sh, 0, sh->N, counts, recv_off, recv_buf, recv_meta, expert_x,
+                               expert_scale, expert_cnt, expert_off, expert_src, expert_rpos);
 }
 
 /* Stand-in for the grouped GEMM ([EFA] dispatch/combine overview: the grouped GEMM multiplies
@@ -370,22 +399,28 @@ void oracle_expert(const oracle_shape* sh, int mode, const uint8_t* expert_x,
  * weighted average of all expert contributions locally.
  * cs[d] is rank d's combine send buffer in its receive order; cr[s] is rank s's combine receive
  * buffer laid out like its dispatch send buffer. */
-void oracle_combine(const oracle_shape* sh, int mode, const uint16_t* expert_y,
-                    const int32_t* expert_rpos, const int32_t* recv_off, const int32_t* send_off,
-                    const int32_t* send_pos, const float* topk_w, uint16_t* cs_buf, uint16_t* cr_buf,
-                    uint16_t* out) {
-    const int N = sh->N, T = sh->T, H = sh->H, R = sh->R;
-    const long TR = (long)T * R;
-    /* shuffle: expert-major row q goes back to receive position rpos[q] */
-    for (int d = 0; d < N; ++d) {
+/* shuffle of ranks d in [r0, r1): expert-major row q goes back to receive position rpos[q] */
+void oracle_combine_pack_ranks(const oracle_shape* sh, int r0, int r1, const uint16_t* expert_y,
+                               const int32_t* expert_rpos, const int32_t* recv_off, uint16_t* cs_buf) {
+    const int N = sh->N, H = sh->H;
+    assert(0 <= r0 && r0 <= r1 && r1 <= N);
+    for (int d = r0; d < r1; ++d) {
         long total = recv_off[(long)d * (N + 1) + N];
         for (long q = 0; q < total; ++q) {
             long r = expert_rpos[rrow0(sh, d) + q];
             memcpy(cs_buf + (rrow0(sh, d) + r) * H, expert_y + (rrow0(sh, d) + q) * H, 2L * H);
         }
     }
-    /* network back: segment (d -> s) lands where s's dispatch segment for d sat */
-    for (int s = 0; s < N; ++s) {
+}
+
+/* network back to ranks s in [r0, r1): segment (d -> s) lands where s's dispatch segment for d
+ * sat */
+void oracle_combine_net_ranks(const oracle_shape* sh, int r0, int r1, const int32_t* recv_off,
+                              const int32_t* send_off, const uint16_t* cs_buf, uint16_t* cr_buf) {
+    const int N = sh->N, H = sh->H;
+    const long TR = (long)sh->T * sh->R;
+    assert(0 <= r0 && r0 <= r1 && r1 <= N);
+    for (int s = r0; s < r1; ++s) {
         const int32_t* soff = send_off + (long)s * (N + 1);
         for (int d = 0; d < N; ++d) {
             long n = soff[d + 1] - soff[d];
@@ -394,8 +429,16 @@ void oracle_combine(const oracle_shape* sh, int mode, const uint16_t* expert_y,
             memcpy(cr_buf + dst * H, cs_buf + src * H, 2L * n * H);
         }
     }
-    /* weighted sum over the token's R slots */
-    for (int s = 0; s < N; ++s) {
+}
+
+/* weighted sum over the token's R slots, for the tokens of ranks s in [r0, r1) */
+void oracle_combine_sum_ranks(const oracle_shape* sh, int r0, int r1, int mode, const int32_t* send_pos,
+                              const float* topk_w, const uint16_t* cr_buf, uint16_t* out) {
+    const int N = sh->N, T = sh->T, H = sh->H, R = sh->R;
+    const long TR = (long)T * R;
+    assert(0 <= r0 && r0 <= r1 && r1 <= N);
+    (void)N;
+    for (int s = r0; s < r1; ++s) {
         for (int t = 0; t < ntok(sh, s); ++t) {
             const long base = (long)s * TR + (long)t * R;
             for (int h = 0; h < H; ++h) {
@@ -413,6 +456,15 @@ void oracle_combine(const oracle_shape* sh, int mode, const uint16_t* expert_y,
             }
         }
     }
+}
+
+void oracle_combine(const oracle_shape* sh, int mode, const uint16_t* expert_y,
+                    const int32_t* expert_rpos, const int32_t* recv_off, const int32_t* send_off,
+                    const int32_t* send_pos, const float* topk_w, uint16_t* cs_buf, uint16_t* cr_buf,
+                    uint16_t* out) {
+    oracle_combine_pack_ranks(sh, 0, sh->N, expert_y, expert_rpos, recv_off, cs_buf);
+    oracle_combine_net_ranks(sh, 0, sh->N, recv_off, send_off, cs_buf, cr_buf);
+    oracle_combine_sum_ranks(sh, 0, sh->N, mode, send_pos, topk_w, cr_buf, out);
 }
 
 /* Combine with the sum taken on the sending side ([EFA] results for the EP64 prefill latency

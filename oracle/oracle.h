@@ -121,4 +121,33 @@ void oracle_prefill_combine(const oracle_shape* sh, int mode, const uint16_t* ex
                             const int32_t* slot_pos, const int32_t* topk_idx, const float* topk_w,
                             float* partial, uint16_t* out);
 
+
+/* Rank-range (token-range) forms of the steps above: the same loops restricted to the ranks
+ * [r0, r1) (route: tokens [t0, t1)); arrays stay full-size and global-indexed.  Ranges of one step
+ * touch disjoint outputs, so several may run at once on different threads; a step may start only
+ * once every range of the step before it has finished.  The network step handles destinations
+ * (each computes its receive offsets and copies its N incoming segments); the combine splits into
+ * the shuffle (by destination), the network back (by source) and the weighted sum (by source).
+ * The single calls above are these over the full range. */
+void oracle_route_tokens(int t0, int t1, int E, int R, const float* logits, const float* bias,
+                         int32_t* topk_idx, float* topk_w);
+void oracle_dispatch_send_ranks(const oracle_shape* sh, int r0, int r1, const uint8_t* x,
+                                const float* x_scale, const int32_t* topk_idx, int32_t* counts,
+                                int32_t* send_off, int32_t* send_pos, uint8_t* send_buf,
+                                int32_t* send_meta);
+void oracle_net_dispatch_ranks(const oracle_shape* sh, int r0, int r1, const int32_t* send_off,
+                               const uint8_t* send_buf, const int32_t* send_meta, uint8_t* recv_buf,
+                               int32_t* recv_meta, int32_t* recv_off);
+void oracle_dispatch_recv_ranks(const oracle_shape* sh, int r0, int r1, const int32_t* counts,
+                                const int32_t* recv_off, const uint8_t* recv_buf,
+                                const int32_t* recv_meta, uint8_t* expert_x, float* expert_scale,
+                                int32_t* expert_cnt, int32_t* expert_off, int32_t* expert_src,
+                                int32_t* expert_rpos);
+void oracle_combine_pack_ranks(const oracle_shape* sh, int r0, int r1, const uint16_t* expert_y,
+                               const int32_t* expert_rpos, const int32_t* recv_off, uint16_t* cs_buf);
+void oracle_combine_net_ranks(const oracle_shape* sh, int r0, int r1, const int32_t* recv_off,
+                              const int32_t* send_off, const uint16_t* cs_buf, uint16_t* cr_buf);
+void oracle_combine_sum_ranks(const oracle_shape* sh, int r0, int r1, int mode, const int32_t* send_pos,
+                              const float* topk_w, const uint16_t* cr_buf, uint16_t* out);
+
 #endif
