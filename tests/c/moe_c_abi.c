@@ -106,6 +106,73 @@ static void host_checks(void) {
     CHECK(sz.capacity == 128 * 8 && sz.partial == 32LL * 128 * 7168 * 4, "prefill sizes");
     CHECK(moe_abi_version() == MOE_ABI_VERSION, "abi version %d", moe_abi_version());
     CHECK(moe_route(NULL, NULL, NULL, NULL, NULL, NULL) == MOE_EINVAL, "null shape accepted");
+    /* the no-allocation send refuses, before any device work, a call whose histograms exceed the
+     * library's static array (1024 ranks and experts, 1600 slots per rank) */
+    void* good = (void*)(uintptr_t)(1 << 20);
+    memset(&sh, 0, sizeof sh);
+    sh.N = 1024; sh.T = 200; sh.H = 64; sh.E = 1024; sh.R = 8; sh.dtype = MOE_BF16;
+    MOE(moe_sizes(&sh, &sz));
+    CHECK(sz.workspace > (int64_t)MOE_STATIC_SCRATCH_BYTES, "workspace %lld", (long long)sz.workspace);
+    CHECK(moe_dispatch_send_noalloc(&sh, good, NULL, good, good, good, good, good, good, NULL) == MOE_ENOSCRATCH,
+          "oversized no-allocation send accepted");
+    CHECK(moe_stream_copy(good, (char*)good + 32, 64, NULL) == MOE_EINVAL, "overlapping copy accepted");
+    CHECK(moe_stream_copy(good, (char*)good + 4096, 24, NULL) == MOE_EINVAL, "ragged copy accepted");
+}
+
+/* ---------------------------------------------------------------- no-allocation send, stream copy */
+
+/* moe_dispatch_send_noalloc on a shape whose ranks span several count chunks (the static
+ * histograms in use), against the oracle's dispatch send; then moe_stream_copy of its send buffer */
+static void noalloc_and_copy(void) {
+    const int N = 2, T = 700, H = 64, E = 32, R = 8;
+    moe_shape sh;
+    memset(&sh, 0, sizeof sh);
+    sh.N = N; sh.T = T; sh.H = H; sh.E = E; sh.R = R; sh.dtype = MOE_BF16;
+    moe_sizes_t sz;
+    MOE(moe_sizes(&sh, &sz));
+    CHECK(sz.workspace > 0, "this shape should need histograms");
+    const int64_t P = sz.row_bytes, TR = (int64_t)T * R;
+    float* logits = halloc(sz.logits);
+    uint16_t* x = halloc(sz.x);
+    for (int64_t i = 0; i < (int64_t)N * T * E; ++i) logits[i] = rnd_uniform(-3.0f, 3.0f);
+    for (int64_t i = 0; i < (int64_t)N * T * H; ++i) x[i] = bf16_trunc(rnd_uniform(-2.0f, 2.0f));
+    int32_t* status = dalloc(4);
+    HIP(hipMemset(status, 0, 4));
+    sh.status = status;
+    void *d_logits = dalloc(sz.logits), *d_x = dalloc(sz.x), *d_idx = dalloc(sz.topk_idx), *d_w = dalloc(sz.topk_w),
+         *d_counts = dalloc(sz.counts), *d_soff = dalloc(sz.send_off), *d_spos = dalloc(sz.send_pos),
+         *d_sbuf = dalloc(sz.send_buf), *d_smeta = dalloc(sz.send_meta), *d_copy = dalloc(sz.send_buf);
+    h2d(d_logits, logits, sz.logits);
+    h2d(d_x, x, sz.x);
+    MOE(moe_route(&sh, d_logits, NULL, d_idx, d_w, NULL));
+    MOE(moe_dispatch_send_noalloc(&sh, d_x, NULL, d_idx, d_counts, d_soff, d_spos, d_sbuf, d_smeta, NULL));
+    MOE(moe_stream_copy(d_sbuf, d_copy, sz.send_buf, NULL));
+    HIP(hipDeviceSynchronize());
+    int32_t* g_idx = halloc(sz.topk_idx); int32_t* g_counts = halloc(sz.counts);
+    int32_t* g_soff = halloc(sz.send_off); int32_t* g_spos = halloc(sz.send_pos);
+    uint8_t* g_sbuf = halloc(sz.send_buf); int32_t* g_smeta = halloc(sz.send_meta);
+    uint8_t* g_copy = halloc(sz.send_buf);
+    int32_t g_status = -99;
+    d2h(g_idx, d_idx, sz.topk_idx); d2h(g_counts, d_counts, sz.counts); d2h(g_soff, d_soff, sz.send_off);
+    d2h(g_spos, d_spos, sz.send_pos); d2h(g_sbuf, d_sbuf, sz.send_buf); d2h(g_smeta, d_smeta, sz.send_meta);
+    d2h(g_copy, d_copy, sz.send_buf); d2h(&g_status, status, 4);
+    oracle_shape osh = {N, T, H, E, R, 0, sz.capacity, NULL, NULL};
+    int32_t* o_counts = halloc(sz.counts); int32_t* o_soff = halloc(sz.send_off);
+    int32_t* o_spos = halloc(sz.send_pos); uint8_t* o_sbuf = halloc(sz.send_buf);
+    int32_t* o_smeta = halloc(sz.send_meta);
+    oracle_dispatch_send(&osh, (const uint8_t*)x, NULL, g_idx, o_counts, o_soff, o_spos, o_sbuf, o_smeta);
+    CHECK(g_status == 0, "status word %d", g_status);
+    CHECK(!memcmp(g_counts, o_counts, sz.counts), "no-allocation send: counts");
+    CHECK(!memcmp(g_soff, o_soff, sz.send_off), "no-allocation send: send_off");
+    CHECK(!memcmp(g_spos, o_spos, sz.send_pos), "no-allocation send: send_pos");
+    for (int s = 0; s < N; ++s) {
+        const int64_t n = o_soff[s * (N + 1) + N];
+        CHECK(!memcmp(g_sbuf + s * TR * P, o_sbuf + s * TR * P, n * P), "no-allocation send: send_buf rank %d", s);
+        CHECK(!memcmp(g_smeta + 2 * s * TR, o_smeta + 2 * s * TR, n * 8), "no-allocation send: send_meta rank %d", s);
+    }
+    CHECK(!memcmp(g_copy, g_sbuf, sz.send_buf), "stream copy differs from its source");
+    printf("no-allocation send: N%d T%d H%d E%d R%d equal to the oracle; stream copy of %lld bytes exact\n",
+           N, T, H, E, R, (long long)sz.send_buf);
 }
 
 /* ---------------------------------------------------------------- decode path */
@@ -314,6 +381,7 @@ int main(int argc, char** argv) {
         HIP(hipSetDevice(0));
         decode_path();
         prefill_path();
+        noalloc_and_copy();
     }
     if (failures) {
         fprintf(stderr, "%d check(s) failed\n", failures);
