@@ -672,6 +672,7 @@ def overlap_leg(name, steps=10, warmup=2, inter=2048, cu_splits=(256, 224, 192, 
     res = {"workload": name, "shared_expert": f"bf16 MLP {c.H}->{inter}->{c.H} on {c.N * c.T} tokens "
                                                f"(torch GEMMs on a second stream)",
            "total_cus": total_cus}
+    torch.cuda.synchronize()
     res.update(measure(torch.cuda.current_stream()))
     sweep = {}
     for n in cu_splits:
@@ -723,8 +724,11 @@ def microbatch_leg(name, steps=10, warmup=2, inter=2048) -> dict:
     assert not c.rows_fp8 and c.T % 2 == 0, "the micro-batch leg runs on a bf16 workload, T even"
     Th = c.T // 2
     inp = ms.config_inputs(c)
-    s1 = torch.cuda.current_stream()
-    s2 = torch.cuda.Stream()   # default priority
+    # two streams taken from torch's pool one after the other (default priority): consecutive pool
+    # streams sit on different hardware queues, whereas a stream taken late in a run can share a
+    # queue with the one the path runs on and serialise behind it
+    s1 = torch.cuda.Stream()
+    s2 = torch.cuda.Stream()
     gen = torch.Generator(device="cuda").manual_seed(0)
     wg = (torch.randn(c.H, inter, device="cuda", generator=gen) * c.H ** -0.5).to(torch.bfloat16)
     wu = (torch.randn(c.H, inter, device="cuda", generator=gen) * c.H ** -0.5).to(torch.bfloat16)
@@ -741,6 +745,7 @@ def microbatch_leg(name, steps=10, warmup=2, inter=2048) -> dict:
         b.x.copy_(torch.from_numpy(np.ascontiguousarray(x[:, h * Th:(h + 1) * Th])))
         xs = b.x.view(torch.bfloat16).view(c.N * Th, c.H)
         mbs.append((b, xs, torch.empty_like(xs)))
+    torch.cuda.synchronize()   # the uploads ran on the current stream, which s1 and s2 do not wait for
 
     def dispatch(mb, st):
         b = mb[0]
