@@ -1035,8 +1035,8 @@ def acc_combine_leg(name, steps=20, warmup=3) -> dict:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--extra", default=",".join(EXTRA),
                     help="comma-separated workloads reported beside the headline ('' for none)")
