@@ -832,6 +832,45 @@ def microbatch_leg(name, steps=10, warmup=2, inter=2048) -> dict:
     return res
 
 
+LAUNCH_REPS = 8
+# kernels in one rank's decode layer: route; count and pack; network; unpack; combine pack and
+# network back; weighted sum
+KERNELS_PER_RANK_LAYER = 8
+
+
+def graph_period(fn, reps) -> float:
+    """Median µs per call of fn(stream) when LAUNCH_REPS calls are captured in one HIP graph and
+    the graph is replayed (HIP events around each replay)."""
+    import numpy as np
+    import torch
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(LAUNCH_REPS):
+            fn(torch.cuda.current_stream())
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(LAUNCH_REPS):
+            fn(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    t = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        t.append(e0.elapsed_time(e1) * 1e3 / LAUNCH_REPS)
+    del g
+    return round(float(np.median(t)), 2)
+
+
 def rank_leg(name, steps=20, warmup=3) -> dict:
     """One rank's share at its real shape: every call restricted to a single rank (as each GPU of
     an expert-parallel deployment runs it), timed with HIP events, for the rank that receives the
@@ -938,6 +977,18 @@ def rank_leg(name, steps=20, warmup=3) -> dict:
         out[label] = {"rank": r, "rows_received": int(recv[r]), "us_per_layer": round(sum(per.values()), 2),
                       "graph_replay_us_per_layer": round(g0.elapsed_time(g1) * 1e3 / steps, 2),
                       "per_call_us": per, "send_side_sum_combine_us": acc}
+        if label == "median_rank":
+            # each call alone: a graph of LAUNCH_REPS repeats of it (every call is idempotent once
+            # the full step has run), replayed; beside it the same for a 16-byte stream copy, the
+            # cost of one graph-launched kernel that does (almost) nothing
+            fl_src = torch.zeros(16, dtype=torch.uint8, device="cuda")
+            fl_dst = torch.zeros(16, dtype=torch.uint8, device="cuda")
+            floor = graph_period(lambda s_: moe.moe_stream_copy(fl_src, fl_dst, 16, s_), steps)
+            periods = {n: graph_period(lambda s_, i=i: calls_on(s_)[i](), steps) for i, n in enumerate(calls)}
+            out[label]["graph_period_us"] = periods
+            out[label]["launch_floor_us"] = floor
+            out[label]["kernels_per_layer"] = KERNELS_PER_RANK_LAYER
+            out[label]["launch_floor_us_per_layer"] = round(floor * KERNELS_PER_RANK_LAYER, 2)
         del graph
     status = int(b.status.item())
     if status != 0:
