@@ -236,7 +236,10 @@ __global__ __launch_bounds__(kBlock) void k_acc_partial(Dims D, const uint16_t* 
 // over the call's ranks) are resolved by wave 0, one per lane; the rows that hold a partial are
 // gathered at the front of the block's row list (a ballot) and only they are streamed, so the
 // rows that move nothing (most of them where a token's rows crowd onto one rank) cost a resolve
-// lane, not a block.  STRIDE: blocks stride over a capped grid.
+// lane, not a block.  STRIDE: blocks stride over a capped grid.  Cached stores, as in the
+// receive-side network back: the source's sum reads these rows next (same process, cache flushed
+// between layers: the send half 338 -> 304 us on DeepSeek-V3, 379 -> 361 us on Kimi-K2, the sum
+// within 4 us).
 // Threads per block of the partial network kernel (512 let four rows stream in one pass but lost
 // the Kimi-K2 gain: 406 us).
 #ifndef MOE_ACC_NET_THREADS
@@ -312,7 +315,7 @@ __global__ __launch_bounds__(MOE_ACC_NET_THREADS) void k_acc_net(Dims D, const u
             if (lane == 0) nlive = __popcll(m);
         }
         __syncthreads();
-        block_stream_rows<U>(rows, nlive, D.Y16, D.Y16, D.Y16, cs_buf, stage);
+        block_stream_rows<U, true, false>(rows, nlive, D.Y16, D.Y16, D.Y16, cs_buf, stage);
     };
     if constexpr (STRIDE) {
         for (long base = (long)blockIdx.x * W; base < total; base += (long)gridDim.x * W) {
