@@ -84,9 +84,12 @@ def prefill_alg_bytes(c) -> dict:
     return b
 
 
-def run_prefill_workload(name, steps, warmup, check=True):
-    """The replicated-token path: route -> prefill dispatch | (stand-in expert, untimed) |
-    local combine -> all-reduce, per call timed with HIP events on the kernels' stream."""
+def run_prefill_workload(name, steps, warmup, check=True, flush_mall=True):
+    """The replicated-token path: route -> prefill dispatch | (stand-in expert, outside the
+    metric) | local combine -> all-reduce, per call timed with HIP events on the kernels' stream,
+    medians over the steps, timed with the memory-side cache flushed between steps and back to
+    back as the decode workloads are.  The dispatch's cached stores leave part of their write-back
+    to the stand-in, so the layer is also reported with the stand-in counted."""
     import numpy as np
     import torch
 
@@ -121,25 +124,37 @@ def run_prefill_workload(name, steps, warmup, check=True):
         for f in calls:
             f()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
-    for k in range(steps):
-        for i, f in enumerate(calls):
-            evs[k][i].record(st)
-            f()
-        evs[k][len(calls)].record(st)
-    torch.cuda.synchronize()
-    per = {n: round(sum(evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(steps)) * 1e3 / steps, 2)
-           for i, n in enumerate(names)}
+    scratch = torch.zeros(1 << 28, dtype=torch.int32, device="cuda")
     ab = prefill_alg_bytes(c)
-    dispatch_us = per["route"] + per["prefill_dispatch"]
-    combine_us = per["combine_local"] + per["allreduce"]
-    layer_us = dispatch_us + combine_us
-    res = dict(workload=name, dtype=c.dtype, layer_us=round(layer_us, 2),
-               dispatch_us=round(dispatch_us, 2), combine_us=round(combine_us, 2), per_call_us=per,
-               gbs=round(ab["total"] / (layer_us * 1e-6) / 1e9, 1),
-               per_call_gbs={n: round(ab[n] / (per[n] * 1e-6) / 1e9, 1)
-                             for n in ["route", "prefill_dispatch", "combine_local", "allreduce"]},
+
+    def timed(flush):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
+        for k in range(steps):
+            if flush:
+                scratch.sum()
+            for i, f in enumerate(calls):
+                evs[k][i].record(st)
+                f()
+            evs[k][len(calls)].record(st)
+        torch.cuda.synchronize()
+        per = {n: round(float(np.median([evs[k][i].elapsed_time(evs[k][i + 1]) * 1e3 for k in range(steps)])), 2)
+               for i, n in enumerate(names)}
+        dispatch_us = per["route"] + per["prefill_dispatch"]
+        combine_us = per["combine_local"] + per["allreduce"]
+        layer_us = dispatch_us + combine_us
+        return dict(layer_us=round(layer_us, 2), layer_with_stub_us=round(layer_us + per["stub"], 2),
+                    dispatch_us=round(dispatch_us, 2), combine_us=round(combine_us, 2), per_call_us=per,
+                    gbs=round(ab["total"] / (layer_us * 1e-6) / 1e9, 1),
+                    per_call_gbs={n: round(ab[n] / (per[n] * 1e-6) / 1e9, 1)
+                                  for n in ["route", "prefill_dispatch", "combine_local", "allreduce"]})
+
+    head = timed(flush_mall)
+    other = timed(not flush_mall)
+    del scratch
+    res = dict(workload=name, dtype=c.dtype, mall_flushed_between_steps=bool(flush_mall), **head,
                alg_bytes=ab["total"])
+    res["other_protocol"] = {"mall_flushed_between_steps": not flush_mall,
+                             **{k: other[k] for k in ("layer_us", "layer_with_stub_us", "per_call_us", "gbs")}}
     if check:
         # identity experts: out == bf16(x * sum_k w_k) up to the torch reference's own double
         # rounding; every slot lands on exactly one rank
@@ -1130,7 +1145,7 @@ def main():
     extras = {}
     for name in [e for e in args.extra.split(",") if e and e != args.workload]:
         if ms.CONFIGS[name].layout == "prefill":
-            r = run_prefill_workload(name, args.steps, args.warmup, check=not args.no_check)
+            r = run_prefill_workload(name, args.steps, args.warmup, check=not args.no_check, flush_mall=flush)
             r["frac_of_peak"] = round(r["gbs"] / PEAK_HBM_GBS, 4)
             extras[name] = r
             continue
