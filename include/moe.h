@@ -28,8 +28,9 @@
  *    token's R slots) set *shape->status to MOE_EBADIDX if it is still 0 (sticky) and drop the
  *    offending slot: it is not counted, not sent, gets send_pos = -1 and adds nothing to the
  *    combine.  The caller reads the status word after its own synchronisation.
- *  - Calls are reentrant; the library keeps no state.  Two calls that overlap in time must not
- *    share output buffers or a workspace.
+ *  - Calls are reentrant; the library keeps no state, except the static per-GPU histogram array
+ *    of moe_dispatch_send_noalloc (calls of it that overlap in time on one GPU race on it).  Two
+ *    calls that overlap in time must not share output buffers or a workspace.
  */
 #ifndef MOE_H
 #define MOE_H
