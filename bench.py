@@ -446,20 +446,24 @@ def cpu_baseline(name, budget_s=20.0) -> dict:
         x, xs = inp["x"], inp["x_scale"]
         if c.quant:
             x, xs = oracle.quantize_e4m3(x)
-        t0 = time.perf_counter()
+        ts = [time.perf_counter()]
         sh = oracle.shape(c.N, c.T, c.H, c.E, c.R, c.rows_fp8, tokens=tok)
         idx, w = oracle.route(inp["logits"], inp["bias"], c.R)
+        ts.append(time.perf_counter())
         r = oracle.dispatch_send(sh, x, xs, idx.reshape(c.N, -1))
+        ts.append(time.perf_counter())
         sh = oracle.packed_shape(c.N, c.T, c.H, c.E, c.R, c.rows_fp8,
                                  np.diff(r["send_off"], axis=1).sum(axis=0), tok)
         r.update(oracle.net_dispatch(sh, r["send_off"], r["send_buf"], r["send_meta"]))
+        ts.append(time.perf_counter())
         r.update(oracle.dispatch_recv(sh, r["counts"], r["recv_off"], r["recv_buf"], r["recv_meta"]))
-        t1 = time.perf_counter()
+        ts.append(time.perf_counter())
         y = oracle.expert(sh, 0, r["expert_x"], r["expert_scale"], r["expert_off"])
         t2 = time.perf_counter()
         out = oracle.combine(sh, 0, y, r["expert_rpos"], r["recv_off"], r["send_off"], r["send_pos"], w)
         t3 = time.perf_counter()
-        return (t1 - t0) + (t3 - t2), y, out["out"]
+        stages = [b - a for a, b in zip(ts, ts[1:])] + [t3 - t2]
+        return sum(stages), stages, y, out["out"]
 
     def layer_threaded(pool, parts, y):
         x, xs = inp["x"], inp["x_scale"]
@@ -479,11 +483,12 @@ def cpu_baseline(name, budget_s=20.0) -> dict:
                                      w, pool, parts)
         return time.perf_counter() - t0, out["out"]
 
-    times, t_start = [], time.perf_counter()
+    times, stage_times, t_start = [], [], time.perf_counter()
     y = out1 = None
     while True:
-        t, y, out1 = layer_single()
+        t, st_, y, out1 = layer_single()
         times.append(t)
+        stage_times.append(st_)
         # about budget_s/2 .. budget_s of host work: at least 3 layers, at most 20
         if len(times) >= 20 or (len(times) >= 3 and time.perf_counter() - t_start > budget_s * 0.5):
             break
@@ -511,6 +516,9 @@ def cpu_baseline(name, budget_s=20.0) -> dict:
     return {"value": round(ab["total"] / t1core / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "host_cpus": os.cpu_count(), "cpu_share": cores, "cpu_model": model,
             "us_per_layer": round(t1core * 1e6, 1),
+            "per_stage_us": {n: round(float(np.median([st_[i] for st_ in stage_times])) * 1e6, 1)
+                             for i, n in enumerate(["route", "dispatch_send", "net_dispatch", "dispatch_recv",
+                                                    "combine"])},
             "sample": f"one full {name} layer (all {c.N} ranks) through the single-threaded C oracle "
                       f"(route, dispatch, network, unpack, combine; stand-in expert excluded), "
                       f"median of {len(times)}",

@@ -66,3 +66,13 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU only" in r.stderr
     assert r.stdout == ""
+
+
+def test_cpu_baseline_leg_on_the_tiny_workload():
+    # the oracle leg runs without a GPU: its contract fields, the per-stage times that make up the
+    # layer, and the threaded run's output equal to the single-threaded one (checked inside)
+    r = bench.cpu_baseline("tiny", budget_s=1.0)
+    assert r["kind"] == "oracle" and r["unit"] == "GB/s" and r["cores"] == 1 and r["value"] > 0
+    assert set(r["per_stage_us"]) == {"route", "dispatch_send", "net_dispatch", "dispatch_recv", "combine"}
+    assert r["threaded"]["cores"] >= 1 and r["threaded"]["value"] > 0
+    assert "tiny" in r["sample"]
