@@ -1129,6 +1129,9 @@ def main():
                     help="headline from steps run back to back instead of with the memory-side "
                          "cache flushed between steps (a 1 GiB scratch read, untimed by the per-call "
                          "events, included in ms_per_step); both are measured and reported")
+    ap.add_argument("--tokens-sweep", default="",
+                    help="comma-separated tokens per rank: also time the headline workload's shape "
+                         "at each (cache flushed between steps), reported as tokens_sweep")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the N expert-parallel ranks are simulated inside one "
@@ -1211,10 +1214,36 @@ def main():
     if calib is not None:
         line["copy_ceiling"] = calib
         line["frac_of_copy_ceiling"] = round(head["gbs"] / calib["stream_copy"]["gbs"], 4)
+    if args.tokens_sweep:
+        line["tokens_sweep"] = tokens_sweep(args.workload, [int(t) for t in args.tokens_sweep.split(",")],
+                                            args.steps, args.warmup, check=not args.no_check)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.workload)
     line["children_at_exit"] = end_children()
     print(json.dumps(line), flush=True)
+
+
+def tokens_sweep(name, ts, steps, warmup, check=True) -> list:
+    """The workload's shape at other tokens per rank (decode batch sizes): per-call medians with
+    the memory-side cache flushed between steps, as the headline is timed."""
+    import dataclasses
+
+    import moe_synth as ms
+
+    base = ms.CONFIGS[name]
+    out = []
+    for T in ts:
+        c = dataclasses.replace(base, name=f"{name}@T{T}", T=T, desc=f"{base.desc} at T = {T}")
+        ms.CONFIGS[c.name] = c
+        try:
+            r = run_workload(c.name, steps, warmup, check=check, flush_mall=True)
+        finally:
+            del ms.CONFIGS[c.name]
+        out.append({"T": T, "us_per_layer": round(r["layer_us"], 2),
+                    "frac_of_peak": round(r["gbs"] / PEAK_HBM_GBS, 4),
+                    "graph_replay_us_per_step": r["graph_replay_us_per_step"],
+                    "per_call_us": r["per_call_us"]})
+    return out
 
 
 def end_children() -> int:
