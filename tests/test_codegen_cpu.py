@@ -3,8 +3,8 @@
 Two properties that no parity test can see but that bound the kernels' speed:
 
 - no kernel spills to scratch (private) memory;
-- in the row-copy kernels, no 16-byte load is issued right after a wait for every outstanding
-  memory operation (``s_waitcnt vmcnt(0)``).  That pattern means the compiler could not keep the
+- no 16-byte load is issued right after a wait for every outstanding memory operation
+  (``s_waitcnt vmcnt(0)``), in the row-copy kernels (which must have such loads) or any other.  That pattern means the compiler could not keep the
   thread's loads in flight together and issued them one at a time; it appeared when each load sat
   under a per-lane condition, and cost the network and unpack kernels 5-10%.
 """
@@ -35,8 +35,18 @@ def _hipcc():
     return b
 
 
+_ASM = {}
+
+
 def _device_asm(tmp_path, source):
-    """gfx950 assembly of one source and the compiler's resource-usage remarks."""
+    """gfx950 assembly of one source and the compiler's resource-usage remarks (compiled once per
+    test session)."""
+    if source not in _ASM:
+        _ASM[source] = _compile(tmp_path, source)
+    return _ASM[source]
+
+
+def _compile(tmp_path, source):
     b = _hipcc()
     flags = [f for f in b.FLAGS if f not in ("-fPIC", "-shared")]
     out = os.path.join(str(tmp_path), os.path.basename(source) + ".s")
@@ -90,6 +100,20 @@ def test_row_copy_loads_stay_in_flight(tmp_path, source):
                     serial.append(name)
     assert checked > 0, "no 16-byte loads found in the row-copy kernels"
     assert not serial, f"loads issued after a full wait in {sorted(set(serial))[:4]}"
+
+
+@pytest.mark.parametrize("source", SOURCES)
+def test_no_16_byte_load_waits_for_every_earlier_load(tmp_path, source):
+    # the same property for every kernel, row copies or not (weighted sums, packs, prefill): a
+    # 16-byte load right after a full wait would mean the loads of a thread go out one at a time
+    asm, _ = _device_asm(tmp_path, source)
+    serial = []
+    for name, lines in _functions(asm):
+        for k, line in enumerate(lines):
+            if re.match(r"(global|flat|buffer)_load_dwordx4", line) and \
+                    any(re.match(r"s_waitcnt vmcnt\(0\)", p) for p in lines[max(0, k - 2):k]):
+                serial.append(name)
+    assert not serial, f"{source}: loads issued after a full wait in {sorted(set(serial))[:4]}"
 
 
 def test_lds_staged_stream_build_uses_direct_to_lds_loads(tmp_path):
