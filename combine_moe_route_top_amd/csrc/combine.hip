@@ -115,6 +115,7 @@ __global__ __launch_bounds__(kBlock) void k_combine_pack(Dims D, const uint16_t*
     __syncthreads();
     const long total = gb[D.rc];
     auto pass = [&](long base) {
+        if (base >= total) return;  // the block's rows all lie past the call's rows (block-uniform)
         const long G = base + wave_id();
         RowDesc rd = {0, 0, 0, 0};
         if (wave_id() < RPB && G < total) {
@@ -165,6 +166,7 @@ __global__ __launch_bounds__(kBlock) void k_combine_net(Dims D, const uint16_t* 
     __syncthreads();
     const long total = gb[D.rc];
     auto pass = [&](long base) {
+        if (base >= total) return;  // the block's rows all lie past the call's rows (block-uniform)
         const long G = base + wave_id();
         RowDesc rd = {0, 0, 0, 0};
         if (wave_id() < RPB && G < total) {

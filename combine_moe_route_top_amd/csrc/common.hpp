@@ -125,24 +125,20 @@ inline long recv_rows_bound(const Dims& D) {
 }
 
 // Blocks for a row kernel whose rows are only known on the device: one block per RPB rows of
-// the bound when the call covers all ranks and every rank sends T tokens (every row exists); half
-// that with per-rank token counts, blocks then striding over the rows, since ranks that send
-// fewer tokens leave part of the bound empty and the blocks past the rows still cost their launch
-// (in one process, DeepSeek-V3 with token counts uniform on 1..T: unpack 96 -> 83 us, combine
-// 228 -> 201 us; every rank sending T tokens with counts given: 161 -> 166 and 395 -> 407 us,
-// the price of striding); at most kSubrangeBlocks when the call covers a subset of the ranks
-// (most of the bound is usually empty).
+// the bound when the call covers all ranks, at most kSubrangeBlocks when it covers a subset (most
+// of the bound is usually empty; blocks then stride over the rows).  With per-rank token counts
+// part of an all-rank bound is empty too; the blocks past the call's rows return before they
+// resolve or stream anything, which leaves them only their launch (letting them stream their dead
+// rows' dummy loads cost the ragged DeepSeek-V3 mix, tokens uniform on 1..T, 96 against 84 us in
+// the unpack and 228 against 206 us in the combine).  Halving the grid for calls with token counts
+// gained 8 us more there but cost calls whose ranks all send T tokens as much, so the grid stays.
 #ifndef MOE_SUBRANGE_BLOCKS
 #define MOE_SUBRANGE_BLOCKS 4096
 #endif
 constexpr long kSubrangeBlocks = MOE_SUBRANGE_BLOCKS;
 inline long row_blocks(const Dims& D, long rows_bound, int rpb) {
     long b = (rows_bound + rpb - 1) / rpb;
-    if (D.rc < D.N) {
-        if (b > kSubrangeBlocks) b = kSubrangeBlocks;
-    } else if (D.tok) {
-        b = (b + 1) / 2;
-    }
+    if (D.rc < D.N && b > kSubrangeBlocks) b = kSubrangeBlocks;
     return b > D.rc ? b : D.rc;
 }
 

@@ -395,6 +395,7 @@ __global__ __launch_bounds__(kBlock) void k_unpack(Dims D, const int32_t* __rest
     __syncthreads();
     const long total = gb[D.rc];
     auto pass = [&](long base) {
+        if (base >= total) return;  // the block's rows all lie past the call's rows (block-uniform)
         const long G = base + wave_id();
         RowDesc rd = {0, 0, 0, 0};
         if (wave_id() < RPB && G < total) {
