@@ -329,6 +329,12 @@ __global__ __launch_bounds__(kBlock) void k_net_dispatch(Dims D, const int32_t* 
     }
     if (wave_id() < RPB && lane_id() == 0) rows[wave_id()] = rd;
     __syncthreads();
+    // rows past their rank's send total (ranks that send fewer than T tokens) are dead; a block
+    // with no live row has nothing to stream (the same test in every thread: block-uniform)
+    bool live = false;
+#pragma unroll
+    for (int w = 0; w < RPB; ++w) live |= rows[w].dst_a != 0;
+    if (!live) return;
     block_stream_rows<U, true, !CACHED>(rows, RPB, D.P16, D.P16, D.P16, send_buf, stage);
 }
 
