@@ -398,7 +398,6 @@ def traffic_record(kernel, workload):
     """Scaled FETCH_SIZE + WRITE_SIZE bytes per launch from the committed counter summary, or
     None if there is none or the kernel's source changed since the counters were taken."""
     import glob
-    import hashlib
     import re
     for path in glob.glob(os.path.join(ROOT, "profiles", "counters_*.md")):
         for line in open(path):
