@@ -4,6 +4,8 @@ Small shapes span several chunks, blocks and ragged tails; the full workloads ru
 real sizes with the launch configuration the benchmark times.  Every test prints the case it
 runs before touching the GPU.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -341,13 +343,19 @@ def _sweep_case(seed):
     kind = rng.choice(["bf16", "bf16", "fp8", "quant"])
     H = int(rng.choice([512, 1024])) if kind != "bf16" else 8 * int(rng.integers(1, 97))
     bias = str(rng.choice(["none", "zipf"]))
-    tokens = rng.integers(0, T + 1, N).astype(np.int32) if rng.random() < 0.4 else None
+    with_tokens = rng.random() < 0.4 or os.environ.get("MOE_SWEEP_TOKENS") == "1"
+    tokens = rng.integers(0, T + 1, N).astype(np.int32) if with_tokens else None
     tight = bool(rng.random() < 0.25)
     split = bool(rng.random() < 0.5)
     return N, T, H, E, R, str(kind), bias, tokens, tight, split
 
 
-@pytest.mark.parametrize("seed", range(96))
+# 96 seeds by default; a wider one-off run sets MOE_SWEEP_SEEDS=first:last (and MOE_SWEEP_TOKENS=1
+# to give every case per-rank token counts)
+_SWEEP = [int(v) for v in os.environ.get("MOE_SWEEP_SEEDS", "0:96").split(":")]
+
+
+@pytest.mark.parametrize("seed", range(*_SWEEP))
 def test_random_shape_sweep(seed):
     # random configurations, each compared with the oracle stage by stage
     N, T, H, E, R, kind, bias, tokens, tight, split = _sweep_case(seed)
