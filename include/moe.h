@@ -17,7 +17,9 @@
  *    or synchronises; each call only enqueues kernels on `stream` (a hipStream_t; NULL is the
  *    legacy default stream) and returns.  Outputs are valid once the stream reaches that point.
  *  - Return value: MOE_OK, or a negative moe_status after host-side validation (nothing is
- *    enqueued then), or MOE_EHIP if a launch failed.
+ *    enqueued then), or MOE_EHIP if a launch failed.  Launches are checked with hipGetLastError(),
+ *    which also returns (and clears) an error an earlier HIP call on the same thread left unread;
+ *    such an error is reported as MOE_EHIP by the next call.
  *  - Payload buffers (x, x_scale, send_buf, recv_buf, expert_x, expert_scale, expert_y,
  *    cs_buf, cr_buf, out) must be 16-byte aligned; metadata 8-byte; everything else 4-byte.
  *  - Index types are int32.  Rows are addressed as [rank][row] with the row strides given by
